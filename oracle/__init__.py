@@ -212,7 +212,7 @@ def ref_f64(x: np.ndarray, w: np.ndarray, peers, tp: int, rank: int, rows=None) 
 def schedule(M: int, N: int, tp: int, rank: int, bm: int, bn: int, group_m: int):
     """Tile schedule: dict of int32 arrays d, tm, tn, flag indexed by slot."""
     S = M // tp
-    T = tp * (S // bm) * (N // bn)
+    T = tp * (-(-S // bm)) * (-(-N // bn))
     out = {k: np.empty(T, np.int32) for k in ("d", "tm", "tn", "flag")}
     _check(lib().oracle_schedule(M, N, tp, rank, bm, bn, group_m, _ptr(out["d"], _i32p),
                                  _ptr(out["tm"], _i32p), _ptr(out["tn"], _i32p),

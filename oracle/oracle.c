@@ -223,7 +223,8 @@ int oracle_ref_f64(int64_t nrows, const int64_t *rows, int64_t M, int64_t N, int
 
 /* The pages name tile-coordinate swizzling (FLUX TL;DR) without details.  The
  * schedule fixed here: the output is cut into BM x BN tiles that never cross a
- * slice boundary (BM divides S, BN divides N); slot q of the T = tp*TMs*TN
+ * slice boundary; a slice has TMs = ceil(S/BM) tile rows and TN = ceil(N/BN)
+ * tile columns, the last of each possibly partial; slot q of the T = tp*TMs*TN
  * slots visits destination slices in the order rank, rank+1, ... (mod tp), so
  * this rank's own slice comes first and every rank targets a different
  * destination at each step; within a slice, tiles are visited in groups of
@@ -241,8 +242,8 @@ int oracle_schedule(int64_t M, int64_t N, int32_t tp, int32_t rank, int32_t bm, 
         return ORACLE_EINVAL;
     if (M % tp) return ORACLE_EINVAL;
     const int64_t S = M / tp;
-    if (S % bm || N % bn) return ORACLE_EINVAL;
-    const int64_t tms = S / bm, tn_count = N / bn, ts = tms * tn_count;
+    if (S == 0) return ORACLE_EINVAL;
+    const int64_t tms = (S + bm - 1) / bm, tn_count = (N + bn - 1) / bn, ts = tms * tn_count;
     const int64_t total = (int64_t)tp * ts;
     for (int64_t q = 0; q < total; ++q) {
         int64_t step = q / ts;

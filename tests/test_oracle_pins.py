@@ -386,4 +386,22 @@ def test_schedule_rejects_bad_shapes():
     with pytest.raises(RuntimeError):
         oracle.schedule(100, 64, 8, 0, 16, 64, 1)  # M not divisible by tp
     with pytest.raises(RuntimeError):
-        oracle.schedule(128, 64, 8, 0, 32, 64, 1)  # BM does not divide S
+        oracle.schedule(8, 64, 16, 0, 16, 64, 1)  # empty slice
+
+
+@pytest.mark.parametrize("M,N,bm,bn,gm", [(8 * 40, 200, 16, 64, 3), (8 * 7, 24, 16, 64, 1),
+                                          (8 * 100, 1000, 32, 128, 2)])
+def test_schedule_ragged_tiles_cover_slice_exactly_once(M, N, bm, bn, gm):
+    # partial last tile row / column: every element of every slice is covered
+    # by exactly one tile, and no tile crosses a slice boundary
+    tp, rank = 8, 4
+    S = M // tp
+    s = oracle.schedule(M, N, tp, rank, bm, bn, gm)
+    tms = -(-S // bm)
+    cover = np.zeros((M, N), np.int32)
+    for q in range(s["d"].size):
+        d, tm, tn = int(s["d"][q]), int(s["tm"][q]), int(s["tn"][q])
+        r0 = d * S + (tm - d * tms) * bm
+        r1 = min(r0 + bm, (d + 1) * S)
+        cover[r0:r1, tn * bn:min(N, tn * bn + bn)] += 1
+    assert np.all(cover == 1)
