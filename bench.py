@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused BF16 GEMM + reduce-scatter (one TP=8 rank's share).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload o_proj]
+
+A step is one fused run of the whole hot path (GEMM tiles, routed BF16
+epilogue with ready flags, reducers summing this rank's slice with the 7 peer
+partials) over inputs already resident in HBM.  Prints ONE JSON line:
+fused TFLOP/s (value), its fraction of the MI355X dense BF16 MFMA peak, the
+overlap efficiency 1 - (T_fused - T_gemm) / T_reduce against the same GEMM and
+the standalone reduce kernel run alone, a roofline object for the fused kernel,
+and the CPU oracle timed on the host cores as a baseline.  With --sweep (the
+default) the other benchmark shapes are timed too and reported under "sweep".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA (AMD published figure)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (AMD published figure)
+METRIC = "fused GEMM+RS TFLOP/s (% bf16 MFMA peak) + overlap efficiency, M=512..32768"
+DEFAULT_WORKLOAD = "o_proj"
+SWEEP = ("down_proj", "mixtral_down", "large_prefill")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tensor_gemm_reduce_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-sweep", dest="sweep", action="store_false")
+    p.add_argument("--no-cpu", dest="cpu", action="store_false")
+    p.add_argument("--no-check", dest="check", action="store_false")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--tile", default="auto")
+    p.add_argument("--reducers", type=int, default=-1)
+    p.add_argument("--protocol", type=int, default=0)
+    p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Device inputs/outputs and a handle for one benchmark shape."""
+
+    def __init__(self, name, args, rank=0):
+        import numpy as np
+        import torch
+
+        import synthetic
+        from tensor_gemm_reduce_amd import gemm_rs as gr
+
+        self.cfg = cfg = synthetic.CONFIGS[name]
+        self.name = name
+        self.rank = rank
+        x, w, peers = synthetic.make_inputs(cfg, "normal")
+        self.host_inputs = (x, w, peers)
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+        self.x, self.w = d(x), d(w)
+        self.peers = [d(p) for p in peers]
+        z = lambda: torch.empty((cfg.S, cfg.N), dtype=torch.int16, device="cuda")
+        self.send = [z() for _ in range(7)]
+        self.local = z()
+        self.out = z()
+        self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
+                            num_reducers=args.reducers, flag_protocol=args.protocol)
+        self.gr = gr
+
+    def run(self, mode):
+        self.op.run(mode, self.x, self.w, self.send, self.peers, self.out, self.local)
+
+    def matmul(self):
+        import torch
+
+        return torch.nn.functional.linear(self.x.view(torch.bfloat16), self.w.view(torch.bfloat16))
+
+
+def time_each(fn, warmup, iters):
+    """Per-launch durations (us) from event pairs on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) * 1e3 for s, e in ev]
+
+
+def summary(us):
+    q = statistics.quantiles(us, n=10) if len(us) >= 10 else [min(us)] * 9 + [max(us)]
+    return {"median_us": statistics.median(us), "mean_us": statistics.fmean(us), "p10_us": q[0],
+            "p90_us": q[-1]}
+
+
+def measure_case(c: Case, warmup, iters):
+    gr = c.gr
+    cfg = c.cfg
+    fused = summary(time_each(lambda: c.run(gr.MODE_FUSED), warmup, iters))
+    gemm = summary(time_each(lambda: c.run(gr.MODE_GEMM_ONLY), warmup, iters))
+    red = summary(time_each(lambda: c.run(gr.MODE_REDUCE_ONLY), warmup, iters))
+    seq = summary(time_each(lambda: c.run(gr.MODE_SEQUENTIAL), warmup, iters))
+    mm = summary(time_each(c.matmul, warmup, iters))
+    st = c.op.status()
+    if st != gr.OK:
+        raise RuntimeError(f"{c.name}: device status {gr.gemm_rs_strerror(st)}")
+    tf, tg, tr = fused["median_us"], gemm["median_us"], red["median_us"]
+    return {
+        "shape": {"M": cfg.M, "N": cfg.N, "K_local": cfg.K_local, "tp": cfg.tp},
+        "launch": c.op.info.as_dict(),
+        "T_fused_us": fused, "T_gemm_us": gemm, "T_reduce_us": red, "T_seq_us": seq,
+        "T_torch_linear_us": mm,
+        "fused_tflops": cfg.flops / tf * 1e-6,
+        "fused_pct_peak": 100.0 * cfg.flops / tf * 1e-6 / PEAK_BF16_TFLOPS,
+        "gemm_only_tflops": cfg.flops / tg * 1e-6,
+        "reduce_gbs": cfg.reduce_bytes / tr * 1e-3,
+        "reduce_pct_hbm": 100.0 * cfg.reduce_bytes / tr * 1e-3 / PEAK_HBM_GBS,
+        "overlap": 1.0 - (tf - tg) / tr,
+        "speedup_vs_sequential": seq["median_us"] / tf,
+    }
+
+
+def check_case(c: Case, rows_per=3):
+    """Untimed parity check on sampled rows against the oracle."""
+    import numpy as np
+
+    import oracle
+
+    x, w, peers = c.host_inputs
+    cfg = c.cfg
+    c.run(c.gr.MODE_FUSED)
+    import torch
+
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, cfg.S - 1], rng.integers(0, cfg.S, rows_per)])).astype(np.int64)
+    host = lambda t: t.cpu().numpy().view(np.uint16)
+    local = host(c.local)[rows]
+    out = host(c.out)[rows]
+    want_out = oracle.slice_sum(local, [p[rows] for p in peers], tp=8)
+    ref = oracle.ref_f64(x, w, None, tp=8, rank=c.rank, rows=rows)
+    err_local = float(np.max(np.abs(oracle.bf16_to_f32(local) - ref)) / np.max(np.abs(ref)))
+    ok = bool(np.array_equal(out, want_out)) and err_local <= 1e-2
+    return {"ok": ok, "rows": int(rows.size), "local_max_rel_err": err_local}
+
+
+def cpu_baseline(c: Case, seconds):
+    """The oracle as it stands, on the host cores, over whole rows of the same
+    workload until about `seconds` have elapsed."""
+    import numpy as np
+
+    import oracle
+
+    x, w, peers = c.host_inputs
+    cfg = c.cfg
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(cores, int(omp)) if omp and omp.isdigit() else cores
+    oracle.lib()
+    t_total, rows_done, reps = 0.0, 0, 0
+    S = cfg.S
+    chunk = max(1, min(S, 64))
+    start = 0
+    while t_total < seconds and reps < 10_000:
+        rows = (np.arange(chunk) + start) % S
+        t0 = time.perf_counter()
+        # whole path for these slice rows: all 8 destination row blocks of the
+        # GEMM (routing), the BF16 rounding and the slice sum
+        locals_ = None
+        for d in range(8):
+            part = oracle.f32_to_bf16(oracle.gemm_f32acc(x, w, rows=d * S + rows))
+            if d == c.rank:
+                locals_ = part
+        oracle.slice_sum(locals_, [p[rows] for p in peers], tp=8)
+        t_total += time.perf_counter() - t0
+        rows_done += chunk
+        start += chunk
+        reps += 1
+    flops = 2.0 * rows_done * 8 * cfg.N * cfg.K_local
+    return {"value": flops / t_total * 1e-12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} slice rows x 8 destination blocks of {c.name} (GEMM, BF16 rounding, "
+                      f"routing, slice sum) in {t_total:.1f} s",
+            "seconds": t_total}
+
+
+def load_traffic(workload):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return t
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of a TP=8 layer on a single GPU; --gpus {args.gpus} "
+              "is not supported (no multi-GPU path in this build).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from tensor_gemm_reduce_amd import gemm_rs as gr
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    c = Case(args.workload, args)
+    cfg = c.cfg
+    check = check_case(c) if args.check else None
+    log(f"[{args.workload}] parity check: {check}")
+
+    # timed region: exactly K fused steps, synchronized on both sides
+    for _ in range(args.warmup):
+        c.run(gr.MODE_FUSED)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        c.run(gr.MODE_FUSED)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = c.op.status()
+    if st != gr.OK:
+        raise RuntimeError(f"device status {gr.gemm_rs_strerror(st)}")
+    per_launch = [s.elapsed_time(e) * 1e3 for s, e in evs]
+    mean_us = statistics.fmean(per_launch)
+    ms_per_step = wall / args.steps * 1e3
+    value = cfg.flops * args.steps / wall * 1e-12
+    log(f"[{args.workload}] fused: {mean_us:.2f} us/launch (events), {ms_per_step * 1e3:.2f} us/step (wall)")
+
+    m = measure_case(c, args.warmup, args.steps)
+    log(f"[{args.workload}] " + json.dumps({k: m[k] for k in ("fused_tflops", "overlap", "reduce_gbs")}))
+
+    traffic = load_traffic(args.workload)
+    achieved = cfg.flops / mean_us * 1e-6
+    roofline = {
+        "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": achieved / PEAK_BF16_TFLOPS,
+        "traffic": (traffic["fetch_bytes"] + traffic["write_bytes"]) if traffic else None,
+        "kernel": "fused_kernel", "algorithmic_flops_per_launch": cfg.flops,
+        "avg_launch_us": mean_us,
+    }
+    cpu = cpu_baseline(c, args.cpu_seconds) if args.cpu else None
+
+    sweep = {}
+    if args.sweep:
+        for name in SWEEP:
+            try:
+                sc = Case(name, args)
+                sweep[name] = measure_case(sc, args.warmup, args.steps)
+                sweep[name]["parity"] = check_case(sc) if args.check else None
+                del sc
+                torch.cuda.empty_cache()
+                log(f"[{name}] " + json.dumps({k: sweep[name][k] for k in
+                                               ("fused_tflops", "fused_pct_peak", "overlap", "reduce_gbs")}))
+            except Exception as e:  # report, keep the headline line
+                sweep[name] = {"error": repr(e)}
+                log(f"[{name}] error: {e!r}")
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            json.dump({args.workload: m, **sweep}, f, indent=1)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {cfg.description}; M={cfg.M} N={cfg.N} "
+                               f"K_local={cfg.K_local} tp={cfg.tp}, rank 0, bf16 in / fp32 accumulate",
+                   "global_batch": cfg.M, "parallelism": "tp8 (one rank simulated)"},
+        "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "overlap": m["overlap"],
+        "T_fused_us": m["T_fused_us"]["median_us"], "T_gemm_us": m["T_gemm_us"]["median_us"],
+        "T_reduce_us": m["T_reduce_us"]["median_us"],
+        "reduce_gbs": m["reduce_gbs"],
+        "parity": check,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": {k: ({"fused_tflops": v.get("fused_tflops"), "fused_pct_peak": v.get("fused_pct_peak"),
+                       "overlap": v.get("overlap"), "T_fused_us": v.get("T_fused_us", {}).get("median_us"),
+                       "T_gemm_us": v.get("T_gemm_us", {}).get("median_us"),
+                       "T_reduce_us": v.get("T_reduce_us", {}).get("median_us"),
+                       "reduce_gbs": v.get("reduce_gbs"),
+                       "T_torch_linear_us": v.get("T_torch_linear_us", {}).get("median_us"),
+                       "parity_ok": (v.get("parity") or {}).get("ok")} if "error" not in v else v)
+                  for k, v in sweep.items()},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "hip": torch.version.hip},
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

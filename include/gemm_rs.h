@@ -1,0 +1,202 @@
+/*
+ * gemm_rs.h -- C ABI of the fused BF16 GEMM + reduce-scatter library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is one rank's share of a tensor-parallel row-parallel linear
+ * layer (problem page "A fused GEMM + reduce-scatter kernel hiding 90% of
+ * communication on 8 H100 GPUs", sections "What is asked" and "How it gets
+ * verified"): rank r holds X_r (M x K_local) and its weight shard W_r, computes
+ * the partial product P_r = X_r * W_r in BF16 with FP32 accumulation, and the
+ * partials of all tp ranks are summed so that rank d keeps row slice d of the
+ * total.  Following FLUX (TL;DR of "FLUX: Fast Software-based Communication
+ * Overlap On GPUs Through Kernel Fusion": reduce-scatter fused as a GEMM
+ * epilogue, tile coordinate swizzling) and mKernel ("mKernel: Fast Multi-GPU,
+ * Multi-Node Fused Kernels", sections 3 and 3.2: compute and communication
+ * roles inside one persistent kernel, tile readiness flags), one persistent
+ * kernel both computes the GEMM tiles and reduces this rank's slice:
+ *
+ *   compute workgroups  walk the tile schedule, run the MFMA main loop, round
+ *                       each finished tile to BF16, store it into the buffer of
+ *                       its destination slice and release its ready flag;
+ *   reducer workgroups  wait for the flags of this rank's own slice and sum each
+ *                       tile with the tp-1 peer partials into `out`.
+ *
+ * On one GPU the tp-1 peer partials are buffers already resident in HBM that
+ * stand in for the other ranks' remote writes, and the tp-1 send buffers stand
+ * in for remote stores; there is no inter-GPU traffic.
+ *
+ * Numerics (fixed so that results are reproducible bit for bit):
+ *   - partial tiles: FP32 MFMA accumulation, rounded to BF16 to nearest-even;
+ *   - slice sum: FP32 additions in the order (((0 + peer_0) + peer_1) + ...
+ *     + peer_{tp-2}) + local, then one round-to-nearest-even to BF16, where
+ *     peer slot i holds peer rank p_i = (i < rank ? i : i + 1).
+ *
+ * Layouts (all row-major BF16, raw 16-bit patterns, device memory):
+ *   x      [M][K_local]        this rank's activations X_r
+ *   w      [N][K_local]        this rank's weight shard, K contiguous (the
+ *                              layout of a linear layer's weight; the product
+ *                              is X_r * W_r with W_r = w^T)
+ *   send[i], peers[i], out, local_slice: [S][N] with S = M / tp
+ * Every pointer must be 16-byte aligned; K_local and N must be multiples of 8.
+ *
+ * Errors: every function returns GEMM_RS_OK (0) or a negative GEMM_RS_ERR_*
+ * code; nothing aborts and nothing throws across the ABI.  gemm_rs_strerror
+ * gives a message (for GEMM_RS_ERR_HIP it includes the last HIP error).
+ *
+ * Threading: a handle may be used from one host thread at a time, and runs on
+ * one handle must not overlap on the device (they share the ready flags):
+ * issue them on one stream, or synchronise between streams.
+ */
+#ifndef GEMM_RS_H
+#define GEMM_RS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes -------------------------------------------------------- */
+#define GEMM_RS_OK 0
+#define GEMM_RS_ERR_INVALID_ARG (-1)       /* null pointer, bad enum, bad size  */
+#define GEMM_RS_ERR_UNSUPPORTED_SHAPE (-2) /* tp != 8, M % tp, N or K % 8, ... */
+#define GEMM_RS_ERR_MISALIGNED (-3)        /* a buffer is not 16-byte aligned   */
+#define GEMM_RS_ERR_NO_DEVICE (-4)         /* current device is not gfx950      */
+#define GEMM_RS_ERR_HIP (-5)               /* a HIP runtime call failed         */
+#define GEMM_RS_ERR_TIMEOUT (-6)           /* a reducer gave up waiting (watchdog) */
+#define GEMM_RS_ERR_NO_MEMORY (-7)         /* device or host allocation failed  */
+
+/* ---- run modes ---------------------------------------------------------- */
+#define GEMM_RS_MODE_FUSED 0       /* one persistent kernel: compute + reducers  */
+#define GEMM_RS_MODE_GEMM_ONLY 1   /* the same GEMM on all CUs, no flags, no sum */
+#define GEMM_RS_MODE_REDUCE_ONLY 2 /* standalone slice sum of local + peers      */
+#define GEMM_RS_MODE_SEQUENTIAL 3  /* GEMM_ONLY then REDUCE_ONLY on one stream   */
+
+/* ---- tile configurations (BM x BN output tile, BK = 64) ------------------ */
+#define GEMM_RS_TILE_AUTO 0
+#define GEMM_RS_TILE_16x64 1
+#define GEMM_RS_TILE_64x128 2
+#define GEMM_RS_TILE_128x128 3
+#define GEMM_RS_TILE_128x256 4
+#define GEMM_RS_TILE_256x128 5
+#define GEMM_RS_TILE_256x256 6
+#define GEMM_RS_TILE_COUNT 7
+
+/* ---- flag protocols (how a finished tile is published) ------------------- */
+#define GEMM_RS_FLAG_WAVE_FENCE 0 /* every wave: agent release fence; barrier; one store */
+#define GEMM_RS_FLAG_WG_RELEASE 1 /* barrier; one agent-scope release store          */
+
+/* ---- debug flags -------------------------------------------------------- */
+#define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
+                                 the compute workgroup and a release timestamp */
+
+typedef struct gemm_rs_config {
+    int32_t M;            /* tokens: rows of X_r and of the partial product   */
+    int32_t N;            /* output features (columns of the product)         */
+    int32_t K_local;      /* this rank's share of the reduction dimension     */
+    int32_t tp;           /* tensor-parallel degree; must be 8                */
+    int32_t rank;         /* this rank, 0 <= rank < tp                        */
+    int32_t tile;         /* GEMM_RS_TILE_*                                   */
+    int32_t group_m;      /* tile rows per raster group; 0 = automatic        */
+    int32_t num_reducers; /* reducer workgroups in FUSED mode; -1 = automatic */
+    int32_t flag_protocol;/* GEMM_RS_FLAG_*                                   */
+    int32_t debug_flags;  /* GEMM_RS_DEBUG_* bits                             */
+    int32_t drop_flag;    /* debug: index of a ready flag the producer never
+                             releases, to exercise the watchdog; -1 = none    */
+    int32_t flag_stride;  /* 32-bit words between ready flags (1 or 32)       */
+    int64_t watchdog_us;  /* reducer wait limit per tile in microseconds;
+                             0 = default (2 000 000)                          */
+} gemm_rs_config;
+
+typedef struct gemm_rs_info {
+    int32_t bm, bn, bk;       /* resolved tile                                 */
+    int32_t group_m;          /* resolved raster group                         */
+    int32_t tiles;            /* T: tiles of the whole M x N partial           */
+    int32_t tiles_per_slice;  /* T_s                                           */
+    int32_t tile_rows_per_slice, tile_cols;
+    int32_t grid;             /* workgroups launched in FUSED mode             */
+    int32_t compute_wgs;      /* of which compute                              */
+    int32_t reducer_wgs;      /* of which reducers                             */
+    int32_t num_cus;          /* compute units of the device                   */
+    int32_t wgs_per_cu;       /* resident workgroups per CU for this kernel    */
+    int32_t lds_bytes;        /* LDS per workgroup                             */
+    int32_t reduce_grid;      /* workgroups of the standalone reduce kernel    */
+    uint32_t epoch;           /* value the last FUSED run stored in its flags  */
+} gemm_rs_info;
+
+typedef struct gemm_rs_handle gemm_rs_handle;
+
+/* Checks a configuration without touching the GPU (pure host code).
+ * Returns GEMM_RS_OK, GEMM_RS_ERR_INVALID_ARG or GEMM_RS_ERR_UNSUPPORTED_SHAPE. */
+int gemm_rs_validate(const gemm_rs_config *cfg);
+
+/* Resolves the tile and raster group that gemm_rs_create would pick, on the
+ * host only (no GPU).  info fields that need a device are left 0. */
+int gemm_rs_plan(const gemm_rs_config *cfg, gemm_rs_info *info);
+
+/* Host-only enumeration of the tile schedule (the same code the kernels run):
+ * for each slot q < tiles, the destination slice, the tile row in the M x N
+ * partial (units of bm rows counted per slice: d * tile_rows_per_slice + row
+ * inside the slice), the tile column and the ready-flag index.  Any output may
+ * be NULL; n is the capacity of each array (>= tiles). */
+int gemm_rs_plan_slots(const gemm_rs_config *cfg, int32_t *slot_d, int32_t *slot_tm,
+                       int32_t *slot_tn, int32_t *slot_flag, size_t n);
+
+/* Creates a handle on the current HIP device: validates cfg, checks that the
+ * device is gfx950, and allocates the handle-owned device state (ready flags
+ * zeroed, arrival ticket, status word, trace log, and a [S][N] BF16 scratch
+ * used as the local slice when gemm_rs_run gets local_slice == NULL).
+ * On success *out receives the handle; on failure *out is set to NULL. */
+int gemm_rs_create(const gemm_rs_config *cfg, gemm_rs_handle **out);
+
+/* Enqueues one run on `stream` (a hipStream_t; NULL = the null stream) and
+ * returns without waiting.
+ *   mode         GEMM_RS_MODE_*.
+ *   x, w         device inputs (see Layouts); unused by REDUCE_ONLY.
+ *   send         host array of tp-1 device pointers; send[i] receives the
+ *                partial's slice for peer rank p_i.  Unused by REDUCE_ONLY.
+ *   peers        host array of tp-1 device pointers to the peer partials of
+ *                this rank's slice; unused by GEMM_ONLY.
+ *   out          device [S][N]: the reduced slice; unused by GEMM_ONLY.
+ *   local_slice  device [S][N]: this rank's own slice of its partial (written by
+ *                the GEMM, read by the sum); NULL = the handle's scratch.
+ * The caller owns every buffer and keeps it alive until the stream work is
+ * done.  Runs on one handle must not overlap on the device.
+ * M == 0 or N == 0 enqueues nothing; K_local == 0 gives a zero partial. */
+int gemm_rs_run(gemm_rs_handle *h, int32_t mode, const void *x, const void *w,
+                void *const *send, const void *const *peers, void *out,
+                void *local_slice, void *stream);
+
+/* Waits for the handle's last run and returns its device status:
+ * GEMM_RS_OK, or GEMM_RS_ERR_TIMEOUT if a reducer gave up waiting for a ready
+ * flag (the kernel still exits; `out` is then incomplete).  Reading the status
+ * clears it. */
+int gemm_rs_status(gemm_rs_handle *h);
+
+/* Fills *info with the resolved launch parameters of a handle. */
+int gemm_rs_query(gemm_rs_handle *h, gemm_rs_info *info);
+
+/* Copies debug state of the last run to host memory (waits for it first):
+ *   slot_log   if non-NULL, 4 words per schedule slot: the tile's flag index,
+ *              the compute workgroup's ticket, and the 64-bit release time
+ *              (100 MHz counter; low word then high word).  Written only when
+ *              the run had GEMM_RS_DEBUG_TRACE; slot_words >= 4 * tiles.
+ *   flags      if non-NULL, the current value of each ready flag;
+ *              flag_words >= tiles. */
+int gemm_rs_debug_read(gemm_rs_handle *h, uint32_t *slot_log, size_t slot_words,
+                       uint32_t *flags, size_t flag_words);
+
+/* Waits for outstanding work and frees the handle's device state.  NULL is a
+ * no-op. */
+void gemm_rs_destroy(gemm_rs_handle *h);
+
+/* Message for an error code (static storage; for GEMM_RS_ERR_HIP the last HIP
+ * error seen by this thread). */
+const char *gemm_rs_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_RS_H */

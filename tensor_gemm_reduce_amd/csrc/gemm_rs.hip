@@ -1,0 +1,454 @@
+// gemm_rs.hip -- host side of the C ABI declared in include/gemm_rs.h, and the
+// kernel instantiations for gfx950.
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "gemm_rs.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+using namespace gemm_rs;
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_fail(hipError_t e, const char* what)
+{
+    snprintf(g_hip_msg, sizeof g_hip_msg, "%s: %s", what, hipGetErrorString(e));
+    return GEMM_RS_ERR_HIP;
+}
+
+#define HIP_TRY(call)                                   \
+    do {                                                \
+        hipError_t e_ = (call);                         \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+// Tile table: id -> (BM, BN) and the kernel instantiation.
+typedef TileCfg<16, 64, 1, 4, 16> Tile16x64;
+typedef TileCfg<64, 128, 2, 2, 32> Tile64x128;
+typedef TileCfg<128, 128, 2, 2, 32> Tile128x128;
+typedef TileCfg<128, 256, 2, 2, 32> Tile128x256;
+typedef TileCfg<256, 128, 2, 2, 32> Tile256x128;
+typedef TileCfg<256, 256, 2, 2, 32> Tile256x256;
+
+struct TileDesc {
+    int bm, bn, bk, lds_bytes;
+    const void* kernel;
+};
+
+template <class C>
+TileDesc desc()
+{
+    return TileDesc{C::BM, C::BN, C::BK, C::LDS_BYTES, reinterpret_cast<const void*>(&fused_kernel<C>)};
+}
+
+TileDesc tile_desc(int id)
+{
+    switch (id) {
+    case GEMM_RS_TILE_16x64: return desc<Tile16x64>();
+    case GEMM_RS_TILE_64x128: return desc<Tile64x128>();
+    case GEMM_RS_TILE_128x128: return desc<Tile128x128>();
+    case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
+    case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
+    case GEMM_RS_TILE_256x256: return desc<Tile256x256>();
+    default: return TileDesc{0, 0, 0, 0, nullptr};
+    }
+}
+
+// Host-only tile geometry (no kernel pointer needed).
+void tile_shape(int id, int* bm, int* bn)
+{
+    static const int shapes[GEMM_RS_TILE_COUNT][2] = {
+        {0, 0}, {16, 64}, {64, 128}, {128, 128}, {128, 256}, {256, 128}, {256, 256}};
+    *bm = (id > 0 && id < GEMM_RS_TILE_COUNT) ? shapes[id][0] : 0;
+    *bn = (id > 0 && id < GEMM_RS_TILE_COUNT) ? shapes[id][1] : 0;
+}
+
+int auto_tile(const gemm_rs_config& c)
+{
+    const int S = c.M / c.tp;
+    if (S >= 256 && c.N >= 256) return GEMM_RS_TILE_256x256;
+    if (S >= 128 && c.N >= 128) return GEMM_RS_TILE_128x128;
+    if (S >= 64 && c.N >= 128) return GEMM_RS_TILE_64x128;
+    return GEMM_RS_TILE_16x64;
+}
+
+int resolve_tile(const gemm_rs_config& c) { return c.tile == GEMM_RS_TILE_AUTO ? auto_tile(c) : c.tile; }
+
+Geometry geometry_of(const gemm_rs_config& c)
+{
+    int bm, bn;
+    tile_shape(resolve_tile(c), &bm, &bn);
+    int gm = c.group_m;
+    const int S = c.M / c.tp;
+    const int tms = S > 0 ? ceil_div(S, bm) : 0;
+    if (gm <= 0) gm = tms < 8 ? (tms > 0 ? tms : 1) : 8;
+    return make_geometry(c.M, c.N, c.K_local, c.tp, c.rank, bm, bn, 64, gm);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct gemm_rs_handle {
+    gemm_rs_config cfg;
+    Geometry g;
+    int tile_id;
+    TileDesc td;
+    int device;
+    int num_cus;
+    int wgs_per_cu;
+    int grid;
+    int compute_wgs;
+    int reducer_wgs;
+    int reduce_grid;
+    int flag_stride;
+    uint32_t* flags;
+    uint32_t* ticket;
+    int32_t* status;
+    uint32_t* trace;
+    uint16_t* scratch;
+    uint32_t epoch;
+    uint32_t ticket_base;
+    hipStream_t last_stream;
+};
+
+extern "C" {
+
+int gemm_rs_validate(const gemm_rs_config* c)
+{
+    if (!c) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->M < 0 || c->N < 0 || c->K_local < 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->rank < 0 || c->rank >= c->tp) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->tile < 0 || c->tile >= GEMM_RS_TILE_COUNT) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->group_m < 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->num_reducers < -1) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->flag_protocol != GEMM_RS_FLAG_WAVE_FENCE && c->flag_protocol != GEMM_RS_FLAG_WG_RELEASE)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (c->debug_flags & ~GEMM_RS_DEBUG_TRACE) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->watchdog_us < 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->tp != 8) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    if (c->M % c->tp != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    if (c->N % 8 != 0 || c->K_local % 8 != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    // every row-major element offset must fit the kernels' 64-bit arithmetic
+    // and every tile count a 32-bit int
+    const int64_t S = c->M / c->tp;
+    if ((int64_t)c->M * c->K_local > ((int64_t)1 << 40) || (int64_t)c->N * c->K_local > ((int64_t)1 << 40) ||
+        S * (int64_t)c->N > ((int64_t)1 << 40))
+        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    int bm, bn;
+    tile_shape(resolve_tile(*c), &bm, &bn);
+    const int64_t tiles = (int64_t)c->tp * ((S + bm - 1) / bm) * (((int64_t)c->N + bn - 1) / bn);
+    if (tiles > (1 << 30)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    if (c->drop_flag >= 0 && c->drop_flag >= tiles) return GEMM_RS_ERR_INVALID_ARG;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_plan(const gemm_rs_config* c, gemm_rs_info* info)
+{
+    int rc = gemm_rs_validate(c);
+    if (rc != GEMM_RS_OK) return rc;
+    if (!info) return GEMM_RS_ERR_INVALID_ARG;
+    memset(info, 0, sizeof *info);
+    const Geometry g = geometry_of(*c);
+    info->bm = g.bm;
+    info->bn = g.bn;
+    info->bk = g.bk;
+    info->group_m = g.group_m;
+    info->tiles = g.tiles;
+    info->tiles_per_slice = g.ts;
+    info->tile_rows_per_slice = g.tms;
+    info->tile_cols = g.tnc;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_plan_slots(const gemm_rs_config* c, int32_t* slot_d, int32_t* slot_tm, int32_t* slot_tn,
+                       int32_t* slot_flag, size_t n)
+{
+    int rc = gemm_rs_validate(c);
+    if (rc != GEMM_RS_OK) return rc;
+    const Geometry g = geometry_of(*c);
+    if ((size_t)g.tiles > n) return GEMM_RS_ERR_INVALID_ARG;
+    for (int q = 0; q < g.tiles; ++q) {
+        const TileCoord t = decode_slot(g, q);
+        if (slot_d) slot_d[q] = t.d;
+        if (slot_tm) slot_tm[q] = t.d * g.tms + t.tml;
+        if (slot_tn) slot_tn[q] = t.tn;
+        if (slot_flag) slot_flag[q] = t.flag;
+    }
+    return GEMM_RS_OK;
+}
+
+const char* gemm_rs_strerror(int code)
+{
+    switch (code) {
+    case GEMM_RS_OK: return "success";
+    case GEMM_RS_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_RS_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (tp must be 8, M a multiple of tp, N and K_local multiples of 8)";
+    case GEMM_RS_ERR_MISALIGNED: return "buffer not 16-byte aligned";
+    case GEMM_RS_ERR_NO_DEVICE: return "current HIP device is not a gfx950 GPU";
+    case GEMM_RS_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP runtime error";
+    case GEMM_RS_ERR_TIMEOUT: return "a reducer timed out waiting for a tile's ready flag";
+    case GEMM_RS_ERR_NO_MEMORY: return "out of memory";
+    default: return "unknown error";
+    }
+}
+
+static void free_state(gemm_rs_handle* h)
+{
+    if (h->flags) (void)hipFree(h->flags);
+    if (h->ticket) (void)hipFree(h->ticket);
+    if (h->status) (void)hipFree(h->status);
+    if (h->trace) (void)hipFree(h->trace);
+    if (h->scratch) (void)hipFree(h->scratch);
+}
+
+int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
+{
+    if (!out) return GEMM_RS_ERR_INVALID_ARG;
+    *out = nullptr;
+    int rc = gemm_rs_validate(c);
+    if (rc != GEMM_RS_OK) return rc;
+
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_RS_ERR_NO_DEVICE;
+
+    gemm_rs_handle* h = new (std::nothrow) gemm_rs_handle();
+    if (!h) return GEMM_RS_ERR_NO_MEMORY;
+    h->cfg = *c;
+    h->g = geometry_of(*c);
+    h->tile_id = resolve_tile(*c);
+    h->td = tile_desc(h->tile_id);
+    h->device = dev;
+    h->num_cus = prop.multiProcessorCount;
+    h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
+
+    hipError_t e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+    if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, kThreads, h->td.lds_bytes);
+    if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
+    h->wgs_per_cu = occ < 1 ? 1 : occ;
+    h->grid = h->num_cus * h->wgs_per_cu;
+    int red = c->num_reducers;
+    if (red < 0) red = h->grid / 32 > 0 ? h->grid / 32 : 1;
+    if (red >= h->grid) red = h->grid - 1;
+    h->reducer_wgs = red;
+    h->compute_wgs = h->grid - red;
+    h->reduce_grid = h->num_cus * 8;
+
+    const size_t tiles = (size_t)(h->g.tiles > 0 ? h->g.tiles : 1);
+    const size_t slice = (size_t)h->g.S * (size_t)h->g.N;
+    if (hipMalloc(&h->flags, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->ticket, sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->status, 2 * sizeof(int32_t)) != hipSuccess ||
+        hipMalloc(&h->trace, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->scratch, (slice > 0 ? slice : 8) * sizeof(uint16_t)) != hipSuccess) {
+        free_state(h);
+        delete h;
+        return GEMM_RS_ERR_NO_MEMORY;
+    }
+    if (hipMemset(h->flags, 0, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->ticket, 0, sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->status, 0, 2 * sizeof(int32_t)) != hipSuccess ||
+        hipMemset(h->trace, 0, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        free_state(h);
+        delete h;
+        return hip_fail(hipGetLastError(), "hipMemset");
+    }
+    h->epoch = 0;
+    h->ticket_base = 0;
+    h->last_stream = nullptr;
+    *out = h;
+    return GEMM_RS_OK;
+}
+
+static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, void* const* send,
+                      const void* const* peers, void* out, uint16_t* local)
+{
+    memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w);
+    const int r = h->g.rank;
+    for (int d = 0; d < h->g.tp; ++d) {
+        if (d == r)
+            a.dst[d] = local;
+        else
+            a.dst[d] = send ? static_cast<uint16_t*>(send[d < r ? d : d - 1]) : nullptr;
+    }
+    for (int i = 0; i < kPeers; ++i) a.peers[i] = peers ? static_cast<const uint16_t*>(peers[i]) : nullptr;
+    a.out = static_cast<uint16_t*>(out);
+    a.flags = h->flags;
+    a.ticket = h->ticket;
+    a.status = h->status;
+    a.trace = h->trace;
+    a.g = h->g;
+    const int64_t us = h->cfg.watchdog_us > 0 ? h->cfg.watchdog_us : 2000000;
+    a.watchdog_ticks = us * 100;  // 100 MHz real-time counter
+    a.flag_stride = h->flag_stride;
+    a.protocol = h->cfg.flag_protocol;
+    a.drop_flag = h->cfg.drop_flag;
+    a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
+}
+
+static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
+{
+    a.ticket_base = h->ticket_base;
+    if (fused) {
+        a.flags_on = 1;
+        a.num_compute = h->compute_wgs;
+        a.num_reducers = h->reducer_wgs;
+        a.epoch = ++h->epoch;
+    } else {
+        a.flags_on = 0;
+        a.num_compute = h->grid;
+        a.num_reducers = 0;
+        a.epoch = h->epoch;
+    }
+    void* params[] = {&a};
+    HIP_TRY(hipLaunchKernel(h->td.kernel, dim3(h->grid), dim3(kThreads), params, h->td.lds_bytes, s));
+    h->ticket_base += (uint32_t)h->grid;
+    return GEMM_RS_OK;
+}
+
+static int launch_reduce(gemm_rs_handle* h, Args& a, hipStream_t s)
+{
+    const int64_t chunks = (int64_t)h->g.S * h->g.N / 8;
+    int64_t want = (chunks + kThreads - 1) / kThreads;
+    int grid = (int)(want < h->reduce_grid ? want : h->reduce_grid);
+    if (grid < 1) grid = 1;
+    void* params[] = {&a};
+    HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel), dim3(grid), dim3(kThreads), params,
+                            0, s));
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                const void* const* peers, void* out, void* local_slice, void* stream)
+{
+    if (!h) return GEMM_RS_ERR_INVALID_ARG;
+    if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    h->last_stream = s;
+    // an empty slice or no columns: nothing is read or written, buffers may be NULL
+    if (h->g.S == 0 || h->g.N == 0) return GEMM_RS_OK;
+    const bool needs_gemm = mode != GEMM_RS_MODE_REDUCE_ONLY;
+    const bool needs_sum = mode != GEMM_RS_MODE_GEMM_ONLY;
+    uint16_t* local = static_cast<uint16_t*>(local_slice ? local_slice : h->scratch);
+    if (!aligned16(local)) return GEMM_RS_ERR_MISALIGNED;
+    if (needs_gemm) {
+        // with K_local == 0 the inputs are never read and may be NULL
+        if (!send || ((!x || !w) && h->g.K > 0)) return GEMM_RS_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(w)) return GEMM_RS_ERR_MISALIGNED;
+        for (int i = 0; i < kPeers; ++i) {
+            if (!send[i]) return GEMM_RS_ERR_INVALID_ARG;
+            if (!aligned16(send[i])) return GEMM_RS_ERR_MISALIGNED;
+        }
+    }
+    if (needs_sum) {
+        if (!out || !peers) return GEMM_RS_ERR_INVALID_ARG;
+        if (!aligned16(out)) return GEMM_RS_ERR_MISALIGNED;
+        for (int i = 0; i < kPeers; ++i) {
+            if (!peers[i]) return GEMM_RS_ERR_INVALID_ARG;
+            if (!aligned16(peers[i])) return GEMM_RS_ERR_MISALIGNED;
+        }
+    }
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != h->device) return GEMM_RS_ERR_INVALID_ARG;
+
+    Args a;
+    fill_args(h, a, x, w, send, peers, out, local);
+    int rc = GEMM_RS_OK;
+    switch (mode) {
+    case GEMM_RS_MODE_FUSED: rc = launch_gemm(h, a, true, s); break;
+    case GEMM_RS_MODE_GEMM_ONLY: rc = launch_gemm(h, a, false, s); break;
+    case GEMM_RS_MODE_REDUCE_ONLY: rc = launch_reduce(h, a, s); break;
+    case GEMM_RS_MODE_SEQUENTIAL:
+        rc = launch_gemm(h, a, false, s);
+        if (rc == GEMM_RS_OK) rc = launch_reduce(h, a, s);
+        break;
+    }
+    return rc;
+}
+
+int gemm_rs_status(gemm_rs_handle* h)
+{
+    if (!h) return GEMM_RS_ERR_INVALID_ARG;
+    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    int32_t st[2] = {0, 0};
+    HIP_TRY(hipMemcpy(st, h->status, sizeof st, hipMemcpyDeviceToHost));
+    if (st[0] != 0) {
+        HIP_TRY(hipMemset(h->status, 0, sizeof st));
+        HIP_TRY(hipDeviceSynchronize());
+        return st[0];
+    }
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
+{
+    if (!h || !info) return GEMM_RS_ERR_INVALID_ARG;
+    memset(info, 0, sizeof *info);
+    info->bm = h->g.bm;
+    info->bn = h->g.bn;
+    info->bk = h->g.bk;
+    info->group_m = h->g.group_m;
+    info->tiles = h->g.tiles;
+    info->tiles_per_slice = h->g.ts;
+    info->tile_rows_per_slice = h->g.tms;
+    info->tile_cols = h->g.tnc;
+    info->grid = h->grid;
+    info->compute_wgs = h->compute_wgs;
+    info->reducer_wgs = h->reducer_wgs;
+    info->num_cus = h->num_cus;
+    info->wgs_per_cu = h->wgs_per_cu;
+    info->lds_bytes = h->td.lds_bytes;
+    info->reduce_grid = h->reduce_grid;
+    info->epoch = h->epoch;
+    return GEMM_RS_OK;
+}
+
+int gemm_rs_debug_read(gemm_rs_handle* h, uint32_t* slot_log, size_t slot_words, uint32_t* flags,
+                       size_t flag_words)
+{
+    if (!h) return GEMM_RS_ERR_INVALID_ARG;
+    const size_t tiles = (size_t)h->g.tiles;
+    if (slot_log && slot_words < 4 * tiles) return GEMM_RS_ERR_INVALID_ARG;
+    if (flags && flag_words < tiles) return GEMM_RS_ERR_INVALID_ARG;
+    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    if (slot_log && tiles)
+        HIP_TRY(hipMemcpy(slot_log, h->trace, 4 * tiles * sizeof(uint32_t), hipMemcpyDeviceToHost));
+    if (flags && tiles) {
+        if (h->flag_stride == 1) {
+            HIP_TRY(hipMemcpy(flags, h->flags, tiles * sizeof(uint32_t), hipMemcpyDeviceToHost));
+        } else {
+            HIP_TRY(hipMemcpy2D(flags, sizeof(uint32_t), h->flags, h->flag_stride * sizeof(uint32_t),
+                                sizeof(uint32_t), tiles, hipMemcpyDeviceToHost));
+        }
+    }
+    return GEMM_RS_OK;
+}
+
+void gemm_rs_destroy(gemm_rs_handle* h)
+{
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    free_state(h);
+    delete h;
+}
+
+}  // extern "C"
