@@ -99,7 +99,8 @@ class Case:
 
 
 def time_each(fn, warmup, iters):
-    """Per-launch durations (us) from event pairs on the current stream."""
+    """Per-launch durations (us) from event pairs on the current stream (host
+    launch overhead included: for probes only)."""
     import torch
 
     for _ in range(warmup):
@@ -114,8 +115,50 @@ def time_each(fn, warmup, iters):
     return [s.elapsed_time(e) * 1e3 for s, e in ev]
 
 
+class Replay:
+    """fn captured `n` times back to back into one HIP graph.  The library keeps
+    its run state on the device, so every replay is n new runs; replaying
+    removes the host launch gaps that would dominate microsecond kernels."""
+
+    def __init__(self, fn, n):
+        import torch
+
+        self.n = n
+        fn()  # warm the code path outside capture
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.Stream()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=self.stream):
+            for _ in range(n):
+                fn()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
+
+
+def time_replays(fn, warmup, iters, per_graph=10):
+    """Median over ceil(iters / per_graph) replays of the per-launch time (us)
+    of a graph of per_graph back-to-back launches."""
+    import torch
+
+    g = Replay(fn, per_graph)
+    reps = max(1, -(-iters // per_graph))
+    for _ in range(max(1, -(-warmup // per_graph))):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for s, e in ev:
+        s.record(stream)
+        g.replay()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) * 1e3 / per_graph for s, e in ev]
+
+
 def summary(us):
-    q = statistics.quantiles(us, n=10) if len(us) >= 10 else [min(us)] * 9 + [max(us)]
+    q = statistics.quantiles(us, n=10) if len(us) >= 2 else [us[0]] * 9
     return {"median_us": statistics.median(us), "mean_us": statistics.fmean(us), "p10_us": q[0],
             "p90_us": q[-1]}
 
@@ -123,11 +166,11 @@ def summary(us):
 def measure_case(c: Case, warmup, iters):
     gr = c.gr
     cfg = c.cfg
-    fused = summary(time_each(lambda: c.run(gr.MODE_FUSED), warmup, iters))
-    gemm = summary(time_each(lambda: c.run(gr.MODE_GEMM_ONLY), warmup, iters))
-    red = summary(time_each(lambda: c.run(gr.MODE_REDUCE_ONLY), warmup, iters))
-    seq = summary(time_each(lambda: c.run(gr.MODE_SEQUENTIAL), warmup, iters))
-    mm = summary(time_each(c.matmul, warmup, iters))
+    fused = summary(time_replays(lambda: c.run(gr.MODE_FUSED), warmup, iters))
+    gemm = summary(time_replays(lambda: c.run(gr.MODE_GEMM_ONLY), warmup, iters))
+    red = summary(time_replays(lambda: c.run(gr.MODE_REDUCE_ONLY), warmup, iters))
+    seq = summary(time_replays(lambda: c.run(gr.MODE_SEQUENTIAL), warmup, iters))
+    mm = summary(time_replays(c.matmul, warmup, iters))
     st = c.op.status()
     if st != gr.OK:
         raise RuntimeError(f"{c.name}: device status {gr.gemm_rs_strerror(st)}")
@@ -243,25 +286,26 @@ def main():
     check = check_case(c) if args.check else None
     log(f"[{args.workload}] parity check: {check}")
 
-    # timed region: exactly K fused steps, synchronized on both sides
-    for _ in range(args.warmup):
-        c.run(gr.MODE_FUSED)
+    # timed region: exactly K fused steps (one replay of a graph of K
+    # back-to-back launches), synchronized on both sides; HIP events on the
+    # replay stream give the average launch duration
+    steps = Replay(lambda: c.run(gr.MODE_FUSED), args.steps)
+    for _ in range(max(1, -(-args.warmup // args.steps))):
+        steps.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, e in evs:
-        s.record(stream)
-        c.run(gr.MODE_FUSED)
-        e.record(stream)
+    ev0.record(stream)
+    steps.replay()
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st = c.op.status()
     if st != gr.OK:
         raise RuntimeError(f"device status {gr.gemm_rs_strerror(st)}")
-    per_launch = [s.elapsed_time(e) * 1e3 for s, e in evs]
-    mean_us = statistics.fmean(per_launch)
+    mean_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
     ms_per_step = wall / args.steps * 1e3
     value = cfg.flops * args.steps / wall * 1e-12
     log(f"[{args.workload}] fused: {mean_us:.2f} us/launch (events), {ms_per_step * 1e3:.2f} us/step (wall)")

@@ -37,15 +37,19 @@
  *                              layout of a linear layer's weight; the product
  *                              is X_r * W_r with W_r = w^T)
  *   send[i], peers[i], out, local_slice: [S][N] with S = M / tp
- * Every pointer must be 16-byte aligned; K_local and N must be multiples of 8.
+ * Every pointer must be 16-byte aligned; K_local and N must be multiples of 8;
+ * M * K_local and N * K_local must stay below 2^30 elements.
  *
  * Errors: every function returns GEMM_RS_OK (0) or a negative GEMM_RS_ERR_*
  * code; nothing aborts and nothing throws across the ABI.  gemm_rs_strerror
  * gives a message (for GEMM_RS_ERR_HIP it includes the last HIP error).
  *
  * Threading: a handle may be used from one host thread at a time, and runs on
- * one handle must not overlap on the device (they share the ready flags):
- * issue them on one stream, or synchronise between streams.
+ * one handle must not overlap on the device (they share the ready flags and
+ * the handle's device counters): issue them on one stream, or synchronise
+ * between streams.  The run epoch and all counters live in device memory and
+ * are advanced by the kernel itself, so runs may be captured into a HIP graph
+ * and replayed; each replay is a new run.
  */
 #ifndef GEMM_RS_H
 #define GEMM_RS_H
@@ -122,7 +126,10 @@ typedef struct gemm_rs_info {
     int32_t wgs_per_cu;       /* resident workgroups per CU for this kernel    */
     int32_t lds_bytes;        /* LDS per workgroup                             */
     int32_t reduce_grid;      /* workgroups of the standalone reduce kernel    */
-    uint32_t epoch;           /* value the last FUSED run stored in its flags  */
+    int32_t xcd_split;        /* how a round of slots is split over the 8 XCDs:
+                                 0 contiguous blocks, 1 every 8th slot         */
+    uint32_t epoch;           /* value the last FUSED run stored in its flags
+                                 (read from the device; waits for the stream) */
 } gemm_rs_info;
 
 typedef struct gemm_rs_handle gemm_rs_handle;

@@ -2,6 +2,7 @@
 // kernel instantiations for gfx950.
 #include <hip/hip_runtime.h>
 
+#include <stddef.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -30,23 +31,38 @@ int hip_fail(hipError_t e, const char* what)
         if (e_ != hipSuccess) return hip_fail(e_, #call); \
     } while (0)
 
-// Tile table: id -> (BM, BN) and the kernel instantiation.
-typedef TileCfg<16, 64, 1, 4, 16> Tile16x64;
-typedef TileCfg<64, 128, 2, 2, 32> Tile64x128;
-typedef TileCfg<128, 128, 2, 2, 32> Tile128x128;
-typedef TileCfg<128, 256, 2, 2, 32> Tile128x256;
-typedef TileCfg<256, 128, 2, 2, 32> Tile256x128;
-typedef TileCfg<256, 256, 2, 2, 32> Tile256x256;
+// Tile table: id -> tile shape, stage depth and the kernel instantiation.
+//                 BM   BN   BK  NS  waves  MFMA
+typedef TileCfg<16, 64, 128, 2, 1, 4, 16> Tile16x64;
+typedef TileCfg<64, 128, 64, 2, 2, 2, 32> Tile64x128;
+typedef TileCfg<128, 128, 32, 3, 2, 2, 32> Tile128x128;
+typedef TileCfg<128, 256, 32, 4, 2, 2, 32> Tile128x256;
+typedef TileCfg<256, 128, 32, 4, 2, 2, 32> Tile256x128;
+typedef TileCfg<256, 256, 32, 4, 2, 2, 32> Tile256x256;
 
 struct TileDesc {
-    int bm, bn, bk, lds_bytes;
-    const void* kernel;
+    int bm, bn, bk;
+    int lds_bytes;           // fused kernel: stages + reduce-engine slots
+    int gemm_lds_bytes;      // GEMM-only kernel: stages
+    const void* kernel;      // fused: compute + reducers, flags
+    const void* gemm_kernel; // the same GEMM without flags or reduction
 };
 
 template <class C>
 TileDesc desc()
 {
-    return TileDesc{C::BM, C::BN, C::BK, C::LDS_BYTES, reinterpret_cast<const void*>(&fused_kernel<C>)};
+    static_assert(C::LDS_BYTES + kEngineBytes <= 160 * 1024 - 64, "LDS of one workgroup");
+    // tiles that cannot fit two workgroups per CU get the occupancy-1 kernel
+    const void* k;
+    const void* g;
+    if constexpr (C::LDS_BYTES + kEngineBytes > 80 * 1024 - 64) {
+        k = reinterpret_cast<const void*>(&fused_kernel_1w<C, true>);
+        g = reinterpret_cast<const void*>(&fused_kernel_1w<C, false>);
+    } else {
+        k = reinterpret_cast<const void*>(&fused_kernel<C, true>);
+        g = reinterpret_cast<const void*>(&fused_kernel<C, false>);
+    }
+    return TileDesc{C::BM, C::BN, C::BK, C::LDS_BYTES + kEngineBytes, C::LDS_BYTES, k, g};
 }
 
 TileDesc tile_desc(int id)
@@ -58,7 +74,7 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256>();
-    default: return TileDesc{0, 0, 0, 0, nullptr};
+    default: return TileDesc{0, 0, 0, 0, 0, nullptr, nullptr};
     }
 }
 
@@ -110,15 +126,48 @@ struct gemm_rs_handle {
     int reducer_wgs;
     int reduce_grid;
     int flag_stride;
+    int strided;
     uint32_t* flags;
-    uint32_t* ticket;
-    int32_t* status;
+    DeviceState* state;
     uint32_t* trace;
     uint16_t* scratch;
-    uint32_t epoch;
-    uint32_t ticket_base;
     hipStream_t last_stream;
 };
+
+namespace {
+
+// Distinct tile rows plus tile columns that one XCD touches in the first round
+// of the schedule (a proxy for its L2 footprint per K step) under the
+// contiguous or the strided split of the round.
+long xcd_footprint(const Geometry& g, int grid, int R, bool strided)
+{
+    long worst = 0;
+    const int C = grid - R;
+    const int n = C < g.tiles ? C : g.tiles;
+    for (int x = 0; x < kGroups; ++x) {
+        const int gq = grid / kGroups, rq = R / kGroups, rr = R % kGroups;
+        const int cnt = gq - rq - (x < rr ? 1 : 0);
+        const int base = x * (gq - rq) - (x < rr ? x : rr);
+        // at most 64 tile rows and 512 columns are tracked exactly
+        unsigned char rowseen[8 * 64] = {0};
+        static thread_local unsigned char colseen[512];
+        memset(colseen, 0, sizeof colseen);
+        long rowsn = 0, colsn = 0;
+        for (int l = 0; l < cnt; ++l) {
+            const int q = strided ? l * kGroups + x : base + l;
+            if (q >= n) continue;
+            const TileCoord t = decode_slot(g, q);
+            const int rk = (t.d * g.tms + t.tml) % (8 * 64), ck = t.tn % 512;
+            if (!rowseen[rk]) { rowseen[rk] = 1; ++rowsn; }
+            if (!colseen[ck]) { colseen[ck] = 1; ++colsn; }
+        }
+        const long fp = rowsn * g.bm + colsn * g.bn;
+        if (fp > worst) worst = fp;
+    }
+    return worst;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -144,6 +193,12 @@ int gemm_rs_validate(const gemm_rs_config* c)
     const int64_t S = c->M / c->tp;
     if ((int64_t)c->M * c->K_local > ((int64_t)1 << 40) || (int64_t)c->N * c->K_local > ((int64_t)1 << 40) ||
         S * (int64_t)c->N > ((int64_t)1 << 40))
+        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    // the reduce engine addresses the slice with 32-bit element offsets
+    if ((int64_t)(c->M / c->tp) * c->N >= ((int64_t)1 << 31)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    // X_r and W_r are read through buffer resources with 31-bit byte offsets
+    if ((int64_t)c->M * c->K_local * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)c->N * c->K_local * 2 >= ((int64_t)1 << 31))
         return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     int bm, bn;
     tile_shape(resolve_tile(*c), &bm, &bn);
@@ -206,8 +261,7 @@ const char* gemm_rs_strerror(int code)
 static void free_state(gemm_rs_handle* h)
 {
     if (h->flags) (void)hipFree(h->flags);
-    if (h->ticket) (void)hipFree(h->ticket);
-    if (h->status) (void)hipFree(h->status);
+    if (h->state) (void)hipFree(h->state);
     if (h->trace) (void)hipFree(h->trace);
     if (h->scratch) (void)hipFree(h->scratch);
 }
@@ -236,24 +290,32 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
 
     hipError_t e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                h->td.gemm_lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     int occ = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, kThreads, h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
     h->wgs_per_cu = occ < 1 ? 1 : occ;
-    h->grid = h->num_cus * h->wgs_per_cu;
-    int red = c->num_reducers;
-    if (red < 0) red = h->grid / 32 > 0 ? h->grid / 32 : 1;
+    // a whole number of workgroups per XCD group
+    h->grid = (h->num_cus * h->wgs_per_cu) / kGroups * kGroups;
+    if (h->grid < kGroups) h->grid = kGroups;
+    // automatic: no dedicated reducers, the compute waves run the reduce engine
+    int red = c->num_reducers < 0 ? 0 : c->num_reducers;
     if (red >= h->grid) red = h->grid - 1;
     h->reducer_wgs = red;
     h->compute_wgs = h->grid - red;
     h->reduce_grid = h->num_cus * 8;
+    h->strided = (h->reducer_wgs % kGroups == 0 && h->g.tiles > 0 &&
+                  xcd_footprint(h->g, h->grid, h->reducer_wgs, true) <
+                      xcd_footprint(h->g, h->grid, h->reducer_wgs, false))
+                     ? 1 : 0;
 
     const size_t tiles = (size_t)(h->g.tiles > 0 ? h->g.tiles : 1);
     const size_t slice = (size_t)h->g.S * (size_t)h->g.N;
     if (hipMalloc(&h->flags, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc(&h->ticket, sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc(&h->status, 2 * sizeof(int32_t)) != hipSuccess ||
+        hipMalloc(&h->state, sizeof(DeviceState)) != hipSuccess ||
         hipMalloc(&h->trace, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->scratch, (slice > 0 ? slice : 8) * sizeof(uint16_t)) != hipSuccess) {
         free_state(h);
@@ -261,16 +323,13 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
         return GEMM_RS_ERR_NO_MEMORY;
     }
     if (hipMemset(h->flags, 0, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
-        hipMemset(h->ticket, 0, sizeof(uint32_t)) != hipSuccess ||
-        hipMemset(h->status, 0, 2 * sizeof(int32_t)) != hipSuccess ||
+        hipMemset(h->state, 0, sizeof(DeviceState)) != hipSuccess ||
         hipMemset(h->trace, 0, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_state(h);
         delete h;
         return hip_fail(hipGetLastError(), "hipMemset");
     }
-    h->epoch = 0;
-    h->ticket_base = 0;
     h->last_stream = nullptr;
     *out = h;
     return GEMM_RS_OK;
@@ -292,10 +351,12 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     for (int i = 0; i < kPeers; ++i) a.peers[i] = peers ? static_cast<const uint16_t*>(peers[i]) : nullptr;
     a.out = static_cast<uint16_t*>(out);
     a.flags = h->flags;
-    a.ticket = h->ticket;
-    a.status = h->status;
+    a.state = h->state;
     a.trace = h->trace;
     a.g = h->g;
+    a.x_bytes = (uint32_t)((int64_t)h->g.M * h->g.K * 2);
+    a.w_bytes = (uint32_t)((int64_t)h->g.N * h->g.K * 2);
+    a.strided = h->strided;
     const int64_t us = h->cfg.watchdog_us > 0 ? h->cfg.watchdog_us : 2000000;
     a.watchdog_ticks = us * 100;  // 100 MHz real-time counter
     a.flag_stride = h->flag_stride;
@@ -306,21 +367,14 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
 {
-    a.ticket_base = h->ticket_base;
-    if (fused) {
-        a.flags_on = 1;
-        a.num_compute = h->compute_wgs;
-        a.num_reducers = h->reducer_wgs;
-        a.epoch = ++h->epoch;
-    } else {
-        a.flags_on = 0;
-        a.num_compute = h->grid;
-        a.num_reducers = 0;
-        a.epoch = h->epoch;
-    }
+    a.fused = fused ? 1 : 0;
+    a.num_compute = fused ? h->compute_wgs : h->grid;
+    a.num_reducers = fused ? h->reducer_wgs : 0;
+    // GEMM_ONLY has no reducers, so its groups always split evenly
+    if (!fused) a.strided = h->strided;
     void* params[] = {&a};
-    HIP_TRY(hipLaunchKernel(h->td.kernel, dim3(h->grid), dim3(kThreads), params, h->td.lds_bytes, s));
-    h->ticket_base += (uint32_t)h->grid;
+    HIP_TRY(hipLaunchKernel(fused ? h->td.kernel : h->td.gemm_kernel, dim3(h->grid), dim3(kThreads), params,
+                            fused ? h->td.lds_bytes : h->td.gemm_lds_bytes, s));
     return GEMM_RS_OK;
 }
 
@@ -390,9 +444,10 @@ int gemm_rs_status(gemm_rs_handle* h)
     if (!h) return GEMM_RS_ERR_INVALID_ARG;
     HIP_TRY(hipStreamSynchronize(h->last_stream));
     int32_t st[2] = {0, 0};
-    HIP_TRY(hipMemcpy(st, h->status, sizeof st, hipMemcpyDeviceToHost));
+    char* dev_status = reinterpret_cast<char*>(h->state) + offsetof(DeviceState, status);
+    HIP_TRY(hipMemcpy(st, dev_status, sizeof st, hipMemcpyDeviceToHost));
     if (st[0] != 0) {
-        HIP_TRY(hipMemset(h->status, 0, sizeof st));
+        HIP_TRY(hipMemset(dev_status, 0, sizeof st));
         HIP_TRY(hipDeviceSynchronize());
         return st[0];
     }
@@ -418,7 +473,11 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->wgs_per_cu = h->wgs_per_cu;
     info->lds_bytes = h->td.lds_bytes;
     info->reduce_grid = h->reduce_grid;
-    info->epoch = h->epoch;
+    info->xcd_split = h->strided;
+    DeviceState ds;
+    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    HIP_TRY(hipMemcpy(&ds, h->state, sizeof ds, hipMemcpyDeviceToHost));
+    info->epoch = ds.epoch;
     return GEMM_RS_OK;
 }
 

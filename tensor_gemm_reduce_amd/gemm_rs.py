@@ -61,7 +61,7 @@ class gemm_rs_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "group_m", "tiles", "tiles_per_slice", "tile_rows_per_slice",
         "tile_cols", "grid", "compute_wgs", "reducer_wgs", "num_cus", "wgs_per_cu",
-        "lds_bytes", "reduce_grid")] + [("epoch", ctypes.c_uint32)]
+        "lds_bytes", "reduce_grid", "xcd_split")] + [("epoch", ctypes.c_uint32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -16,6 +16,10 @@ from gpu_util import (Buffers, SENTINEL, assert_close_partial, host, max_rel, or
 
 pytestmark = pytest.mark.gpu
 
+# reducers: 0 = the reduce engine inside the compute waves (default),
+# 8 = dedicated reducer workgroups
+REDUCERS = [0, 8]
+
 
 def _op(cfg, M=None, **kw):
     M = cfg.M if M is None else M
@@ -33,22 +37,24 @@ def _full_compare(cfg, mode, rank, **kw):
 
 # ------------------------------------------------------------------ exact (integer inputs)
 
+@pytest.mark.parametrize("red", REDUCERS)
 @pytest.mark.parametrize("rank", range(8))
-def test_tiny_integer_bit_exact_all_ranks(rank):
+def test_tiny_integer_bit_exact_all_ranks(rank, red):
     cfg = synthetic.CONFIGS["tiny"]
-    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", rank)
+    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", rank, num_reducers=red)
     for i in range(7):
         assert np.array_equal(host(b.send[i]), send_o[i]), f"send[{i}]"
     assert np.array_equal(host(b.local), local_o)
     assert np.array_equal(host(b.out), out_o)
 
 
+@pytest.mark.parametrize("red", REDUCERS)
 @pytest.mark.parametrize("tile", ["16x64", "64x128", "128x128", "128x256", "256x128", "256x256"])
-def test_every_tile_config_integer_bit_exact(tile):
+def test_every_tile_config_integer_bit_exact(tile, red):
     # ragged: S = 264 is not a multiple of any BM > 8 and N = 392 of no BN;
     # K_local = 136 leaves a partial last K step
     cfg = synthetic.Config("ragged", 5, 8 * 264, 392, 136)
-    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", 5, tile=tile)
+    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", 5, tile=tile, num_reducers=red)
     for i in range(7):
         assert np.array_equal(host(b.send[i]), send_o[i]), f"send[{i}]"
     assert np.array_equal(host(b.local), local_o)
@@ -83,12 +89,13 @@ def test_reduce_scatter_invariant_consistent_peers():
 
 # ------------------------------------------------------------------ random inputs, full compare
 
+@pytest.mark.parametrize("red", REDUCERS)
 @pytest.mark.parametrize("name", ["tiny", "o_proj"])
 @pytest.mark.parametrize("mode", ["normal", "balanced"])
-def test_full_compare_within_tolerance(name, mode):
+def test_full_compare_within_tolerance(name, mode, red):
     cfg = synthetic.CONFIGS[name]
     rank = 5
-    op, b, (x, w, peers), (send_o, local_o, out_o) = _full_compare(cfg, mode, rank)
+    op, b, (x, w, peers), (send_o, local_o, out_o) = _full_compare(cfg, mode, rank, num_reducers=red)
     S = cfg.S
     rows = np.arange(S)
     for i in range(7):
@@ -105,13 +112,15 @@ def test_full_compare_within_tolerance(name, mode):
 
 # ------------------------------------------------------------------ full shapes, sampled rows
 
+@pytest.mark.parametrize("red", [-1, 8])
 @pytest.mark.parametrize("name", ["o_proj", "down_proj", "mixtral_down", "large_prefill"])
 @pytest.mark.parametrize("mode", ["normal", "integer"])
-def test_benchmark_shapes_sampled_rows(name, mode):
+def test_benchmark_shapes_sampled_rows(name, mode, red):
+    # red=-1: the launch configuration the benchmark times
     cfg = synthetic.CONFIGS[name]
     rank = 5
     x, w, peers = synthetic.make_inputs(cfg, mode)
-    op = _op(cfg, rank=rank)
+    op = _op(cfg, rank=rank, num_reducers=red)
     b = Buffers(x, w, peers, cfg.S, cfg.N)
     run(op, b)
     rng = np.random.default_rng(1)
@@ -158,8 +167,9 @@ def test_modes_agree_bit_exactly():
 
 
 @pytest.mark.parametrize("kw", [
-    dict(flag_protocol=gr.FLAG_WG_RELEASE), dict(flag_stride=32), dict(num_reducers=1),
-    dict(num_reducers=64), dict(group_m=1), dict(tile="128x128", group_m=3),
+    dict(flag_stride=32), dict(num_reducers=1), dict(num_reducers=64), dict(num_reducers=0, group_m=1),
+    dict(num_reducers=0, tile="128x128", group_m=3), dict(num_reducers=0, tile="256x256"),
+    dict(num_reducers=8, flag_stride=32, tile="128x256"),
 ])
 def test_knobs_keep_results(kw):
     cfg = synthetic.CONFIGS["mixtral_down"]

@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
     ("tiny", None, {}),
     ("o_proj", None, {}),
     ("mixtral_down", 2048, dict(tile="128x128", group_m=3)),
-    ("down_proj", None, dict(flag_protocol=gr.FLAG_WG_RELEASE, flag_stride=32)),
+    ("down_proj", None, dict(flag_stride=32)),
+    ("down_proj", None, dict(num_reducers=8)),
 ])
 def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
     cfg = synthetic.CONFIGS[name]
@@ -34,10 +35,21 @@ def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
         assert np.array_equal(log[:, 0].astype(np.int64), sched["flag"].astype(np.int64))
         # every ready flag holds this run's epoch
         assert np.all(flags == epoch)
-        # static slot distribution: compute workgroup c took slots c, c+C, ...
+        # static slot distribution: the l-th compute workgroup of XCD group x
+        # holds position p of every round of C slots, p = l*8 + x (strided
+        # split) or the group's block offset + l (contiguous split)
         C = info.compute_wgs
         q = np.arange(info.tiles)
-        assert np.array_equal(log[:, 1].astype(np.int64), q % C)
+        grp = (log[:, 1] >> 16).astype(np.int64)
+        loc = (log[:, 1] & 0xFFFF).astype(np.int64)
+        if info.xcd_split:
+            pos = loc * 8 + grp
+        else:
+            gq = info.grid // 8
+            rq, rr = divmod(info.reducer_wgs, 8)
+            pos = grp * (gq - rq) - np.minimum(grp, rr) + loc
+        assert np.all(grp < 8)
+        assert np.array_equal(pos, q % C)
         # per compute workgroup, releases happen in slot order
         stamp = log[:, 2].astype(np.uint64) | (log[:, 3].astype(np.uint64) << np.uint64(32))
         for c in range(min(C, info.tiles)):
@@ -45,14 +57,16 @@ def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
             assert np.all(s[1:] >= s[:-1]), c
 
 
-def test_watchdog_reports_a_dropped_flag_and_kernel_exits():
+@pytest.mark.parametrize("red", [0, 8])
+def test_watchdog_reports_a_dropped_flag_and_kernel_exits(red):
     cfg = synthetic.CONFIGS["tiny"]
     rank = 2
     x, w, peers = synthetic.make_inputs(cfg, "integer")
     plan = gr.gemm_rs_plan(gr.make_config(cfg.M, cfg.N, cfg.K_local, rank=rank))
     sched = oracle.schedule(cfg.M, cfg.N, 8, rank, plan.bm, plan.bn, plan.group_m)
     dropped = int(sched["flag"][0])  # first tile of the own slice
-    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, drop_flag=dropped, watchdog_us=2000)
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, drop_flag=dropped, watchdog_us=2000,
+                   num_reducers=red)
     b = Buffers(x, w, peers, cfg.S, cfg.N)
     run(op, b, check_status=False)
     assert op.status() == gr.ERR_TIMEOUT
@@ -60,9 +74,13 @@ def test_watchdog_reports_a_dropped_flag_and_kernel_exits():
     # the routed partial is still complete; only the timed-out tile's sum is missing
     send_o, local_o, out_o = oracle.gemm_rs(x, w, peers, tp=8, rank=rank)
     assert np.array_equal(host(b.local), local_o)
-    r0, c0 = 0, 0
+    # the dropped tile is the first own-slice tile: rows [0, bm), columns [0, bn)
     got = host(b.out)
-    assert np.all(got[r0:r0 + plan.bm, c0:c0 + plan.bn] == SENTINEL)
+    assert np.all(got[:plan.bm, :plan.bn] == SENTINEL)
+    # every other tile of the slice was still summed
+    mask = np.ones(got.shape, bool)
+    mask[:plan.bm, :plan.bn] = False
+    assert np.array_equal(got[mask], out_o[mask])
     # a fresh handle on the same buffers runs normally afterwards
     op2 = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank)
     run(op2, b)
@@ -81,7 +99,8 @@ def test_alternating_inputs_never_read_stale_tiles():
     want = [dev(oracle.gemm_rs(x, w, p, 8, rank)[2]) for x, w, p in ins]
     bufs = [Buffers(x, w, p, base.S, base.N) for x, w, p in ins]
     shared_send, shared_local, shared_out = bufs[0].send, bufs[0].local, bufs[0].out
-    for kw in (dict(), dict(flag_protocol=gr.FLAG_WG_RELEASE), dict(num_reducers=1)):
+    for kw in (dict(num_reducers=0), dict(num_reducers=0, tile="128x128"), dict(num_reducers=8),
+               dict(num_reducers=1)):
         op = gr.GemmRS(base.M, base.N, base.K_local, rank=rank, **kw)
         bad = 0
         for it in range(40):
@@ -94,3 +113,37 @@ def test_alternating_inputs_never_read_stale_tiles():
         torch.cuda.synchronize()
         assert op.status() == gr.OK
         assert bad == 0, (kw, bad)
+
+
+@pytest.mark.parametrize("red", [0, 8])
+def test_graph_replays_match_eager(red):
+    """Runs captured into a HIP graph and replayed are new runs each time (the
+    epoch and counters live on the device): every replay, with eager runs and
+    synchronisations in between, must give the eager result."""
+    cfg = synthetic.CONFIGS["o_proj"]
+    rank = 6
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    want = dev(oracle.gemm_rs(x, w, peers, 8, rank)[2])
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, num_reducers=red)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    fill = np.array(SENTINEL, np.uint16).view(np.int16).item()
+    run(op, b)
+    assert torch.equal(b.out, want)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local)
+    torch.cuda.synchronize()
+    for it in range(6):
+        b.out.fill_(fill)
+        b.local.fill_(fill)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert op.status() == gr.OK
+        assert torch.equal(b.out, want), it
+        if it % 2:
+            run(op, b)  # an eager run between replays
+            assert torch.equal(b.out, want)
+    assert gr.gemm_rs_query(op.h).epoch == 1 + 6 + 3
