@@ -38,10 +38,11 @@ typedef TileCfg<64, 128, 64, 2, 2, 2, 32> Tile64x128;
 typedef TileCfg<128, 128, 32, 3, 2, 2, 32> Tile128x128;
 typedef TileCfg<128, 256, 32, 4, 2, 2, 32> Tile128x256;
 typedef TileCfg<256, 128, 32, 4, 2, 2, 32> Tile256x128;
-typedef TileCfg<256, 256, 32, 4, 2, 2, 32> Tile256x256;
+typedef TileCfg<256, 256, 32, 4, 2, 4, 32> Tile256x256;
 
 struct TileDesc {
     int bm, bn, bk;
+    int threads;             // workgroup size
     int lds_bytes;           // fused kernel: stages + reduce-engine slots
     int gemm_lds_bytes;      // GEMM-only kernel: stages
     const void* kernel;      // fused: compute + reducers, flags
@@ -51,18 +52,24 @@ struct TileDesc {
 template <class C>
 TileDesc desc()
 {
-    static_assert(C::LDS_BYTES + kEngineBytes <= 160 * 1024 - 64, "LDS of one workgroup");
-    // tiles that cannot fit two workgroups per CU get the occupancy-1 kernel
+    constexpr int engine = C::WAVES * kEngineSlots * kEngineSlotBytes;
+    static_assert(C::LDS_BYTES + engine <= 160 * 1024 - 64, "LDS of one workgroup");
+    // eight-wave tiles run one workgroup per CU with two waves per SIMD; four-
+    // wave tiles that cannot fit two workgroups per CU get the occupancy-1
+    // kernel (one wave per SIMD, the whole register file)
     const void* k;
     const void* g;
-    if constexpr (C::LDS_BYTES + kEngineBytes > 80 * 1024 - 64) {
+    if constexpr (C::WAVES == 8) {
+        k = reinterpret_cast<const void*>(&fused_kernel_8w<C, true>);
+        g = reinterpret_cast<const void*>(&fused_kernel_8w<C, false>);
+    } else if constexpr (C::LDS_BYTES + engine > 80 * 1024 - 64) {
         k = reinterpret_cast<const void*>(&fused_kernel_1w<C, true>);
         g = reinterpret_cast<const void*>(&fused_kernel_1w<C, false>);
     } else {
         k = reinterpret_cast<const void*>(&fused_kernel<C, true>);
         g = reinterpret_cast<const void*>(&fused_kernel<C, false>);
     }
-    return TileDesc{C::BM, C::BN, C::BK, C::LDS_BYTES + kEngineBytes, C::LDS_BYTES, k, g};
+    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::LDS_BYTES + engine, C::LDS_BYTES, k, g};
 }
 
 TileDesc tile_desc(int id)
@@ -74,7 +81,7 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256>();
-    default: return TileDesc{0, 0, 0, 0, 0, nullptr, nullptr};
+    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr};
     }
 }
 
@@ -295,7 +302,7 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
                                 h->td.gemm_lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, kThreads, h->td.lds_bytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, h->td.threads, h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
     h->wgs_per_cu = occ < 1 ? 1 : occ;
     // a whole number of workgroups per XCD group
@@ -373,7 +380,7 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // GEMM_ONLY has no reducers, so its groups always split evenly
     if (!fused) a.strided = h->strided;
     void* params[] = {&a};
-    HIP_TRY(hipLaunchKernel(fused ? h->td.kernel : h->td.gemm_kernel, dim3(h->grid), dim3(kThreads), params,
+    HIP_TRY(hipLaunchKernel(fused ? h->td.kernel : h->td.gemm_kernel, dim3(h->grid), dim3(h->td.threads), params,
                             fused ? h->td.lds_bytes : h->td.gemm_lds_bytes, s));
     return GEMM_RS_OK;
 }
@@ -381,11 +388,11 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
 static int launch_reduce(gemm_rs_handle* h, Args& a, hipStream_t s)
 {
     const int64_t chunks = (int64_t)h->g.S * h->g.N / 8;
-    int64_t want = (chunks + kThreads - 1) / kThreads;
+    int64_t want = (chunks + kReduceThreads - 1) / kReduceThreads;
     int grid = (int)(want < h->reduce_grid ? want : h->reduce_grid);
     if (grid < 1) grid = 1;
     void* params[] = {&a};
-    HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel), dim3(grid), dim3(kThreads), params,
+    HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel), dim3(grid), dim3(kReduceThreads), params,
                             0, s));
     return GEMM_RS_OK;
 }

@@ -42,7 +42,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;  // 4 wave64 per workgroup
+constexpr int kReduceThreads = 256;  // standalone reduce kernel
 constexpr int kPeers = 7;      // tp - 1 with tp = 8
 constexpr int kGroups = 8;     // XCDs of an MI355X
 constexpr int kStatusTimeout = -6;  // GEMM_RS_ERR_TIMEOUT
@@ -84,14 +84,16 @@ struct Args {
 };
 
 // BM x BN output tile, BK deep stages, NS stages in LDS, WAVES_M x WAVES_N
-// waves, MF x MF MFMA output blocks (32: v_mfma_f32_32x32x16_bf16, 16:
-// v_mfma_f32_16x16x32_bf16).
+// waves (4: one wave per SIMD, 8: two), MF x MF MFMA output blocks (32:
+// v_mfma_f32_32x32x16_bf16, 16: v_mfma_f32_16x16x32_bf16).
 template <int BM_, int BN_, int BK_, int NS_, int WAVES_M_, int WAVES_N_, int MF_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
     static_assert(NS >= 2 && NS <= 4, "stage depth");
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
     static constexpr int MF = MF_;
     static constexpr int KF = MF_ == 32 ? 16 : 32;  // k per MFMA
     static constexpr int KSUB = BK / KF;
@@ -101,8 +103,8 @@ struct TileCfg {
     static constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
     static constexpr int ROW_BYTES = BK * 2;
     static constexpr int A_CHUNKS = BM * CPR, B_CHUNKS = BN * CPR;
-    static_assert(A_CHUNKS % kThreads == 0 && B_CHUNKS % kThreads == 0, "whole load rounds");
-    static constexpr int A_LD = A_CHUNKS / kThreads, B_LD = B_CHUNKS / kThreads;
+    static_assert(A_CHUNKS % THREADS == 0 && B_CHUNKS % THREADS == 0, "whole load rounds");
+    static constexpr int A_LD = A_CHUNKS / THREADS, B_LD = B_CHUNKS / THREADS;
     static constexpr int LPS = A_LD + B_LD;          // loads per thread per stage
     static_assert(LPS * (NS - 1) <= 63, "vmcnt range");
     static constexpr int A_BYTES = BM * ROW_BYTES;
@@ -177,7 +179,7 @@ __device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int ro
     const uint32_t K = (uint32_t)a.g.K;
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i) {
-        const int p = i * kThreads + tid;
+        const int p = i * C::THREADS + tid;
         const int r = p / C::CPR;
         const int c = (p % C::CPR) ^ swz<C::CPR>(r);
         lp.a_k[i] = (uint16_t)(c * 8);
@@ -185,7 +187,7 @@ __device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int ro
     }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
-        const int p = i * kThreads + tid;
+        const int p = i * C::THREADS + tid;
         const int r = p / C::CPR;
         const int c = (p % C::CPR) ^ swz<C::CPR>(r);
         lp.b_k[i] = (uint16_t)(c * 8);
@@ -210,13 +212,13 @@ __device__ __forceinline__ void issue_stage(const LoadPlan<C>& lp, __amdgpu_buff
     for (int i = 0; i < C::A_LD; ++i) {
         const uint32_t off = (int)lp.a_k[i] < lim ? lp.a_off[i] + (uint32_t)k0 * 2u : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (lds_void_t*)(stage + (i * kThreads + wave * 64) * 16), 16, off, 0, 0, 0);
+            rx, (lds_void_t*)(stage + (i * C::THREADS + wave * 64) * 16), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
         const uint32_t off = (int)lp.b_k[i] < lim ? lp.b_off[i] + (uint32_t)k0 * 2u : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rw, (lds_void_t*)(stage + C::A_BYTES + (i * kThreads + wave * 64) * 16), 16, off, 0, 0, 0);
+            rw, (lds_void_t*)(stage + C::A_BYTES + (i * C::THREADS + wave * 64) * 16), 16, off, 0, 0, 0);
     }
 }
 
@@ -390,8 +392,7 @@ __device__ __forceinline__ u32x4 pack8(const f32x8& acc)
 constexpr int kAuxNt = 2;
 constexpr int kAuxSc1 = 16;
 constexpr int kEngineSlotBytes = 1024;               // one 16-byte chunk per lane
-constexpr int kEngineSlots = 4;                      // per wave
-constexpr int kEngineBytes = 4 * kEngineSlots * kEngineSlotBytes;  // per workgroup
+constexpr int kEngineSlots = 2;                      // per wave
 
 template <int AUX>
 __device__ __forceinline__ void lds_load16(const uint16_t* g, char* slot)
@@ -453,21 +454,24 @@ __device__ __forceinline__ void sum_block(const Args& a, int row0, int rows, int
 // an item spans 64 / (BN/8) consecutive rows of the tile, so a lane's offset
 // inside an item is a constant and the item's base offset is wave-uniform.
 // Compute wave gw (of W) owns items gw, gw + W, gw + 2W, ... -- tile order.
-// Between MFMAs, every NS-1 K steps, a wave issues one operation and consumes
-// the one it issued NS-1 steps earlier, which the stage wait has by then
-// completed (vector-memory operations complete in issue order):
-//   HEAD     peer loads 0..3 of the next item; consume: start its FP32 sum
-//   TAIL     peer loads 4..6, plus the local load if the item's tile is
-//            flagged; consume: finish and store out, or park the FP32 partial
-//   FINISH   the local load of the oldest parked item; consume: add, store out
-//   POLL     64 ready flags (tiles anchor .. anchor+63, one per lane)
-// Peer partials need no flag, so a wave pre-sums while its tiles are still
-// being computed; the local partial is added last, as the sum order requires.
-// After its last tile a wave drains its remaining items, polling flags under
-// the watchdog.
+// An item is summed in four steps of two loads each, in the sum order:
+//   step 0: peers 0, 1    acc = (0 + p0) + p1
+//   step 1: peers 2, 3    acc = (acc + p2) + p3
+//   step 2: peers 4, 5    acc = (acc + p4) + p5
+//   step 3: peer 6 and, if the item's tile is flagged, the local partial:
+//           acc = (acc + p6) + local, stored to out; otherwise acc + p6 is
+//           parked in registers and a later FINISH adds the local partial.
+// POLL reads 64 ready flags (tiles anchor .. anchor+63, one per lane).  Peer
+// loads need no flag, so a wave pre-sums while its tiles are still being
+// computed.  Between MFMAs, every NS-1 K steps, a wave consumes its previous
+// operation and issues the next; the loads go straight into two per-wave LDS
+// slots and have completed by consumption time, because vector-memory
+// operations complete in issue order and the stage wait NS-1 steps later
+// covers a younger load.  After its last tile a wave drains its remaining
+// items, polling flags under the watchdog.
 
-enum EngineOp { kOpNone = 0, kOpHead = 1, kOpTail = 2, kOpTailLocal = 3, kOpFinish = 4, kOpPoll = 5 };
-constexpr int kPark = 4;  // parked FP32 partials per wave
+enum EngineOp { kOpNone = 0, kOpStep = 1, kOpFinish = 2, kOpPoll = 3 };
+constexpr int kPark = 2;  // parked FP32 partials per wave
 
 struct Engine {
     char* slots;    // this wave's kEngineSlots LDS slots
@@ -476,18 +480,18 @@ struct Engine {
     int nitems;     // items of the slice
     int ipt;        // items per tile
     int rpi;        // tile rows per item
-    int lane_row, lane_off;  // this lane's row inside an item and element offset
-    int lane_col;   // this lane's first column inside a tile row
+    int lane_row, lane_col, lane_off;  // this lane's place inside an item
     int op;         // operation in flight
-    int op_item;
+    int op_item, op_step, op_local;
     int loads;      // vector loads the last engine step issued
     int anchor;     // tile of bit 0 of `ready`
     uint64_t ready; // ready tiles anchor .. anchor+63
+    int cur_item;   // item being summed, -1 if none
+    int cur_step;   // its next step
+    f32x8 cur;
     int park_n;
     int park_item[kPark];
     f32x8 park[kPark];
-    f32x8 cur;      // FP32 sum of the item between HEAD and TAIL
-    int cur_item;   // item whose HEAD has been issued, -1 if none
     uint32_t epoch;
 };
 
@@ -508,9 +512,9 @@ __device__ __forceinline__ int64_t item_base(const Engine& e, const Args& a, int
 __device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* slots, int gw, int waves,
                                             uint32_t epoch)
 {
-    e.slots = slots;
     const int lane = threadIdx.x & 63;
     const int cpr = a.g.bn >> 3;  // 16-byte chunks per tile row (8 .. 32)
+    e.slots = slots;
     e.rpi = 64 / cpr;
     e.ipt = a.g.bm / e.rpi;
     e.nitems = a.g.ts * e.ipt;
@@ -521,11 +525,14 @@ __device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* slot
     e.stride = waves;
     e.op = kOpNone;
     e.op_item = 0;
+    e.op_step = 0;
+    e.op_local = 0;
     e.loads = 0;
     e.anchor = 0;
     e.ready = 0;
-    e.park_n = 0;
     e.cur_item = -1;
+    e.cur_step = 0;
+    e.park_n = 0;
     e.epoch = epoch;
 }
 
@@ -566,24 +573,27 @@ __device__ __forceinline__ void park_pop(Engine& e)
     --e.park_n;
 }
 
+__device__ __forceinline__ u32x4 engine_slot(const Engine& e, int k)
+{
+    return *reinterpret_cast<const u32x4*>(e.slots + k * kEngineSlotBytes + (threadIdx.x & 63) * 16);
+}
+
 // Consume the operation in flight (its loads have completed).
 __device__ __forceinline__ void engine_consume(Engine& e, const Args& a)
 {
-    const int lane = threadIdx.x & 63;
-    auto slot = [&](int k) { return *reinterpret_cast<const u32x4*>(e.slots + k * kEngineSlotBytes + lane * 16); };
     const int op = e.op;
-    if (op == kOpHead) {
-        f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = add8(acc, slot(s));
-        e.cur = acc;
-    } else if (op == kOpTail || op == kOpTailLocal) {
+    if (op == kOpStep) {
+        const int s = e.op_step;
         f32x8 acc = e.cur;
-#pragma unroll
-        for (int s = 0; s < 3; ++s) acc = add8(acc, slot(s));
-        if (op == kOpTailLocal) {
-            acc = add8(acc, slot(3));
+        if (s == 0) acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        acc = add8(acc, engine_slot(e, 0));
+        if (s < 3 || e.op_local) acc = add8(acc, engine_slot(e, 1));
+        if (s < 3) {
+            e.cur = acc;
+            e.cur_step = s + 1;
+        } else if (e.op_local) {
             store_out(e, a, e.op_item, acc);
+            e.cur_item = -1;
         } else {
             // a value select per slot (no indexed store) keeps the parked
             // partials in registers
@@ -594,11 +604,13 @@ __device__ __forceinline__ void engine_consume(Engine& e, const Args& a)
                 e.park_item[p] = here ? e.op_item : e.park_item[p];
             }
             ++e.park_n;
+            e.cur_item = -1;
         }
     } else if (op == kOpFinish) {
-        store_out(e, a, e.park_item[0], add8(e.park[0], slot(3)));
+        store_out(e, a, e.park_item[0], add8(e.park[0], engine_slot(e, 1)));
         park_pop(e);
     } else if (op == kOpPoll) {
+        const int lane = threadIdx.x & 63;
         const uint32_t f = *reinterpret_cast<const uint32_t*>(e.slots + lane * 4);
         const bool mine = e.anchor + lane < a.g.ts;
         e.ready |= __builtin_amdgcn_ballot_w64(mine && f == e.epoch);
@@ -608,47 +620,55 @@ __device__ __forceinline__ void engine_consume(Engine& e, const Args& a)
 }
 
 // Choose and issue the next operation.  Every lane issues every load (lanes
-// without a valid chunk read the item's first chunk), so the number of
+// without a valid chunk read the slice's first chunk), so the number of
 // vector-memory instructions equals e.loads exactly.
 __device__ __forceinline__ void engine_issue(Engine& e, const Args& a)
 {
-    int op = kOpNone;
-    int item = 0;
-    if (e.cur_item >= 0) {
-        // the item whose HEAD was consumed goes on with its TAIL
-        item = e.cur_item;
-        op = tile_ready(e, item / e.ipt) ? kOpTailLocal : (e.park_n < kPark ? kOpTail : kOpPoll);
-    } else if (e.park_n > 0 && tile_ready(e, e.park_item[0] / e.ipt)) {
+    int op = kOpNone, item = 0, step = 0, local = 0;
+    if (e.park_n > 0 && tile_ready(e, e.park_item[0] / e.ipt)) {
         op = kOpFinish;
         item = e.park_item[0];
+    } else if (e.cur_item >= 0) {
+        item = e.cur_item;
+        step = e.cur_step;
+        if (step < 3) {
+            op = kOpStep;
+        } else if (tile_ready(e, item / e.ipt)) {
+            op = kOpStep;
+            local = 1;
+        } else {
+            op = e.park_n < kPark ? kOpStep : kOpPoll;
+        }
     } else if (e.next < e.nitems && (e.park_n < kPark || tile_ready(e, e.next / e.ipt))) {
-        op = kOpHead;
+        op = kOpStep;
         item = e.next;
+        e.cur_item = e.next;
+        e.cur_step = 0;
+        e.next += e.stride;
     } else if (e.park_n > 0 || e.next < e.nitems) {
         op = kOpPoll;
     }
     e.op = op;
     e.op_item = item;
+    e.op_step = step;
+    e.op_local = local;
     e.loads = 0;
-    if (op == kOpHead || op == kOpTail || op == kOpTailLocal || op == kOpFinish) {
+    if (op == kOpStep || op == kOpFinish) {
         bool valid;
         const int64_t base = item_base(e, a, item, valid);
         // lanes outside the (ragged) tile read the slice's first chunk
         const int64_t off = valid ? base + e.lane_off : 0;
-        if (op == kOpHead) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) lds_load16<kAuxNt>(a.peers[s] + off, e.slots + s * kEngineSlotBytes);
-            e.loads = 4;
-            e.cur_item = item;
-            e.next += e.stride;
-        } else if (op != kOpFinish) {
-#pragma unroll
-            for (int s = 0; s < 3; ++s) lds_load16<kAuxNt>(a.peers[4 + s] + off, e.slots + s * kEngineSlotBytes);
-            e.loads = 3;
-            e.cur_item = -1;
+        if (op == kOpStep) {
+            const int p = 2 * step;
+            lds_load16<kAuxNt>(a.peers[p] + off, e.slots);
+            e.loads = 1;
+            if (step < 3) {
+                lds_load16<kAuxNt>(a.peers[p + 1] + off, e.slots + kEngineSlotBytes);
+                e.loads = 2;
+            }
         }
-        if (op == kOpTailLocal || op == kOpFinish) {
-            lds_load16<kAuxSc1>(a.dst[a.g.rank] + off, e.slots + 3 * kEngineSlotBytes);
+        if (local || op == kOpFinish) {
+            lds_load16<kAuxSc1>(a.dst[a.g.rank] + off, e.slots + kEngineSlotBytes);
             e.loads += 1;
         }
     } else if (op == kOpPoll) {
@@ -697,13 +717,13 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
         if (gave_up || (int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
             gave_up = true;
             // give up on the oldest pending item's tile
-            const int stuck = (e.cur_item >= 0 ? e.cur_item : (e.park_n > 0 ? e.park_item[0] : e.next)) / e.ipt;
+            const int stuck = (e.park_n > 0 ? e.park_item[0] : (e.cur_item >= 0 ? e.cur_item : e.next)) / e.ipt;
             if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
                 atomicExch(&a.state->status[1], decode_slot(a.g, stuck).flag);
-            if (e.cur_item >= 0 && e.cur_item / e.ipt == stuck) e.cur_item = -1;
 #pragma unroll
             for (int p = 0; p < kPark; ++p)
                 if (e.park_n > 0 && e.park_item[0] / e.ipt == stuck) park_pop(e);
+            if (e.cur_item >= 0 && e.cur_item / e.ipt == stuck) e.cur_item = -1;
             while (e.cur_item < 0 && e.park_n == 0 && e.next < e.nitems && e.next / e.ipt == stuck)
                 e.next += e.stride;
             engine_reanchor(e);
@@ -711,7 +731,6 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
         }
     }
 }
-
 
 // Per-tile hooks run by the K loop right after a stage barrier.
 struct StepHooks {
@@ -726,11 +745,10 @@ template <class C>
 __device__ __forceinline__ void wait_stage(int extra)
 {
     constexpr int B = (C::NS - 2) * C::LPS;
-    static_assert(B + 4 <= 63, "vmcnt range");
+    static_assert(B + 2 <= 63, "vmcnt range");
     switch (extra) {
     case 1: wait_vmcnt<B + 1>(); break;
-    case 3: wait_vmcnt<B + 3>(); break;
-    case 4: wait_vmcnt<B + 4>(); break;
+    case 2: wait_vmcnt<B + 2>(); break;
     default: wait_vmcnt<B>(); break;
     }
 }
@@ -846,8 +864,8 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
     const bool interleave = FUSED && a.num_reducers == 0;
     Engine eng;
     const int wave = uni((int)(threadIdx.x >> 6));
-    engine_init(eng, a, lds + C::LDS_BYTES + wave * kEngineSlots * kEngineSlotBytes, pos * 4 + wave, Ctot * 4,
-                epoch);
+    engine_init(eng, a, lds + C::LDS_BYTES + wave * kEngineSlots * kEngineSlotBytes, pos * C::WAVES + wave,
+                Ctot * C::WAVES, epoch);
     StepHooks hk;
     hk.interleave = interleave;
     hk.pend_q = -1;
@@ -930,7 +948,7 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
         const int rows = tile_rows(a.g, t), cols = tile_cols(a.g, t);
         const int cpr = cols >> 3;
         const uint16_t* local = a.dst[a.g.rank];
-        for (int c = threadIdx.x; c < rows * cpr; c += kThreads) {
+        for (int c = threadIdx.x; c < rows * cpr; c += (int)blockDim.x) {
             const int r = c / cpr;
             const int64_t off = (int64_t)(t.tml * a.g.bm + r) * a.g.N + t.tn * a.g.bn + (c - r * cpr) * 8;
             u32x4 v[kPeers + 1];
@@ -985,7 +1003,15 @@ __device__ __forceinline__ void fused_body(const Args& a)
 
 // Tiles that fit two workgroups per CU keep two waves per SIMD resident.
 template <class C, bool FUSED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(Args a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(Args a)
+{
+    fused_body<C, FUSED>(a);
+}
+
+// Eight-wave workgroups (one per CU): two waves per SIMD, so one wave's
+// MFMAs run while its sibling waits on LDS, a barrier or the reduce engine.
+template <class C, bool FUSED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel_8w(Args a)
 {
     fused_body<C, FUSED>(a);
 }
@@ -993,16 +1019,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Large tiles run one workgroup (one wave per SIMD) per CU: let the compiler
 // use the whole register file for latency hiding.
 template <class C, bool FUSED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_kernel_1w(Args a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_kernel_1w(Args a)
 {
     fused_body<C, FUSED>(a);
 }
 
 // Standalone slice sum: every workgroup reduces, no flags, grid-stride over the
 // whole [S][N] slice.
-__global__ __launch_bounds__(kThreads) void reduce_kernel(Args a)
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Args a)
 {
-    sum_block(a, 0, a.g.S, 0, a.g.N, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+    sum_block(a, 0, a.g.S, 0, a.g.N, blockIdx.x * kReduceThreads + threadIdx.x, gridDim.x * kReduceThreads);
 }
 
 }  // namespace gemm_rs
