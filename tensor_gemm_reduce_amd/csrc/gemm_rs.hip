@@ -31,57 +31,68 @@ int hip_fail(hipError_t e, const char* what)
         if (e_ != hipSuccess) return hip_fail(e_, #call); \
     } while (0)
 
-// Tile table: id -> tile shape, stage depth and the kernel instantiation.
-//                 BM   BN   BK  NS  waves  MFMA
-typedef TileCfg<16, 64, 128, 2, 1, 4, 16> Tile16x64;
-typedef TileCfg<64, 128, 64, 2, 2, 2, 32> Tile64x128;
-typedef TileCfg<128, 128, 32, 3, 2, 2, 32> Tile128x128;
-typedef TileCfg<128, 256, 32, 4, 2, 2, 32> Tile128x256;
-typedef TileCfg<256, 128, 32, 4, 2, 2, 32> Tile256x128;
-typedef TileCfg<256, 256, 32, 4, 2, 4, 32> Tile256x256;
+// Tile table: id -> tile shape, stage depth and the kernel instantiations.
+// Each shape has two load splits: every wave loads stages (GEMM only, and the
+// fused kernel with dedicated reducer workgroups), or the first half of the
+// waves load and the second half run the reduce engine (the fused kernel
+// without dedicated reducers).
+//                      BM   BN   BK  NS  waves  MFMA  loader waves
+#define GEMM_RS_TILE(name, ...)                          \
+    typedef TileCfg<__VA_ARGS__> name;                   \
+    typedef TileCfg<__VA_ARGS__, (name::WAVES / 2)> name##E;
+GEMM_RS_TILE(Tile16x64, 16, 64, 128, 2, 1, 4, 16)
+GEMM_RS_TILE(Tile64x128, 64, 128, 64, 2, 2, 2, 32)
+GEMM_RS_TILE(Tile128x128, 128, 128, 32, 3, 2, 2, 32)
+GEMM_RS_TILE(Tile128x256, 128, 256, 32, 4, 2, 2, 32)
+GEMM_RS_TILE(Tile256x128, 256, 128, 32, 4, 2, 2, 32)
+GEMM_RS_TILE(Tile256x256, 256, 256, 32, 4, 2, 4, 32)
+#undef GEMM_RS_TILE
 
 struct TileDesc {
     int bm, bn, bk;
-    int threads;             // workgroup size
-    int lds_bytes;           // fused kernel: stages + reduce-engine slots
-    int gemm_lds_bytes;      // GEMM-only kernel: stages
-    const void* kernel;      // fused: compute + reducers, flags
-    const void* gemm_kernel; // the same GEMM without flags or reduction
+    int threads;               // workgroup size
+    int engine_lds_bytes;      // fused kernel with the reduce engine: stages + engine areas
+    int lds_bytes;             // the other kernels: stages
+    const void* engine_kernel; // fused: compute waves run the reduce engine
+    const void* kernel;        // fused: dedicated reducer workgroups
+    const void* gemm_kernel;   // the same GEMM without flags or reduction
 };
 
-template <class C>
+// Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
+// tiles that cannot fit two workgroups per CU get the occupancy-1 kernel (one
+// wave per SIMD, the whole register file).
+template <class C, bool FUSED, bool TWO_PER_CU>
+const void* kernel_for()
+{
+    if constexpr (C::WAVES == 8)
+        return reinterpret_cast<const void*>(&fused_kernel_8w<C, FUSED>);
+    else if constexpr (TWO_PER_CU)
+        return reinterpret_cast<const void*>(&fused_kernel<C, FUSED>);
+    else
+        return reinterpret_cast<const void*>(&fused_kernel_1w<C, FUSED>);
+}
+
+template <class C, class CE>
 TileDesc desc()
 {
-    constexpr int engine = C::WAVES * kEngineSlots * kEngineSlotBytes;
-    static_assert(C::LDS_BYTES + engine <= 160 * 1024 - 64, "LDS of one workgroup");
-    // eight-wave tiles run one workgroup per CU with two waves per SIMD; four-
-    // wave tiles that cannot fit two workgroups per CU get the occupancy-1
-    // kernel (one wave per SIMD, the whole register file)
-    const void* k;
-    const void* g;
-    if constexpr (C::WAVES == 8) {
-        k = reinterpret_cast<const void*>(&fused_kernel_8w<C, true>);
-        g = reinterpret_cast<const void*>(&fused_kernel_8w<C, false>);
-    } else if constexpr (C::LDS_BYTES + engine > 80 * 1024 - 64) {
-        k = reinterpret_cast<const void*>(&fused_kernel_1w<C, true>);
-        g = reinterpret_cast<const void*>(&fused_kernel_1w<C, false>);
-    } else {
-        k = reinterpret_cast<const void*>(&fused_kernel<C, true>);
-        g = reinterpret_cast<const void*>(&fused_kernel<C, false>);
-    }
-    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::LDS_BYTES + engine, C::LDS_BYTES, k, g};
+    static_assert(C::LDS_BYTES == CE::LDS_BYTES && CE::EW > 0, "load splits of one shape");
+    constexpr int elds = CE::LDS_BYTES + CE::ENG_LDS;
+    static_assert(elds <= 160 * 1024 - 64, "LDS of one workgroup");
+    constexpr bool two = elds <= 80 * 1024 - 64;
+    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, elds, C::LDS_BYTES, kernel_for<CE, true, two>(),
+                    kernel_for<C, true, two>(), kernel_for<C, false, two>()};
 }
 
 TileDesc tile_desc(int id)
 {
     switch (id) {
-    case GEMM_RS_TILE_16x64: return desc<Tile16x64>();
-    case GEMM_RS_TILE_64x128: return desc<Tile64x128>();
-    case GEMM_RS_TILE_128x128: return desc<Tile128x128>();
-    case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
-    case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
-    case GEMM_RS_TILE_256x256: return desc<Tile256x256>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr};
+    case GEMM_RS_TILE_16x64: return desc<Tile16x64, Tile16x64E>();
+    case GEMM_RS_TILE_64x128: return desc<Tile64x128, Tile64x128E>();
+    case GEMM_RS_TILE_128x128: return desc<Tile128x128, Tile128x128E>();
+    case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
+    case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
+    case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
+    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr};
     }
 }
 
@@ -201,8 +212,9 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if ((int64_t)c->M * c->K_local > ((int64_t)1 << 40) || (int64_t)c->N * c->K_local > ((int64_t)1 << 40) ||
         S * (int64_t)c->N > ((int64_t)1 << 40))
         return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
-    // the reduce engine addresses the slice with 32-bit element offsets
-    if ((int64_t)(c->M / c->tp) * c->N >= ((int64_t)1 << 31)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    // slice buffers are written through buffer resources with 31-bit byte
+    // offsets (and the reduce engine uses 32-bit element offsets)
+    if ((int64_t)(c->M / c->tp) * c->N * 2 >= ((int64_t)1 << 31)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     // X_r and W_r are read through buffer resources with 31-bit byte offsets
     if ((int64_t)c->M * c->K_local * 2 >= ((int64_t)1 << 31) ||
         (int64_t)c->N * c->K_local * 2 >= ((int64_t)1 << 31))
@@ -296,20 +308,27 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     h->num_cus = prop.multiProcessorCount;
     h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
 
-    hipError_t e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+    // automatic: no dedicated reducers, the engine waves of the compute
+    // workgroups run the reduction
+    const int red_req = c->num_reducers < 0 ? 0 : c->num_reducers;
+    hipError_t e = hipFuncSetAttribute(h->td.engine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       h->td.engine_lds_bytes);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                h->td.gemm_lds_bytes);
+        e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, h->td.threads, h->td.lds_bytes);
+    e = red_req == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.engine_kernel, h->td.threads,
+                                                                    h->td.engine_lds_bytes)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, h->td.threads,
+                                                                    h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
     h->wgs_per_cu = occ < 1 ? 1 : occ;
     // a whole number of workgroups per XCD group
     h->grid = (h->num_cus * h->wgs_per_cu) / kGroups * kGroups;
     if (h->grid < kGroups) h->grid = kGroups;
-    // automatic: no dedicated reducers, the compute waves run the reduce engine
-    int red = c->num_reducers < 0 ? 0 : c->num_reducers;
+    int red = red_req;
     if (red >= h->grid) red = h->grid - 1;
     h->reducer_wgs = red;
     h->compute_wgs = h->grid - red;
@@ -363,11 +382,11 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.g = h->g;
     a.x_bytes = (uint32_t)((int64_t)h->g.M * h->g.K * 2);
     a.w_bytes = (uint32_t)((int64_t)h->g.N * h->g.K * 2);
+    a.slice_bytes = (uint32_t)((int64_t)h->g.S * h->g.N * 2);
     a.strided = h->strided;
     const int64_t us = h->cfg.watchdog_us > 0 ? h->cfg.watchdog_us : 2000000;
     a.watchdog_ticks = us * 100;  // 100 MHz real-time counter
     a.flag_stride = h->flag_stride;
-    a.protocol = h->cfg.flag_protocol;
     a.drop_flag = h->cfg.drop_flag;
     a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
 }
@@ -380,8 +399,9 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // GEMM_ONLY has no reducers, so its groups always split evenly
     if (!fused) a.strided = h->strided;
     void* params[] = {&a};
-    HIP_TRY(hipLaunchKernel(fused ? h->td.kernel : h->td.gemm_kernel, dim3(h->grid), dim3(h->td.threads), params,
-                            fused ? h->td.lds_bytes : h->td.gemm_lds_bytes, s));
+    const bool engine = fused && h->reducer_wgs == 0;
+    HIP_TRY(hipLaunchKernel(engine ? h->td.engine_kernel : (fused ? h->td.kernel : h->td.gemm_kernel), dim3(h->grid),
+                            dim3(h->td.threads), params, engine ? h->td.engine_lds_bytes : h->td.lds_bytes, s));
     return GEMM_RS_OK;
 }
 
@@ -478,7 +498,7 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->reducer_wgs = h->reducer_wgs;
     info->num_cus = h->num_cus;
     info->wgs_per_cu = h->wgs_per_cu;
-    info->lds_bytes = h->td.lds_bytes;
+    info->lds_bytes = h->reducer_wgs == 0 ? h->td.engine_lds_bytes : h->td.lds_bytes;
     info->reduce_grid = h->reduce_grid;
     info->xcd_split = h->strided;
     DeviceState ds;

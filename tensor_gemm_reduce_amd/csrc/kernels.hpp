@@ -9,10 +9,17 @@
 //             from HBM straight into LDS (buffer loads with the LDS-direct bit),
 //             NS stages deep, so several BK steps of loads are in flight while
 //             the MFMAs consume the oldest stage.  The epilogue rounds the tile
-//             to BF16, stores it into its destination slice buffer and releases
-//             the tile's ready flag at agent scope;
-//   reducer   claims own-slice tiles in schedule order, waits (acquire) for
-//             their flags and sums each with the tp-1 peer partials.
+//             to BF16, stores it into its destination slice buffer at device
+//             scope and publishes the tile's ready flag;
+//   reducer   sums this rank's slice with the tp-1 peer partials, tile by tile
+//             as the ready flags arrive.
+// The reduction runs either in dedicated reducer workgroups or, by default,
+// inside the compute workgroups: there the first half of the waves ("loader"
+// waves) issue every stage load of the GEMM and the second half ("engine"
+// waves) run the reduce engine between their MFMAs.  Vector-memory operations
+// of one wave retire in issue order, so an HBM load issued by a wave that also
+// waits for stage loads would hold every later stage of that wave behind one
+// HBM round trip; engine waves wait for stage loads only through the barrier.
 //
 // Workgroup g belongs to group g % 8, which is the XCD it runs on (workgroups
 // are dispatched to the 8 XCDs round-robin).  Each group hands out its own
@@ -38,18 +45,41 @@ namespace gemm_rs {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kReduceThreads = 256;  // standalone reduce kernel
 constexpr int kPeers = 7;      // tp - 1 with tp = 8
 constexpr int kGroups = 8;     // XCDs of an MI355X
 constexpr int kStatusTimeout = -6;  // GEMM_RS_ERR_TIMEOUT
-// A buffer-load offset at or past the resource's byte count reads as zero.
+// A buffer offset at or past the resource's byte count reads as zero and
+// drops a store.
 constexpr uint32_t kOob = 0x80000000u;
 // Third descriptor word of a raw buffer resource on gfx9-family GPUs.
 constexpr int kRsrcFlags = 0x00020000;
+// Cache-policy bits of a buffer store: sc1 makes it device scope (written
+// through this XCD's L2 to the memory side, where a device-scope load on any
+// XCD sees it once the store has completed -- no L2 write-back is needed to
+// publish a tile).
+constexpr int kStoreDevice = 16;
+// Cache-policy bits of the engine's loads and stores: peer partials are read
+// once and sums written once (non-temporal); the local slice and the flags are
+// read at device scope (sc1), so a copy left in this XCD's L2 by an earlier
+// run is never used.
+constexpr int kAuxNt = 2;
+constexpr int kAuxSc1 = 16;
+
+// Reduce engine: 16-byte loads per operation (one per lane each), LDS bytes an
+// operation lands in, operations in flight per engine wave, and parked FP32
+// partial sums per engine wave.
+constexpr int kEngLoads = 2;
+constexpr int kEngAreaBytes = kEngLoads * 1024;
+constexpr int kEngAreas = 2;
+constexpr int kPark = 2;
 
 // Handle-owned device state, zeroed at creation.
 struct DeviceState {
@@ -72,21 +102,23 @@ struct Args {
     uint32_t* trace;         // 4 words per slot (debug)
     Geometry g;
     uint32_t x_bytes, w_bytes;
+    uint32_t slice_bytes;    // S * N * 2
     int64_t watchdog_ticks;  // 100 MHz ticks
     int32_t num_compute;     // C: compute workgroups in the grid
     int32_t num_reducers;    // R
     int32_t strided;         // XCD split of a round: 0 contiguous, 1 strided
     int32_t flag_stride;
     int32_t fused;           // 1: release flags, reducers run, epoch advances
-    int32_t protocol;        // 0: per-wave release fence, 1: one release store
     int32_t drop_flag;
     int32_t trace_on;
 };
 
 // BM x BN output tile, BK deep stages, NS stages in LDS, WAVES_M x WAVES_N
 // waves (4: one wave per SIMD, 8: two), MF x MF MFMA output blocks (32:
-// v_mfma_f32_32x32x16_bf16, 16: v_mfma_f32_16x16x32_bf16).
-template <int BM_, int BN_, int BK_, int NS_, int WAVES_M_, int WAVES_N_, int MF_>
+// v_mfma_f32_32x32x16_bf16, 16: v_mfma_f32_16x16x32_bf16).  The first LW waves
+// issue the stage loads (LW = 0: all of them); the other EW waves run the
+// reduce engine.
+template <int BM_, int BN_, int BK_, int NS_, int WAVES_M_, int WAVES_N_, int MF_, int LW_ = 0>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
     static_assert(NS >= 2 && NS <= 4, "stage depth");
@@ -94,6 +126,9 @@ struct TileCfg {
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * WAVES;
     static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
+    static constexpr int LW = LW_ > 0 ? LW_ : WAVES;
+    static constexpr int EW = WAVES - LW;
+    static constexpr int LTHREADS = 64 * LW;
     static constexpr int MF = MF_;
     static constexpr int KF = MF_ == 32 ? 16 : 32;  // k per MFMA
     static constexpr int KSUB = BK / KF;
@@ -103,14 +138,31 @@ struct TileCfg {
     static constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
     static constexpr int ROW_BYTES = BK * 2;
     static constexpr int A_CHUNKS = BM * CPR, B_CHUNKS = BN * CPR;
-    static_assert(A_CHUNKS % THREADS == 0 && B_CHUNKS % THREADS == 0, "whole load rounds");
-    static constexpr int A_LD = A_CHUNKS / THREADS, B_LD = B_CHUNKS / THREADS;
-    static constexpr int LPS = A_LD + B_LD;          // loads per thread per stage
+    static_assert(A_CHUNKS % LTHREADS == 0 && B_CHUNKS % LTHREADS == 0, "whole load rounds");
+    static constexpr int A_LD = A_CHUNKS / LTHREADS, B_LD = B_CHUNKS / LTHREADS;
+    static constexpr int LPS = A_LD + B_LD;          // loads per loader thread per stage
     static_assert(LPS * (NS - 1) <= 63, "vmcnt range");
     static constexpr int A_BYTES = BM * ROW_BYTES;
     static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
     static constexpr int LDS_BYTES = NS * STAGE_BYTES;
     static_assert(CPR == 4 || CPR == 8 || CPR == 16, "swizzle defined for BK = 32, 64, 128");
+    // Epilogue.  With 32x32 MFMA blocks and wave tiles a whole number of 64
+    // columns wide, the BF16 tile goes through a per-wave 4 KiB LDS area (32
+    // rows x 64 columns per pass) so that each store instruction writes 8 full
+    // 128-byte row segments; otherwise every lane stores its own 8 bytes.
+    // STORES is the number of store instructions per wave per tile (issued
+    // unconditionally: lanes outside a ragged tile store out of bounds).
+    static constexpr bool STAGED_EPI = MF == 32 && WTN % 64 == 0;
+    static constexpr int EPI_AREA = 4096;
+    static constexpr int STORES = STAGED_EPI ? FM * (WTN / 64) * 4 : FM * FN * (MF == 32 ? 4 : 1);
+    static_assert(!STAGED_EPI || WAVES * EPI_AREA <= STAGE_BYTES, "epilogue staging fits one stage buffer");
+    static_assert((NS - 2) * LPS + STORES <= 63, "vmcnt range");
+    // Reduce engine: one operation every ENG_E K steps, so that an operation's
+    // loads get about 2 * 2600 cycles before they are consumed (STEP_CYCLES
+    // estimates one K step with two waves per SIMD).
+    static constexpr int STEP_CYCLES = KSUB * FM * FN * (MF == 32 ? 32 : 16) * 2;
+    static constexpr int ENG_E = (2600 + STEP_CYCLES - 1) / STEP_CYCLES;
+    static constexpr int ENG_LDS = EW * kEngAreas * kEngAreaBytes;
 };
 
 template <int MF> struct AccT;
@@ -138,6 +190,30 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most n of this wave's vector-memory instructions are
+// outstanding; n above 15 waits for 15 (longer than needed, never shorter).
+__device__ __forceinline__ void wait_vmcnt_upto(uint32_t n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;
+    }
+}
+
 // Execution barrier without the memory fence __syncthreads() implies (which
 // would wait for every LDS-direct load in flight).  The asm memory clobber
 // keeps the compiler from moving LDS reads of a stage above it.
@@ -156,6 +232,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, b);
 }
 
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // ---------------------------------------------------------------- GEMM tile
 
 template <class C>
@@ -163,9 +241,9 @@ struct TileState {
     typename AccT<C::MF>::type acc[C::FM][C::FN];
 };
 
-// Per-thread load plan of one tile: byte offset of each chunk this thread
-// moves at k = 0 (kOob for rows past the tile's valid extent) and the chunk's
-// k offset (for the K tail).
+// Per-thread load plan of one tile (loader threads): byte offset of each chunk
+// this thread moves at k = 0 (kOob for rows past the tile's valid extent) and
+// the chunk's k offset (for the K tail).
 template <class C>
 struct LoadPlan {
     uint32_t a_off[C::A_LD], b_off[C::B_LD];
@@ -179,7 +257,7 @@ __device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int ro
     const uint32_t K = (uint32_t)a.g.K;
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i) {
-        const int p = i * C::THREADS + tid;
+        const int p = i * C::LTHREADS + tid;
         const int r = p / C::CPR;
         const int c = (p % C::CPR) ^ swz<C::CPR>(r);
         lp.a_k[i] = (uint16_t)(c * 8);
@@ -187,7 +265,7 @@ __device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int ro
     }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
-        const int p = i * C::THREADS + tid;
+        const int p = i * C::LTHREADS + tid;
         const int r = p / C::CPR;
         const int c = (p % C::CPR) ^ swz<C::CPR>(r);
         lp.b_k[i] = (uint16_t)(c * 8);
@@ -196,15 +274,15 @@ __device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int ro
 }
 
 // Issue the LDS-direct loads of the BK slice starting at k0 into stage buffer
-// `stage` (LPS loads per thread).  Each wave instruction fills 1 KiB of LDS:
-// lane l writes bytes [16 l, 16 l + 16) after the wave's base.
+// `stage` (LPS loads per loader thread).  Each wave instruction fills 1 KiB of
+// LDS: lane l writes bytes [16 l, 16 l + 16) after the wave's base.
 //
 // Branch-free: a chunk whose k lies at or past K (the K tail, or a whole stage
 // past the end) gets an offset past the resource and reads as zero; rows past
 // the tile carry kOob already, and kOob + 2 k0 stays past the resource.
 template <class C>
 __device__ __forceinline__ void issue_stage(const LoadPlan<C>& lp, __amdgpu_buffer_rsrc_t rx,
-                                   __amdgpu_buffer_rsrc_t rw, char* stage, int k0, int K)
+                                            __amdgpu_buffer_rsrc_t rw, char* stage, int k0, int K)
 {
     const int wave = threadIdx.x >> 6;
     const int lim = K - k0;  // chunks with k offset >= lim are past K
@@ -212,13 +290,13 @@ __device__ __forceinline__ void issue_stage(const LoadPlan<C>& lp, __amdgpu_buff
     for (int i = 0; i < C::A_LD; ++i) {
         const uint32_t off = (int)lp.a_k[i] < lim ? lp.a_off[i] + (uint32_t)k0 * 2u : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (lds_void_t*)(stage + (i * C::THREADS + wave * 64) * 16), 16, off, 0, 0, 0);
+            rx, (lds_void_t*)(stage + (i * C::LTHREADS + wave * 64) * 16), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
         const uint32_t off = (int)lp.b_k[i] < lim ? lp.b_off[i] + (uint32_t)k0 * 2u : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rw, (lds_void_t*)(stage + C::A_BYTES + (i * C::THREADS + wave * 64) * 16), 16, off, 0, 0, 0);
+            rw, (lds_void_t*)(stage + C::A_BYTES + (i * C::LTHREADS + wave * 64) * 16), 16, off, 0, 0, 0);
     }
 }
 
@@ -253,8 +331,7 @@ __device__ __forceinline__ void load_frags(const char* stage, int s, bf16x8 (&xf
 
 // The W fragment is the MFMA's A operand and the X fragment its B operand, so
 // the accumulator holds the transposed tile: lane l owns output row m = l % MF
-// and, per group of four registers, four consecutive output columns -- one
-// 8-byte store per group in the epilogue.
+// and, per group of four registers, four consecutive output columns.
 template <class C>
 __device__ __forceinline__ void mfma_substep(TileState<C>& st, const bf16x8 (&xf)[C::FM], const bf16x8 (&wf)[C::FN])
 {
@@ -269,25 +346,25 @@ __device__ __forceinline__ void mfma_substep(TileState<C>& st, const bf16x8 (&xf
         }
 }
 
-// One K step: refill the buffer of stage kt-1 with stage kt+NS-1, then the
-// MFMAs of stage kt with the fragments of substep s+1 read while substep s
-// computes.  The scheduling groups place the substep-0 reads first and then
-// one LDS read or one direct load after each MFMA, so neither waits on a full
-// LDS round trip in the middle of the MFMA stream.
-template <class C>
+// One K step: a loader wave refills the buffer of stage kt-1 with stage
+// kt+NS-1; then the MFMAs of stage kt with the fragments of substep s+1 read
+// while substep s computes.  The scheduling groups place the substep-0 reads
+// first and then one LDS read or one direct load after each MFMA, so neither
+// waits on a full LDS round trip in the middle of the MFMA stream.
+template <class C, bool LOADER>
 __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
-                             char* refill, int k_refill, int K, const char* cur, TileState<C>& st)
+                                      char* refill, int k_refill, int K, const char* cur, TileState<C>& st)
 {
     bf16x8 xf[2][C::FM], wf[2][C::FN];
     load_frags<C>(cur, 0, xf[0], wf[0]);
-    issue_stage<C>(lp, rx, rw, refill, k_refill, K);
+    if constexpr (LOADER) issue_stage<C>(lp, rx, rw, refill, k_refill, K);
 #pragma unroll
     for (int s = 0; s < C::KSUB; ++s) {
         if (s + 1 < C::KSUB) load_frags<C>(cur, s + 1, xf[(s + 1) & 1], wf[(s + 1) & 1]);
         mfma_substep<C>(st, xf[s & 1], wf[s & 1]);
     }
     constexpr int kMfmas = C::KSUB * C::FM * C::FN;
-    constexpr int kFill = (C::KSUB - 1) * (C::FM + C::FN) + C::LPS;
+    constexpr int kFill = (C::KSUB - 1) * (C::FM + C::FN) + (LOADER ? C::LPS : 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FM + C::FN, 0);
 #pragma unroll
     for (int m = 0; m < kMfmas; ++m) {
@@ -296,39 +373,76 @@ __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsr
     }
 }
 
-// Round the accumulators to BF16 and store the valid part of the tile at
-// dst[m][n0 + n] (dst already points at the tile's first row).  The stores are
-// device-scope (sc1): they write through this XCD's L2 to the memory side,
-// where a device-scope load on any XCD sees them once they have completed --
-// no L2 write-back is needed to publish the tile.
-template <class C, bool DEVICE_SCOPE>
-__device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st, uint16_t* dst, int rows, int n0,
-                                  int cols)
+// Round the accumulators to BF16 and store the valid part of the tile into the
+// destination slice buffer behind `rd` (byte offsets from the slice start) at
+// device scope; the tile's first row is slice row `row0`.  Exactly C::STORES
+// store instructions per wave, whatever the tile's valid extent: the vector-
+// memory wait counts of the next tile rely on that.
+//
+// Staged path: per pass (one 32-row block i, one 64-column chunk c of the wave
+// tile) each lane writes its 4 x 2 packed groups (row l % 32, 8-byte halves of
+// 16-byte chunks) into the wave's LDS area, chunk k of row r at k ^ ((r>>1)&7)
+// so that both the 32-row writes and the 8-row reads spread over all banks;
+// then the wave reads 8 rows x 8 chunks per instruction and stores them.
+template <class C>
+__device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st, char* area,
+                                           __amdgpu_buffer_rsrc_t rd, int row0, int rows, int n0, int cols)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int64_t N = a.g.N;
+    const uint32_t N = (uint32_t)a.g.N;
+    if constexpr (C::STAGED_EPI) {
+        char* buf = area + wave * C::EPI_AREA;
+        const int r = lane & 31, h = lane >> 5;    // writer: row, chunk half
+        const int rr = lane >> 3, ck = lane & 7;   // reader: row in an 8-row group, chunk
+        char* wbase = buf + r * 128 + h * 8;
+        const int wsw = (r >> 1) & 7;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int m = wm * C::WTM + i * C::MF + (lane % C::MF);
-        if (m >= rows) continue;
-        uint16_t* drow = dst + (int64_t)m * N + n0;
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            constexpr int G = C::MF == 32 ? 4 : 1;
+            for (int c = 0; c < C::WTN / 64; ++c) {
 #pragma unroll
-            for (int grp = 0; grp < G; ++grp) {
-                const int n = C::MF == 32 ? wn * C::WTN + j * 32 + grp * 8 + (lane / 32) * 4
-                                          : wn * C::WTN + j * 16 + (lane / 16) * 4;
-                if (n < cols) {
-                    const uint64_t v = (uint64_t)pack_bf16x2(st.acc[i][j][grp * 4 + 0], st.acc[i][j][grp * 4 + 1]) |
-                                       ((uint64_t)pack_bf16x2(st.acc[i][j][grp * 4 + 2], st.acc[i][j][grp * 4 + 3]) << 32);
-                    if constexpr (DEVICE_SCOPE)
-                        __hip_atomic_store(reinterpret_cast<uint64_t*>(drow + n), v, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                    else
-                        *reinterpret_cast<uint64_t*>(drow + n) = v;
+                for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+                    for (int grp = 0; grp < 4; ++grp) {
+                        const auto& acc = st.acc[i][c * 2 + j2];
+                        const u32x2 v = {pack_bf16x2(acc[grp * 4 + 0], acc[grp * 4 + 1]),
+                                         pack_bf16x2(acc[grp * 4 + 2], acc[grp * 4 + 3])};
+                        *reinterpret_cast<u32x2*>(wbase + (((j2 * 4 + grp) ^ wsw) << 4)) = v;
+                    }
+                // LDS operations of one wave complete in order: the reads below
+                // see the writes above, and the next pass's writes come after
+                // these reads
+                __asm__ __volatile__("" ::: "memory");
+                const int n = wn * C::WTN + c * 64 + ck * 8;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int row = s4 * 8 + rr;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(buf + row * 128 + ((ck ^ ((row >> 1) & 7)) << 4));
+                    const int m = wm * C::WTM + i * 32 + row;
+                    const uint32_t off =
+                        (m < rows && n < cols) ? (((uint32_t)(row0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, kStoreDevice);
+                }
+                __asm__ __volatile__("" ::: "memory");
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int m = wm * C::WTM + i * C::MF + (lane % C::MF);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                constexpr int G = C::MF == 32 ? 4 : 1;
+#pragma unroll
+                for (int grp = 0; grp < G; ++grp) {
+                    const int n = C::MF == 32 ? wn * C::WTN + j * 32 + grp * 8 + (lane / 32) * 4
+                                              : wn * C::WTN + j * 16 + (lane / 16) * 4;
+                    const u32x2 v = {pack_bf16x2(st.acc[i][j][grp * 4 + 0], st.acc[i][j][grp * 4 + 1]),
+                                     pack_bf16x2(st.acc[i][j][grp * 4 + 2], st.acc[i][j][grp * 4 + 3])};
+                    const uint32_t off =
+                        (m < rows && n < cols) ? (((uint32_t)(row0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, kStoreDevice);
                 }
             }
         }
@@ -353,9 +467,6 @@ __device__ __forceinline__ void publish(const Args& a, int q, int flag, uint32_t
 }
 
 // ---------------------------------------------------------------- slice sum
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // acc + the 8 BF16 values packed in v (exact widening, one FP32 rounding per
 // element).
@@ -383,24 +494,13 @@ __device__ __forceinline__ u32x4 pack8(const f32x8& acc)
     return o;
 }
 
-// Engine loads go straight into a per-wave LDS area (LDS-direct global
-// loads), never through registers the compiler would consider live: the data is
-// read back with ds_read only after the step wait has certified its arrival.
-// Peer partials are read once (non-temporal: kept out of L2); the local slice
-// and the flags are read at device scope (sc1), so a copy left in this XCD's
-// L2 by an earlier run is never used.
-constexpr int kAuxNt = 2;
-constexpr int kAuxSc1 = 16;
-constexpr int kEngineSlotBytes = 1024;               // one 16-byte chunk per lane
-constexpr int kEngineSlots = 2;                      // per wave
-
 template <int AUX>
-__device__ __forceinline__ void lds_load16(const uint16_t* g, char* slot)
+__device__ __forceinline__ void lds_load16(const uint16_t* g, const char* slot)
 {
     __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)slot, 16, 0, AUX);
 }
 
-__device__ __forceinline__ void lds_load_flag(const uint32_t* g, char* slot)
+__device__ __forceinline__ void lds_load_flag(const uint32_t* g, const char* slot)
 {
     __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)slot, 4, 0, kAuxSc1);
 }
@@ -427,7 +527,7 @@ __device__ __forceinline__ void sum_chunk(const Args& a, const uint16_t* local, 
 // Sum a rows x cols block of the slice starting at (row0, col0), 16-byte
 // chunks distributed over `nthreads` threads starting at `tid`.
 __device__ __forceinline__ void sum_block(const Args& a, int row0, int rows, int col0, int cols, int tid,
-                                 int nthreads)
+                                          int nthreads)
 {
     const uint16_t* local = a.dst[a.g.rank];
     const int cpr = cols >> 3;
@@ -450,89 +550,111 @@ __device__ __forceinline__ void sum_block(const Args& a, int row0, int rows, int
 // ---------------------------------------------------------------- reduce engine
 //
 // The slice sum is cut into items: item i covers 64 16-byte chunks (512
-// elements) of own-slice tile u = i / IPT (schedule slot u), one chunk per lane;
-// an item spans 64 / (BN/8) consecutive rows of the tile, so a lane's offset
-// inside an item is a constant and the item's base offset is wave-uniform.
-// Compute wave gw (of W) owns items gw, gw + W, gw + 2W, ... -- tile order.
-// An item is summed in four steps of two loads each, in the sum order:
+// elements) of own-slice tile t = i / IPT, one chunk per lane, where own tiles
+// are numbered row-major (t = tile row * tile columns + tile column, so own
+// tile t carries ready flag rank * tiles_per_slice + t); an item spans
+// 64 / (BN/8) consecutive rows of the tile, so a lane's offset inside an item
+// is a constant and the item's base offset is wave-uniform.  Engine wave gw (of
+// W) owns items gw, gw + W, gw + 2W, ... -- tile order.  An item is summed in
+// four steps of two loads each, in the sum order:
 //   step 0: peers 0, 1    acc = (0 + p0) + p1
 //   step 1: peers 2, 3    acc = (acc + p2) + p3
 //   step 2: peers 4, 5    acc = (acc + p4) + p5
 //   step 3: peer 6 and, if the item's tile is flagged, the local partial:
 //           acc = (acc + p6) + local, stored to out; otherwise acc + p6 is
 //           parked in registers and a later FINISH adds the local partial.
-// POLL reads 64 ready flags (tiles anchor .. anchor+63, one per lane).  Peer
-// loads need no flag, so a wave pre-sums while its tiles are still being
-// computed.  Between MFMAs, every NS-1 K steps, a wave consumes its previous
-// operation and issues the next; the loads go straight into two per-wave LDS
-// slots and have completed by consumption time, because vector-memory
-// operations complete in issue order and the stage wait NS-1 steps later
-// covers a younger load.  After its last tile a wave drains its remaining
-// items, polling flags under the watchdog.
+// POLL reads 64 consecutive ready flags (own tiles anchor .. anchor+63, one
+// per lane).  Peer loads need no flag, so a wave pre-sums while its tiles are
+// still being computed.
+//
+// Operations are issued and consumed in order, two in flight: each engine slot
+// consumes the older operation and issues a new one.  The loads land in the
+// wave's two LDS areas (LDS-direct global loads), so no register is live while
+// they fly; the consumer waits with s_waitcnt until at most the vector-memory
+// instructions issued after the operation are outstanding (the wave counts
+// every one it issues: engine loads, out stores, epilogue stores).  Every lane
+// issues every load and store (lanes without a valid chunk read the slice's
+// first chunk or store out of bounds), so the count is exact.  The issue side
+// (which item, which step, parked items, readiness) runs ahead of the consume
+// side (the FP32 sums) by up to two operations.
 
 enum EngineOp { kOpNone = 0, kOpStep = 1, kOpFinish = 2, kOpPoll = 3 };
-constexpr int kPark = 2;  // parked FP32 partials per wave
 
-struct Engine {
-    char* slots;    // this wave's kEngineSlots LDS slots
-    int next;       // next owned item not yet started (wave-uniform)
-    int stride;     // compute waves W
-    int nitems;     // items of the slice
-    int ipt;        // items per tile
-    int rpi;        // tile rows per item
-    int lane_row, lane_col, lane_off;  // this lane's place inside an item
-    int op;         // operation in flight
-    int op_item, op_step, op_local;
-    int loads;      // vector loads the last engine step issued
-    int anchor;     // tile of bit 0 of `ready`
-    uint64_t ready; // ready tiles anchor .. anchor+63
-    int cur_item;   // item being summed, -1 if none
-    int cur_step;   // its next step
-    f32x8 cur;
-    int park_n;
-    int park_item[kPark];
-    f32x8 park[kPark];
-    uint32_t epoch;
+struct EngOp {
+    int op, item, step, local, area, anchor;
+    uint32_t vm_end;  // the wave's vector-memory count right after the operation's issue
 };
 
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+struct Engine {
+    char* areas;    // kEngAreas LDS areas of kEngAreaBytes
+    int next;       // next owned item not yet started
+    int stride;     // engine waves W
+    int nitems;     // items of the slice
+    int ipt, ipt_log2;  // items per tile (a power of two)
+    int rpi;        // tile rows per item
+    int lane_row, lane_col, lane_off;  // this lane's place inside an item
+    // issue side
+    int i_item;     // item whose steps are being issued, -1 if none
+    int i_step;     // its next step
+    int i_park_n;   // items parked, or to be parked by an operation in flight
+    int park_item[kPark];
+    int anchor;     // tile of bit 0 of `ready`
+    uint64_t ready; // ready tiles anchor .. anchor+63
+    int area;       // area of the next operation
+    // consume side
+    f32x8 acc;
+    int c_park_n;
+    f32x8 park[kPark];
+    // in flight, oldest first
+    EngOp o0, o1;
+    uint32_t vm;         // vector-memory instructions issued by this wave
+    uint32_t vm_stores;  // vm right after this wave's last epilogue stores
+    uint32_t epoch;
+};
 
 // Wave-uniform base offset of an item in the slice and whether this lane's
 // chunk lies inside the (possibly ragged) tile.
 __device__ __forceinline__ int64_t item_base(const Engine& e, const Args& a, int item, bool& valid)
 {
-    const int u = item / e.ipt;
-    const int j = item - u * e.ipt;
-    const TileCoord t = decode_slot(a.g, u);
+    const int t = item >> e.ipt_log2;
+    const int j = item & (e.ipt - 1);
+    const int tml = t / a.g.tnc;
+    const int tn = t - tml * a.g.tnc;
     const int row = j * e.rpi;
-    valid = row + e.lane_row < tile_rows(a.g, t) && e.lane_col < tile_cols(a.g, t);
-    return (int64_t)(t.tml * a.g.bm + row) * a.g.N + t.tn * a.g.bn;
+    const int trows = min(a.g.bm, a.g.S - tml * a.g.bm);
+    const int tcols = min(a.g.bn, a.g.N - tn * a.g.bn);
+    valid = row + e.lane_row < trows && e.lane_col < tcols;
+    return (int64_t)(tml * a.g.bm + row) * a.g.N + tn * a.g.bn;
 }
 
-__device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* slots, int gw, int waves,
+__device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* areas, int gw, int waves,
                                             uint32_t epoch)
 {
     const int lane = threadIdx.x & 63;
     const int cpr = a.g.bn >> 3;  // 16-byte chunks per tile row (8 .. 32)
-    e.slots = slots;
+    e.areas = areas;
     e.rpi = 64 / cpr;
     e.ipt = a.g.bm / e.rpi;
+    e.ipt_log2 = __builtin_ctz(e.ipt);
     e.nitems = a.g.ts * e.ipt;
     e.lane_row = lane / cpr;
     e.lane_col = (lane % cpr) * 8;
     e.lane_off = e.lane_row * a.g.N + e.lane_col;
     e.next = uni(gw);
     e.stride = waves;
-    e.op = kOpNone;
-    e.op_item = 0;
-    e.op_step = 0;
-    e.op_local = 0;
-    e.loads = 0;
+    e.i_item = -1;
+    e.i_step = 0;
+    e.i_park_n = 0;
+#pragma unroll
+    for (int p = 0; p < kPark; ++p) e.park_item[p] = 0;
     e.anchor = 0;
     e.ready = 0;
-    e.cur_item = -1;
-    e.cur_step = 0;
-    e.park_n = 0;
+    e.area = 0;
+    e.c_park_n = 0;
+    e.o0 = EngOp{kOpNone, 0, 0, 0, 0, 0, 0u};
+    e.o1 = e.o0;
+    e.vm = 0;
+    e.vm_stores = 0;
     e.epoch = epoch;
 }
 
@@ -542,13 +664,14 @@ __device__ __forceinline__ bool tile_ready(const Engine& e, int tile)
     return b >= 0 && b < 64 && ((e.ready >> b) & 1ull);
 }
 
-// Move the ready window so that it starts at the oldest tile still needed.
+// Move the ready window so that it starts at the oldest tile still needed
+// (issue side: parked items are older than the item being issued, which is
+// older than `next`).
 __device__ __forceinline__ void engine_reanchor(Engine& e)
 {
-    int want = e.park_n > 0 ? e.park_item[0] : e.next;
-    if (e.cur_item >= 0 && e.cur_item < want) want = e.cur_item;
+    int want = e.i_park_n > 0 ? e.park_item[0] : (e.i_item >= 0 ? e.i_item : e.next);
     if (want > e.nitems) want = e.nitems;
-    want /= e.ipt;
+    want >>= e.ipt_log2;
     const int sh = want - e.anchor;
     if (sh > 0) {
         e.ready = sh >= 64 ? 0ull : (e.ready >> sh);
@@ -556,135 +679,161 @@ __device__ __forceinline__ void engine_reanchor(Engine& e)
     }
 }
 
-__device__ __forceinline__ void store_out(const Engine& e, const Args& a, int item, const f32x8& acc)
+__device__ __forceinline__ char* area_ptr(const Engine& e, int area) { return e.areas + area * kEngAreaBytes; }
+
+__device__ __forceinline__ u32x4 engine_chunk(const Engine& e, int area, int k)
+{
+    return *reinterpret_cast<const u32x4*>(area_ptr(e, area) + k * 1024 + (threadIdx.x & 63) * 16);
+}
+
+// One 16-byte store of a finished chunk, issued by every lane (out of bounds
+// where the lane's chunk lies outside the tile).
+__device__ __forceinline__ void store_out(Engine& e, const Args& a, int item, const f32x8& acc)
 {
     bool valid;
     const int64_t base = item_base(e, a, item, valid);
-    if (valid) __builtin_nontemporal_store(pack8(acc), reinterpret_cast<u32x4*>(a.out + base + e.lane_off));
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
+    const uint32_t off = valid ? (uint32_t)(base + e.lane_off) * 2u : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, off, 0, kAuxNt);
+    e.vm += 1;
+}
+
+__device__ __forceinline__ void park_push(Engine& e, const f32x8& acc)
+{
+    // a value select per slot (no indexed store) keeps the partials in
+    // registers; the issue side admits at most kPark parked items
+#pragma unroll
+    for (int p = 0; p < kPark; ++p) e.park[p] = p == e.c_park_n ? acc : e.park[p];
+    ++e.c_park_n;
 }
 
 __device__ __forceinline__ void park_pop(Engine& e)
 {
 #pragma unroll
-    for (int p = 0; p + 1 < kPark; ++p) {
-        e.park_item[p] = e.park_item[p + 1];
-        e.park[p] = e.park[p + 1];
-    }
-    --e.park_n;
+    for (int p = 0; p + 1 < kPark; ++p) e.park[p] = e.park[p + 1];
+    --e.c_park_n;
 }
 
-__device__ __forceinline__ u32x4 engine_slot(const Engine& e, int k)
+__device__ __forceinline__ void park_item_pop(Engine& e)
 {
-    return *reinterpret_cast<const u32x4*>(e.slots + k * kEngineSlotBytes + (threadIdx.x & 63) * 16);
-}
-
-// Consume the operation in flight (its loads have completed).
-__device__ __forceinline__ void engine_consume(Engine& e, const Args& a)
-{
-    const int op = e.op;
-    if (op == kOpStep) {
-        const int s = e.op_step;
-        f32x8 acc = e.cur;
-        if (s == 0) acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        acc = add8(acc, engine_slot(e, 0));
-        if (s < 3 || e.op_local) acc = add8(acc, engine_slot(e, 1));
-        if (s < 3) {
-            e.cur = acc;
-            e.cur_step = s + 1;
-        } else if (e.op_local) {
-            store_out(e, a, e.op_item, acc);
-            e.cur_item = -1;
-        } else {
-            // a value select per slot (no indexed store) keeps the parked
-            // partials in registers
 #pragma unroll
-            for (int p = 0; p < kPark; ++p) {
-                const bool here = p == e.park_n;
-                e.park[p] = here ? acc : e.park[p];
-                e.park_item[p] = here ? e.op_item : e.park_item[p];
-            }
-            ++e.park_n;
-            e.cur_item = -1;
-        }
-    } else if (op == kOpFinish) {
-        store_out(e, a, e.park_item[0], add8(e.park[0], engine_slot(e, 1)));
-        park_pop(e);
-    } else if (op == kOpPoll) {
-        const int lane = threadIdx.x & 63;
-        const uint32_t f = *reinterpret_cast<const uint32_t*>(e.slots + lane * 4);
-        const bool mine = e.anchor + lane < a.g.ts;
-        e.ready |= __builtin_amdgcn_ballot_w64(mine && f == e.epoch);
-    }
-    e.op = kOpNone;
-    engine_reanchor(e);
+    for (int p = 0; p + 1 < kPark; ++p) e.park_item[p] = e.park_item[p + 1];
+    --e.i_park_n;
 }
 
-// Choose and issue the next operation.  Every lane issues every load (lanes
-// without a valid chunk read the slice's first chunk), so the number of
-// vector-memory instructions equals e.loads exactly.
-__device__ __forceinline__ void engine_issue(Engine& e, const Args& a)
+// Consume an operation whose loads have completed.
+__device__ __forceinline__ void engine_consume(Engine& e, const Args& a, const EngOp& o)
 {
-    int op = kOpNone, item = 0, step = 0, local = 0;
-    if (e.park_n > 0 && tile_ready(e, e.park_item[0] / e.ipt)) {
-        op = kOpFinish;
-        item = e.park_item[0];
-    } else if (e.cur_item >= 0) {
-        item = e.cur_item;
-        step = e.cur_step;
-        if (step < 3) {
-            op = kOpStep;
-        } else if (tile_ready(e, item / e.ipt)) {
-            op = kOpStep;
-            local = 1;
-        } else {
-            op = e.park_n < kPark ? kOpStep : kOpPoll;
-        }
-    } else if (e.next < e.nitems && (e.park_n < kPark || tile_ready(e, e.next / e.ipt))) {
-        op = kOpStep;
-        item = e.next;
-        e.cur_item = e.next;
-        e.cur_step = 0;
-        e.next += e.stride;
-    } else if (e.park_n > 0 || e.next < e.nitems) {
-        op = kOpPoll;
+    if (o.op == kOpStep) {
+        const int s = o.step;
+        f32x8 acc = e.acc;
+        if (s == 0) acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        acc = add8(acc, engine_chunk(e, o.area, 0));
+        if (s < 3 || o.local) acc = add8(acc, engine_chunk(e, o.area, 1));
+        if (s < 3)
+            e.acc = acc;
+        else if (o.local)
+            store_out(e, a, o.item, acc);
+        else
+            park_push(e, acc);
+    } else if (o.op == kOpFinish) {
+        store_out(e, a, o.item, add8(e.park[0], engine_chunk(e, o.area, 1)));
+        park_pop(e);
+    } else if (o.op == kOpPoll) {
+        const int lane = threadIdx.x & 63;
+        const uint32_t f = *reinterpret_cast<const uint32_t*>(area_ptr(e, o.area) + lane * 4);
+        const bool mine = o.anchor + lane < a.g.ts;
+        const uint64_t bits = __builtin_amdgcn_ballot_w64(mine && f == e.epoch);
+        // the window has only moved forward since the poll was issued
+        const int sh = e.anchor - o.anchor;
+        if (sh < 64) e.ready |= bits >> sh;
     }
-    e.op = op;
-    e.op_item = item;
-    e.op_step = step;
-    e.op_local = local;
-    e.loads = 0;
-    if (op == kOpStep || op == kOpFinish) {
+}
+
+// Choose and issue the next operation.
+__device__ __forceinline__ EngOp engine_issue(Engine& e, const Args& a)
+{
+    EngOp o{kOpNone, 0, 0, 0, e.area, e.anchor, 0u};
+    if (e.i_park_n > 0 && tile_ready(e, e.park_item[0] >> e.ipt_log2)) {
+        o.op = kOpFinish;
+        o.item = e.park_item[0];
+        park_item_pop(e);
+    } else if (e.i_item >= 0) {
+        o.item = e.i_item;
+        o.step = e.i_step;
+        if (e.i_step < 3) {
+            o.op = kOpStep;
+        } else if (tile_ready(e, e.i_item >> e.ipt_log2)) {
+            o.op = kOpStep;
+            o.local = 1;
+        } else if (e.i_park_n < kPark) {
+            o.op = kOpStep;
+#pragma unroll
+            for (int p = 0; p < kPark; ++p) e.park_item[p] = p == e.i_park_n ? e.i_item : e.park_item[p];
+            ++e.i_park_n;
+        } else {
+            o.op = kOpPoll;
+        }
+        if (o.op == kOpStep && ++e.i_step == 4) e.i_item = -1;
+    } else if (e.next < e.nitems && (e.i_park_n < kPark || tile_ready(e, e.next >> e.ipt_log2))) {
+        o.op = kOpStep;
+        o.item = e.next;
+        e.i_item = e.next;
+        e.i_step = 1;
+        e.next += e.stride;
+    } else if (e.i_park_n > 0 || e.next < e.nitems) {
+        o.op = kOpPoll;
+    }
+    char* ar = area_ptr(e, o.area);
+    if (o.op == kOpStep || o.op == kOpFinish) {
         bool valid;
-        const int64_t base = item_base(e, a, item, valid);
+        const int64_t base = item_base(e, a, o.item, valid);
         // lanes outside the (ragged) tile read the slice's first chunk
         const int64_t off = valid ? base + e.lane_off : 0;
-        if (op == kOpStep) {
-            const int p = 2 * step;
-            lds_load16<kAuxNt>(a.peers[p] + off, e.slots);
-            e.loads = 1;
-            if (step < 3) {
-                lds_load16<kAuxNt>(a.peers[p + 1] + off, e.slots + kEngineSlotBytes);
-                e.loads = 2;
+        if (o.op == kOpStep) {
+            const int p = 2 * o.step;
+            lds_load16<kAuxNt>(a.peers[p] + off, ar);
+            e.vm += 1;
+            if (o.step < 3) {
+                lds_load16<kAuxNt>(a.peers[p + 1] + off, ar + 1024);
+                e.vm += 1;
             }
         }
-        if (local || op == kOpFinish) {
-            lds_load16<kAuxSc1>(a.dst[a.g.rank] + off, e.slots + kEngineSlotBytes);
-            e.loads += 1;
+        if (o.local || o.op == kOpFinish) {
+            lds_load16<kAuxSc1>(a.dst[a.g.rank] + off, ar + 1024);
+            e.vm += 1;
         }
-    } else if (op == kOpPoll) {
+    } else if (o.op == kOpPoll) {
         const int lane = threadIdx.x & 63;
-        const int u = e.anchor + lane < a.g.ts ? e.anchor + lane : 0;
-        lds_load_flag(a.flags + (int64_t)decode_slot(a.g, u).flag * a.flag_stride, e.slots);
-        e.loads = 1;
+        const int t = e.anchor + lane < a.g.ts ? e.anchor + lane : 0;
+        lds_load_flag(a.flags + (int64_t)(a.g.rank * a.g.ts + t) * a.flag_stride, ar);
+        e.vm += 1;
     }
-    // keep every later memory operation (the stage's direct loads) behind these
-    // in issue order: completion is inferred from in-order vmcnt
+    o.vm_end = e.vm;
+    if (o.op != kOpNone) e.area ^= 1;
+    engine_reanchor(e);
+    // keep the issue order of these loads against later memory operations
     __builtin_amdgcn_sched_barrier(0);
+    return o;
+}
+
+// One engine slot: consume the older operation in flight, issue a new one.
+// Returns the operation just consumed.
+__device__ __forceinline__ int engine_step(Engine& e, const Args& a)
+{
+    const int done = e.o0.op;
+    if (done != kOpNone) {
+        wait_vmcnt_upto(e.vm - e.o0.vm_end);
+        engine_consume(e, a, e.o0);
+    }
+    e.o0 = e.o1;
+    e.o1 = engine_issue(e, a);
+    return done;
 }
 
 __device__ __forceinline__ bool engine_busy(const Engine& e)
 {
-    return e.op != kOpNone || e.cur_item >= 0 || e.park_n > 0 || e.next < e.nitems;
+    return e.o0.op != kOpNone || e.o1.op != kOpNone || e.i_item >= 0 || e.i_park_n > 0 || e.next < e.nitems;
 }
 
 // After the last tile: finish the wave's items, waiting for flags.  A tile
@@ -699,14 +848,12 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
     uint64_t last_ready = 0;
     bool gave_up = false;
     while (engine_busy(e)) {
-        if (e.op == kOpNone) engine_issue(e, a);
-        wait_vmcnt<0>();
-        const bool polled = e.op == kOpPoll;
-        engine_consume(e, a);
-        if (!polled) {
+        const int done = engine_step(e, a);
+        if (done != kOpPoll || e.o1.op != kOpPoll) {
             t0 = wall_clock64();
             continue;
         }
+        // polling only: back off, and watch for progress
         if (e.anchor != last_anchor || e.ready != last_ready) {
             last_anchor = e.anchor;
             last_ready = e.ready;
@@ -716,15 +863,24 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
         __builtin_amdgcn_s_sleep(2);
         if (gave_up || (int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
             gave_up = true;
-            // give up on the oldest pending item's tile
-            const int stuck = (e.park_n > 0 ? e.park_item[0] : (e.cur_item >= 0 ? e.cur_item : e.next)) / e.ipt;
+            // settle both operations in flight, then give up on the oldest
+            // pending item's tile
+            wait_vmcnt<0>();
+            engine_consume(e, a, e.o0);
+            engine_consume(e, a, e.o1);
+            e.o0.op = kOpNone;
+            e.o1.op = kOpNone;
+            const int stuck = (e.i_park_n > 0 ? e.park_item[0] : (e.i_item >= 0 ? e.i_item : e.next)) >> e.ipt_log2;
             if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
-                atomicExch(&a.state->status[1], decode_slot(a.g, stuck).flag);
+                atomicExch(&a.state->status[1], a.g.rank * a.g.ts + stuck);
 #pragma unroll
             for (int p = 0; p < kPark; ++p)
-                if (e.park_n > 0 && e.park_item[0] / e.ipt == stuck) park_pop(e);
-            if (e.cur_item >= 0 && e.cur_item / e.ipt == stuck) e.cur_item = -1;
-            while (e.cur_item < 0 && e.park_n == 0 && e.next < e.nitems && e.next / e.ipt == stuck)
+                if (e.i_park_n > 0 && (e.park_item[0] >> e.ipt_log2) == stuck) {
+                    park_item_pop(e);
+                    park_pop(e);
+                }
+            if (e.i_item >= 0 && (e.i_item >> e.ipt_log2) == stuck) e.i_item = -1;
+            while (e.i_item < 0 && e.i_park_n == 0 && e.next < e.nitems && (e.next >> e.ipt_log2) == stuck)
                 e.next += e.stride;
             engine_reanchor(e);
             t0 = wall_clock64();
@@ -732,60 +888,76 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
     }
 }
 
-// Per-tile hooks run by the K loop right after a stage barrier.
+// ---------------------------------------------------------------- tile loop
+
+// Per-tile state shared by the K loop and the role loop.
 struct StepHooks {
-    bool interleave; // run the reduce engine between MFMAs
+    bool interleave; // engine waves run the reduce engine between MFMAs
+    bool stores;     // the previous tile's epilogue stores are still in flight
     int pend_q;      // slot of the previous tile, whose flag is still to be stored
     int pend_flag;
     uint32_t who, epoch;
 };
 
-// Extra loads the reduce engine may have in flight inside the stage window.
+// Stage wait of a loader wave: B = (NS-2)*LPS younger direct loads may stay in
+// flight, plus the previous tile's C::STORES epilogue stores while they are
+// younger than the stage waited for (steps before NS-1).
 template <class C>
-__device__ __forceinline__ void wait_stage(int extra)
+__device__ __forceinline__ void wait_stage(bool stores)
 {
     constexpr int B = (C::NS - 2) * C::LPS;
-    static_assert(B + 2 <= 63, "vmcnt range");
-    switch (extra) {
-    case 1: wait_vmcnt<B + 1>(); break;
-    case 2: wait_vmcnt<B + 2>(); break;
-    default: wait_vmcnt<B>(); break;
-    }
+    if (stores)
+        wait_vmcnt<B + C::STORES>();
+    else
+        wait_vmcnt<B>();
 }
 
 // The K loop of one tile is split in two so that the next tile's first stages
-// can be issued before the current tile's epilogue stores (see compute_role).
+// can be issued before the current tile's epilogue stores (see compute_waves).
 // Stage kt lives in buffer kt % NS and NS-1 stages are always in flight
-// (stages past the end load zeros), so every step waits for the same count:
-// this thread's loads of stage kt are done once at most (NS-2)*LPS newer loads
-// (plus the engine's, see below) are outstanding.  The barrier then certifies
-// that every thread's loads of stage kt have landed and that every wave has
-// finished reading stage kt-1, whose buffer the step refills.
+// (stages past the end load zeros), so every step of a loader wave waits for
+// the same count; the barrier then certifies that every loader's loads of stage
+// kt have landed and that every wave has finished reading stage kt-1, whose
+// buffer the step refills.  Engine waves issue no stage loads: their waits
+// cover only their own epilogue stores (before a flag is published) and their
+// engine operations (inside engine_step).
 template <class C>
 struct TileJob {
     LoadPlan<C> lp;
     int nk;
 };
 
-template <class C>
+template <class C, bool LOADER>
 __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<C>& job, int row0, int rows,
                                               int n0, int cols)
 {
     const int K = a.g.K;
     job.nk = (K + C::BK - 1) / C::BK;
-    if (job.nk == 0) return;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
-    make_plan<C>(a, job.lp, row0, rows, n0, cols);
+    if constexpr (LOADER) {
+        if (job.nk == 0) return;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
+        make_plan<C>(a, job.lp, row0, rows, n0, cols);
 #pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s) issue_stage<C>(job.lp, rx, rw, lds + s * C::STAGE_BYTES, s * C::BK, K);
+        for (int s = 0; s < C::NS - 1; ++s) issue_stage<C>(job.lp, rx, rw, lds + s * C::STAGE_BYTES, s * C::BK, K);
+    }
+}
+
+// Wait until this wave's epilogue stores have completed.
+template <bool LOADER>
+__device__ __forceinline__ void wait_own_stores(const Engine& eng)
+{
+    if constexpr (LOADER)
+        wait_vmcnt<0>();
+    else
+        wait_vmcnt_upto(eng.vm - eng.vm_stores);
 }
 
 // Runs the K loop of a tile whose prologue has been issued.  The previous
 // tile's epilogue stores were issued after this tile's prologue and before the
 // first refill, so they have completed once the refill issued at step 0 has:
 // at step NS-1 (or after the loop) its flag is published.
-template <class C>
+template <class C, bool LOADER>
 __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
                                            StepHooks& hk, Engine& eng)
 {
@@ -800,31 +972,35 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
     const int nk = job.nk;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
-    constexpr int E = C::NS - 1 > 0 ? C::NS - 1 : 1;  // K steps between engine operations
     for (int kt = 0; kt < nk; ++kt) {
-        // engine loads issued inside the stage window (steps kt-NS+2 .. kt-1)
-        // may stay in flight: that is the engine step at kt - kt % E if kt % E
-        // is not 0 (with NS == 2 the window is empty)
-        const int extra = (C::NS > 2 && hk.interleave && kt % E != 0) ? eng.loads : 0;
-        wait_stage<C>(extra);
+        if constexpr (LOADER)
+            wait_stage<C>(hk.stores && kt < C::NS - 1);
+        else if (hk.stores && kt == C::NS - 1)
+            wait_own_stores<false>(eng);
         stage_barrier();
-        if (kt == C::NS - 1 && hk.pend_flag >= 0) {
-            if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
-            hk.pend_flag = -1;
+        if (kt == C::NS - 1) {
+            hk.stores = false;
+            if (hk.pend_flag >= 0) {
+                if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
+                hk.pend_flag = -1;
+            }
         }
-        if (hk.interleave && kt % E == 0) {
-            engine_consume(eng, a);
-            engine_issue(eng, a);
+        if constexpr (!LOADER) {
+            if (hk.interleave && kt % C::ENG_E == 0) engine_step(eng, a);
         }
         const int nxt = kt + C::NS - 1;
-        kstep<C>(job.lp, rx, rw, lds + (nxt % C::NS) * C::STAGE_BYTES, nxt * C::BK, K,
-                 lds + (kt % C::NS) * C::STAGE_BYTES, st);
+        kstep<C, LOADER>(job.lp, rx, rw, lds + (nxt % C::NS) * C::STAGE_BYTES, nxt * C::BK, K,
+                         lds + (kt % C::NS) * C::STAGE_BYTES, st);
     }
-    // drain the zero-filling loads past the end (and any engine loads), and
-    // let every wave finish reading LDS before the next tile's loads
-    // overwrite it; a flag still pending (nk < NS) is published here
-    wait_vmcnt<0>();
+    // loaders drain the zero-filling loads past the end; every wave finishes
+    // reading LDS before the next tile's loads overwrite it; a flag still
+    // pending (nk < NS) is published here
+    if constexpr (LOADER)
+        wait_vmcnt<0>();
+    else if (hk.stores)
+        wait_own_stores<false>(eng);
     stage_barrier();
+    hk.stores = false;
     if (hk.pend_flag >= 0) {
         if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
         hk.pend_flag = -1;
@@ -849,25 +1025,26 @@ __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int gr
     return s;
 }
 
-// Compute role of the l-th compute workgroup of group grp.  Round r covers
-// slots [r*C, r*C + C); the group's share of a round is its C_x slots, either a
-// contiguous block or every 8th slot (strided, used when all C_x are equal).
-// A tile's flag is stored after the next tile's first stage wait, which has
-// already waited for the tile's stores: publishing costs no extra wait.  With
-// no dedicated reducers, the waves also run the reduce engine.
-template <class C, bool FUSED>
-__device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, int l, uint32_t epoch, int base)
+// The tile loop of one wave of a compute workgroup at position `pos` of a
+// round.  Round r covers slots [r*C, r*C + C).  A tile's flag is stored once
+// the next tile's waits have covered the tile's stores: publishing costs no
+// extra wait.  Loader and engine waves run the same loop (the same barriers);
+// engine waves also run the reduce engine.
+template <class C, bool FUSED, bool LOADER>
+__device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos, uint32_t who, uint32_t epoch,
+                                              bool interleave)
 {
     const int Ctot = a.num_compute;
-    const int pos = a.strided ? (l * kGroups + grp) : (base + l);
-    const uint32_t who = ((uint32_t)grp << 16) | (uint32_t)l;
-    const bool interleave = FUSED && a.num_reducers == 0;
-    Engine eng;
     const int wave = uni((int)(threadIdx.x >> 6));
-    engine_init(eng, a, lds + C::LDS_BYTES + wave * kEngineSlots * kEngineSlotBytes, pos * C::WAVES + wave,
-                Ctot * C::WAVES, epoch);
+    Engine eng;
+    if constexpr (!LOADER) {
+        const int ew = wave - C::LW;
+        engine_init(eng, a, lds + C::LDS_BYTES + ew * kEngAreas * kEngAreaBytes, pos * C::EW + ew, Ctot * C::EW,
+                    epoch);
+    }
     StepHooks hk;
     hk.interleave = interleave;
+    hk.stores = false;
     hk.pend_q = -1;
     hk.pend_flag = -1;
     hk.who = who;
@@ -878,20 +1055,29 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
     TileCoord t;
     if (q < a.g.tiles) {
         t = decode_slot(a.g, q);
-        tile_prologue<C>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
+        tile_prologue<C, LOADER>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN,
+                                 tile_cols(a.g, t));
     }
     while (q < a.g.tiles) {
-        tile_kloop<C>(a, lds, st, job, hk, eng);
+        tile_kloop<C, LOADER>(a, lds, st, job, hk, eng);
         // issue the next tile's first stages before this tile's stores
         const int qn = q + Ctot;
         TileCoord tn = t;
         if (qn < a.g.tiles) {
             tn = decode_slot(a.g, qn);
-            tile_prologue<C>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
-                             tile_cols(a.g, tn));
+            tile_prologue<C, LOADER>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
+                                     tile_cols(a.g, tn));
         }
-        uint16_t* dst = a.dst[t.d] + (int64_t)t.tml * C::BM * a.g.N;
-        store_tile<C, FUSED>(a, st, dst, tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
+        // the stage buffer the next tile's prologue left free holds the
+        // epilogue staging areas
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.dst[t.d], 0, a.slice_bytes, kRsrcFlags);
+        store_tile<C>(a, st, lds + (C::NS - 1) * C::STAGE_BYTES, rd, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN,
+                      tile_cols(a.g, t));
+        hk.stores = true;
+        if constexpr (!LOADER) {
+            eng.vm += C::STORES;
+            eng.vm_stores = eng.vm;
+        }
         if (FUSED) {
             hk.pend_q = q;
             hk.pend_flag = t.flag;
@@ -900,11 +1086,29 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
         t = tn;
     }
     if (hk.pend_flag >= 0) {
-        wait_vmcnt<0>();
+        wait_own_stores<LOADER>(eng);
         stage_barrier();
         if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
-    if (interleave) engine_drain(eng, a);
+    if constexpr (!LOADER) {
+        if (interleave) engine_drain(eng, a);
+    }
+}
+
+// Compute role of the l-th compute workgroup of group grp: its position in a
+// round is either the group's block offset + l (contiguous split) or
+// l * 8 + grp (strided, used when all C_x are equal).
+template <class C, bool FUSED>
+__device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, int l, uint32_t epoch, int base)
+{
+    const int pos = a.strided ? (l * kGroups + grp) : (base + l);
+    const uint32_t who = ((uint32_t)grp << 16) | (uint32_t)l;
+    const bool interleave = FUSED && C::EW > 0 && a.num_reducers == 0;
+    const int wave = uni((int)(threadIdx.x >> 6));
+    if (wave < C::LW)
+        compute_waves<C, FUSED, true>(a, lds, pos, who, epoch, interleave);
+    else
+        compute_waves<C, FUSED, false>(a, lds, pos, who, epoch, interleave);
 }
 
 // Dedicated reducer role (used when reducers are requested): claim own-slice
