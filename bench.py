@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tile", default="auto")
     p.add_argument("--reducers", type=int, default=-1)
-    p.add_argument("--protocol", type=int, default=0)
+    p.add_argument("--engine-interval", type=int, default=0,
+                   help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
     p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
     return p.parse_args()
 
@@ -86,7 +87,7 @@ class Case:
         self.local = z()
         self.out = z()
         self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
-                            num_reducers=args.reducers, flag_protocol=args.protocol)
+                            num_reducers=args.reducers, engine_interval=args.engine_interval)
         self.gr = gr
 
     def run(self, mode):
@@ -157,6 +158,36 @@ def time_replays(fn, warmup, iters, per_graph=10):
     return [s.elapsed_time(e) * 1e3 / per_graph for s, e in ev]
 
 
+def time_interleaved(fns, warmup_s=0.3, rounds=20, per_graph=10):
+    """Per-launch times (us) of several launch sequences measured side by side:
+    each is captured as a graph of per_graph launches; the graphs are replayed
+    in turn for about warmup_s seconds (clocks and caches settle), then for
+    `rounds` rounds, each replaying every graph once (the order rotates from
+    round to round) between events.  Returns {name: [us per launch, ...]}."""
+    import torch
+
+    graphs = {k: Replay(f, per_graph) for k, f in fns.items()}
+    names = list(graphs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warmup_s:
+        for k in names:
+            graphs[k].replay()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = {k: [] for k in names}
+    for r in range(rounds):
+        order = names[r % len(names):] + names[:r % len(names)]
+        for k in order:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            graphs[k].replay()
+            e.record(stream)
+            ev[k].append((s, e))
+    torch.cuda.synchronize()
+    return {k: [s.elapsed_time(e) * 1e3 / per_graph for s, e in v] for k, v in ev.items()}
+
+
 def summary(us):
     q = statistics.quantiles(us, n=10) if len(us) >= 2 else [us[0]] * 9
     return {"median_us": statistics.median(us), "mean_us": statistics.fmean(us), "p10_us": q[0],
@@ -166,11 +197,14 @@ def summary(us):
 def measure_case(c: Case, warmup, iters):
     gr = c.gr
     cfg = c.cfg
-    fused = summary(time_replays(lambda: c.run(gr.MODE_FUSED), warmup, iters))
-    gemm = summary(time_replays(lambda: c.run(gr.MODE_GEMM_ONLY), warmup, iters))
-    red = summary(time_replays(lambda: c.run(gr.MODE_REDUCE_ONLY), warmup, iters))
-    seq = summary(time_replays(lambda: c.run(gr.MODE_SEQUENTIAL), warmup, iters))
-    mm = summary(time_replays(c.matmul, warmup, iters))
+    t = time_interleaved({
+        "fused": lambda: c.run(gr.MODE_FUSED),
+        "gemm": lambda: c.run(gr.MODE_GEMM_ONLY),
+        "reduce": lambda: c.run(gr.MODE_REDUCE_ONLY),
+        "seq": lambda: c.run(gr.MODE_SEQUENTIAL),
+        "matmul": c.matmul,
+    }, rounds=max(4, -(-iters // 10)))
+    fused, gemm, red, seq, mm = (summary(t[k]) for k in ("fused", "gemm", "reduce", "seq", "matmul"))
     st = c.op.status()
     if st != gr.OK:
         raise RuntimeError(f"{c.name}: device status {gr.gemm_rs_strerror(st)}")

@@ -77,7 +77,7 @@ extern "C" {
 #define GEMM_RS_MODE_REDUCE_ONLY 2 /* standalone slice sum of local + peers      */
 #define GEMM_RS_MODE_SEQUENTIAL 3  /* GEMM_ONLY then REDUCE_ONLY on one stream   */
 
-/* ---- tile configurations (BM x BN output tile, BK = 64) ------------------ */
+/* ---- tile configurations (BM x BN output tile) ---------------------------- */
 #define GEMM_RS_TILE_AUTO 0
 #define GEMM_RS_TILE_16x64 1
 #define GEMM_RS_TILE_64x128 2
@@ -86,10 +86,6 @@ extern "C" {
 #define GEMM_RS_TILE_256x128 5
 #define GEMM_RS_TILE_256x256 6
 #define GEMM_RS_TILE_COUNT 7
-
-/* ---- flag protocols (how a finished tile is published) ------------------- */
-#define GEMM_RS_FLAG_WAVE_FENCE 0 /* every wave: agent release fence; barrier; one store */
-#define GEMM_RS_FLAG_WG_RELEASE 1 /* barrier; one agent-scope release store          */
 
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
@@ -104,7 +100,10 @@ typedef struct gemm_rs_config {
     int32_t tile;         /* GEMM_RS_TILE_*                                   */
     int32_t group_m;      /* tile rows per raster group; 0 = automatic        */
     int32_t num_reducers; /* reducer workgroups in FUSED mode; -1 = automatic */
-    int32_t flag_protocol;/* GEMM_RS_FLAG_*                                   */
+    int32_t engine_interval; /* FUSED without reducer workgroups: K steps between
+                             reduce-engine slots inside the compute loop;
+                             0 = the engine waves sum the slice after their
+                             last tile (0 .. 4096)                          */
     int32_t debug_flags;  /* GEMM_RS_DEBUG_* bits                             */
     int32_t drop_flag;    /* debug: index of a ready flag the producer never
                              releases, to exercise the watchdog; -1 = none    */

@@ -197,8 +197,7 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->tile < 0 || c->tile >= GEMM_RS_TILE_COUNT) return GEMM_RS_ERR_INVALID_ARG;
     if (c->group_m < 0) return GEMM_RS_ERR_INVALID_ARG;
     if (c->num_reducers < -1) return GEMM_RS_ERR_INVALID_ARG;
-    if (c->flag_protocol != GEMM_RS_FLAG_WAVE_FENCE && c->flag_protocol != GEMM_RS_FLAG_WG_RELEASE)
-        return GEMM_RS_ERR_INVALID_ARG;
+    if (c->engine_interval < 0 || c->engine_interval > 4096) return GEMM_RS_ERR_INVALID_ARG;
     if (c->debug_flags & ~GEMM_RS_DEBUG_TRACE) return GEMM_RS_ERR_INVALID_ARG;
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
@@ -389,6 +388,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.flag_stride = h->flag_stride;
     a.drop_flag = h->cfg.drop_flag;
     a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
+    a.engine_every = h->cfg.engine_interval;
 }
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)

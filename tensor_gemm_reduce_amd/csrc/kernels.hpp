@@ -74,12 +74,10 @@ constexpr int kAuxNt = 2;
 constexpr int kAuxSc1 = 16;
 
 // Reduce engine: 16-byte loads per operation (one per lane each), LDS bytes an
-// operation lands in, operations in flight per engine wave, and parked FP32
-// partial sums per engine wave.
+// operation lands in, operations in flight per engine wave.
 constexpr int kEngLoads = 2;
 constexpr int kEngAreaBytes = kEngLoads * 1024;
 constexpr int kEngAreas = 2;
-constexpr int kPark = 2;
 
 // Handle-owned device state, zeroed at creation.
 struct DeviceState {
@@ -111,6 +109,7 @@ struct Args {
     int32_t fused;           // 1: release flags, reducers run, epoch advances
     int32_t drop_flag;
     int32_t trace_on;
+    int32_t engine_every;    // K steps between reduce-engine slots (0: reduce after the last tile)
 };
 
 // BM x BN output tile, BK deep stages, NS stages in LDS, WAVES_M x WAVES_N
@@ -157,11 +156,6 @@ struct TileCfg {
     static constexpr int STORES = STAGED_EPI ? FM * (WTN / 64) * 4 : FM * FN * (MF == 32 ? 4 : 1);
     static_assert(!STAGED_EPI || WAVES * EPI_AREA <= STAGE_BYTES, "epilogue staging fits one stage buffer");
     static_assert((NS - 2) * LPS + STORES <= 63, "vmcnt range");
-    // Reduce engine: one operation every ENG_E K steps, so that an operation's
-    // loads get about 2 * 2600 cycles before they are consumed (STEP_CYCLES
-    // estimates one K step with two waves per SIMD).
-    static constexpr int STEP_CYCLES = KSUB * FM * FN * (MF == 32 ? 32 : 16) * 2;
-    static constexpr int ENG_E = (2600 + STEP_CYCLES - 1) / STEP_CYCLES;
     static constexpr int ENG_LDS = EW * kEngAreas * kEngAreaBytes;
 };
 
@@ -555,33 +549,31 @@ __device__ __forceinline__ void sum_block(const Args& a, int row0, int rows, int
 // tile t carries ready flag rank * tiles_per_slice + t); an item spans
 // 64 / (BN/8) consecutive rows of the tile, so a lane's offset inside an item
 // is a constant and the item's base offset is wave-uniform.  Engine wave gw (of
-// W) owns items gw, gw + W, gw + 2W, ... -- tile order.  An item is summed in
-// four steps of two loads each, in the sum order:
-//   step 0: peers 0, 1    acc = (0 + p0) + p1
-//   step 1: peers 2, 3    acc = (acc + p2) + p3
-//   step 2: peers 4, 5    acc = (acc + p4) + p5
-//   step 3: peer 6 and, if the item's tile is flagged, the local partial:
-//           acc = (acc + p6) + local, stored to out; otherwise acc + p6 is
-//           parked in registers and a later FINISH adds the local partial.
-// POLL reads 64 consecutive ready flags (own tiles anchor .. anchor+63, one
-// per lane).  Peer loads need no flag, so a wave pre-sums while its tiles are
-// still being computed.
+// W) owns items gw, gw + W, gw + 2W, ... -- tile order.
 //
-// Operations are issued and consumed in order, two in flight: each engine slot
-// consumes the older operation and issues a new one.  The loads land in the
-// wave's two LDS areas (LDS-direct global loads), so no register is live while
-// they fly; the consumer waits with s_waitcnt until at most the vector-memory
-// instructions issued after the operation are outstanding (the wave counts
-// every one it issues: engine loads, out stores, epilogue stores).  Every lane
-// issues every load and store (lanes without a valid chunk read the slice's
-// first chunk or store out of bounds), so the count is exact.  The issue side
-// (which item, which step, parked items, readiness) runs ahead of the consume
-// side (the FP32 sums) by up to two operations.
+// Between MFMAs an engine wave sums the items whose tile is flagged, in four
+// steps of two loads each, in the sum order:
+//   step 0: peers 0, 1      acc = (0 + p0) + p1
+//   step 1: peers 2, 3      acc = (acc + p2) + p3
+//   step 2: peers 4, 5      acc = (acc + p4) + p5
+//   step 3: peer 6, local   acc = (acc + p6) + local, rounded and stored to out
+// and otherwise polls: POLL reads 64 consecutive ready flags (own tiles
+// anchor .. anchor+63, one per lane).  Operations are issued and consumed in
+// order, two in flight: each engine slot consumes the older operation and
+// issues a new one.  The loads land in the wave's two LDS areas (LDS-direct
+// global loads), so no register is live while they fly; the consumer waits
+// with s_waitcnt until at most the vector-memory instructions issued after the
+// operation are outstanding (the wave counts every one it issues: engine
+// loads, out stores, epilogue stores).  Every lane issues every load and store
+// (lanes without a valid chunk read the slice's first chunk and store out of
+// bounds), so the count is exact.  Items still open after the wave's last
+// tile are summed by engine_drain.
 
-enum EngineOp { kOpNone = 0, kOpStep = 1, kOpFinish = 2, kOpPoll = 3 };
+enum EngineOp { kOpNone = 0, kOpStep = 1, kOpPoll = 2 };
 
 struct EngOp {
-    int op, item, step, local, area, anchor;
+    int op, step, area, anchor;
+    uint32_t soff;    // STEP 3: this lane's byte offset in out (kOob: no valid chunk)
     uint32_t vm_end;  // the wave's vector-memory count right after the operation's issue
 };
 
@@ -594,17 +586,15 @@ struct Engine {
     int rpi;        // tile rows per item
     int lane_row, lane_col, lane_off;  // this lane's place inside an item
     // issue side
-    int i_item;     // item whose steps are being issued, -1 if none
+    int i_item;     // item being issued, -1 if none
     int i_step;     // its next step
-    int i_park_n;   // items parked, or to be parked by an operation in flight
-    int park_item[kPark];
+    uint32_t i_off; // this lane's element offset in the slice (0 if no valid chunk)
+    uint32_t i_soff;
     int anchor;     // tile of bit 0 of `ready`
     uint64_t ready; // ready tiles anchor .. anchor+63
     int area;       // area of the next operation
     // consume side
     f32x8 acc;
-    int c_park_n;
-    f32x8 park[kPark];
     // in flight, oldest first
     EngOp o0, o1;
     uint32_t vm;         // vector-memory instructions issued by this wave
@@ -612,9 +602,11 @@ struct Engine {
     uint32_t epoch;
 };
 
-// Wave-uniform base offset of an item in the slice and whether this lane's
-// chunk lies inside the (possibly ragged) tile.
-__device__ __forceinline__ int64_t item_base(const Engine& e, const Args& a, int item, bool& valid)
+// Element offset of this lane's chunk of an item in the slice (0 if the chunk
+// lies outside the possibly ragged tile) and its byte offset for a store
+// (kOob then).  Wave-uniform except for the lane's own place.
+__device__ __forceinline__ void item_offsets(const Engine& e, const Args& a, int item, uint32_t& off,
+                                             uint32_t& soff)
 {
     const int t = item >> e.ipt_log2;
     const int j = item & (e.ipt - 1);
@@ -623,8 +615,10 @@ __device__ __forceinline__ int64_t item_base(const Engine& e, const Args& a, int
     const int row = j * e.rpi;
     const int trows = min(a.g.bm, a.g.S - tml * a.g.bm);
     const int tcols = min(a.g.bn, a.g.N - tn * a.g.bn);
-    valid = row + e.lane_row < trows && e.lane_col < tcols;
-    return (int64_t)(tml * a.g.bm + row) * a.g.N + tn * a.g.bn;
+    const bool valid = row + e.lane_row < trows && e.lane_col < tcols;
+    const uint32_t base = (uint32_t)(tml * a.g.bm + row) * (uint32_t)a.g.N + (uint32_t)(tn * a.g.bn);
+    off = valid ? base + (uint32_t)e.lane_off : 0u;
+    soff = valid ? (base + (uint32_t)e.lane_off) * 2u : kOob;
 }
 
 __device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* areas, int gw, int waves,
@@ -644,14 +638,12 @@ __device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* area
     e.stride = waves;
     e.i_item = -1;
     e.i_step = 0;
-    e.i_park_n = 0;
-#pragma unroll
-    for (int p = 0; p < kPark; ++p) e.park_item[p] = 0;
+    e.i_off = 0;
+    e.i_soff = kOob;
     e.anchor = 0;
     e.ready = 0;
     e.area = 0;
-    e.c_park_n = 0;
-    e.o0 = EngOp{kOpNone, 0, 0, 0, 0, 0, 0u};
+    e.o0 = EngOp{kOpNone, 0, 0, 0, kOob, 0u};
     e.o1 = e.o0;
     e.vm = 0;
     e.vm_stores = 0;
@@ -664,12 +656,10 @@ __device__ __forceinline__ bool tile_ready(const Engine& e, int tile)
     return b >= 0 && b < 64 && ((e.ready >> b) & 1ull);
 }
 
-// Move the ready window so that it starts at the oldest tile still needed
-// (issue side: parked items are older than the item being issued, which is
-// older than `next`).
+// Move the ready window so that it starts at the oldest tile still needed.
 __device__ __forceinline__ void engine_reanchor(Engine& e)
 {
-    int want = e.i_park_n > 0 ? e.park_item[0] : (e.i_item >= 0 ? e.i_item : e.next);
+    int want = e.i_item >= 0 ? e.i_item : e.next;
     if (want > e.nitems) want = e.nitems;
     want >>= e.ipt_log2;
     const int sh = want - e.anchor;
@@ -686,59 +676,20 @@ __device__ __forceinline__ u32x4 engine_chunk(const Engine& e, int area, int k)
     return *reinterpret_cast<const u32x4*>(area_ptr(e, area) + k * 1024 + (threadIdx.x & 63) * 16);
 }
 
-// One 16-byte store of a finished chunk, issued by every lane (out of bounds
-// where the lane's chunk lies outside the tile).
-__device__ __forceinline__ void store_out(Engine& e, const Args& a, int item, const f32x8& acc)
-{
-    bool valid;
-    const int64_t base = item_base(e, a, item, valid);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
-    const uint32_t off = valid ? (uint32_t)(base + e.lane_off) * 2u : kOob;
-    __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, off, 0, kAuxNt);
-    e.vm += 1;
-}
-
-__device__ __forceinline__ void park_push(Engine& e, const f32x8& acc)
-{
-    // a value select per slot (no indexed store) keeps the partials in
-    // registers; the issue side admits at most kPark parked items
-#pragma unroll
-    for (int p = 0; p < kPark; ++p) e.park[p] = p == e.c_park_n ? acc : e.park[p];
-    ++e.c_park_n;
-}
-
-__device__ __forceinline__ void park_pop(Engine& e)
-{
-#pragma unroll
-    for (int p = 0; p + 1 < kPark; ++p) e.park[p] = e.park[p + 1];
-    --e.c_park_n;
-}
-
-__device__ __forceinline__ void park_item_pop(Engine& e)
-{
-#pragma unroll
-    for (int p = 0; p + 1 < kPark; ++p) e.park_item[p] = e.park_item[p + 1];
-    --e.i_park_n;
-}
-
 // Consume an operation whose loads have completed.
 __device__ __forceinline__ void engine_consume(Engine& e, const Args& a, const EngOp& o)
 {
     if (o.op == kOpStep) {
-        const int s = o.step;
-        f32x8 acc = e.acc;
-        if (s == 0) acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        f32x8 acc = o.step == 0 ? f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f} : e.acc;
         acc = add8(acc, engine_chunk(e, o.area, 0));
-        if (s < 3 || o.local) acc = add8(acc, engine_chunk(e, o.area, 1));
-        if (s < 3)
+        acc = add8(acc, engine_chunk(e, o.area, 1));
+        if (o.step < 3) {
             e.acc = acc;
-        else if (o.local)
-            store_out(e, a, o.item, acc);
-        else
-            park_push(e, acc);
-    } else if (o.op == kOpFinish) {
-        store_out(e, a, o.item, add8(e.park[0], engine_chunk(e, o.area, 1)));
-        park_pop(e);
+        } else {
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, o.soff, 0, kAuxNt);
+            e.vm += 1;
+        }
     } else if (o.op == kOpPoll) {
         const int lane = threadIdx.x & 63;
         const uint32_t f = *reinterpret_cast<const uint32_t*>(area_ptr(e, o.area) + lane * 4);
@@ -750,60 +701,45 @@ __device__ __forceinline__ void engine_consume(Engine& e, const Args& a, const E
     }
 }
 
-// Choose and issue the next operation.
-__device__ __forceinline__ EngOp engine_issue(Engine& e, const Args& a)
+// Choose and issue the next operation; with `start` false no new item is
+// begun and no flag is polled.
+__device__ __forceinline__ EngOp engine_issue(Engine& e, const Args& a, bool start)
 {
-    EngOp o{kOpNone, 0, 0, 0, e.area, e.anchor, 0u};
-    if (e.i_park_n > 0 && tile_ready(e, e.park_item[0] >> e.ipt_log2)) {
-        o.op = kOpFinish;
-        o.item = e.park_item[0];
-        park_item_pop(e);
-    } else if (e.i_item >= 0) {
-        o.item = e.i_item;
-        o.step = e.i_step;
-        if (e.i_step < 3) {
-            o.op = kOpStep;
-        } else if (tile_ready(e, e.i_item >> e.ipt_log2)) {
-            o.op = kOpStep;
-            o.local = 1;
-        } else if (e.i_park_n < kPark) {
-            o.op = kOpStep;
-#pragma unroll
-            for (int p = 0; p < kPark; ++p) e.park_item[p] = p == e.i_park_n ? e.i_item : e.park_item[p];
-            ++e.i_park_n;
-        } else {
-            o.op = kOpPoll;
-        }
-        if (o.op == kOpStep && ++e.i_step == 4) e.i_item = -1;
-    } else if (e.next < e.nitems && (e.i_park_n < kPark || tile_ready(e, e.next >> e.ipt_log2))) {
-        o.op = kOpStep;
-        o.item = e.next;
+    EngOp o{kOpNone, 0, e.area, e.anchor, kOob, 0u};
+    if (start && e.i_item < 0 && e.next < e.nitems && tile_ready(e, e.next >> e.ipt_log2)) {
         e.i_item = e.next;
-        e.i_step = 1;
+        e.i_step = 0;
         e.next += e.stride;
-    } else if (e.i_park_n > 0 || e.next < e.nitems) {
-        o.op = kOpPoll;
+        item_offsets(e, a, e.i_item, e.i_off, e.i_soff);
     }
     char* ar = area_ptr(e, o.area);
-    if (o.op == kOpStep || o.op == kOpFinish) {
-        bool valid;
-        const int64_t base = item_base(e, a, o.item, valid);
-        // lanes outside the (ragged) tile read the slice's first chunk
-        const int64_t off = valid ? base + e.lane_off : 0;
-        if (o.op == kOpStep) {
-            const int p = 2 * o.step;
-            lds_load16<kAuxNt>(a.peers[p] + off, ar);
-            e.vm += 1;
-            if (o.step < 3) {
-                lds_load16<kAuxNt>(a.peers[p + 1] + off, ar + 1024);
-                e.vm += 1;
-            }
-        }
-        if (o.local || o.op == kOpFinish) {
+    if (e.i_item >= 0) {
+        o.op = kOpStep;
+        o.step = e.i_step;
+        o.soff = e.i_soff;
+        const uint32_t off = e.i_off;
+        switch (e.i_step) {
+        case 0:
+            lds_load16<kAuxNt>(a.peers[0] + off, ar);
+            lds_load16<kAuxNt>(a.peers[1] + off, ar + 1024);
+            break;
+        case 1:
+            lds_load16<kAuxNt>(a.peers[2] + off, ar);
+            lds_load16<kAuxNt>(a.peers[3] + off, ar + 1024);
+            break;
+        case 2:
+            lds_load16<kAuxNt>(a.peers[4] + off, ar);
+            lds_load16<kAuxNt>(a.peers[5] + off, ar + 1024);
+            break;
+        default:
+            lds_load16<kAuxNt>(a.peers[6] + off, ar);
             lds_load16<kAuxSc1>(a.dst[a.g.rank] + off, ar + 1024);
-            e.vm += 1;
+            break;
         }
-    } else if (o.op == kOpPoll) {
+        e.vm += 2;
+        if (++e.i_step == 4) e.i_item = -1;
+    } else if (start && e.next < e.nitems) {
+        o.op = kOpPoll;
         const int lane = threadIdx.x & 63;
         const int t = e.anchor + lane < a.g.ts ? e.anchor + lane : 0;
         lds_load_flag(a.flags + (int64_t)(a.g.rank * a.g.ts + t) * a.flag_stride, ar);
@@ -818,72 +754,78 @@ __device__ __forceinline__ EngOp engine_issue(Engine& e, const Args& a)
 }
 
 // One engine slot: consume the older operation in flight, issue a new one.
-// Returns the operation just consumed.
-__device__ __forceinline__ int engine_step(Engine& e, const Args& a)
+__device__ __forceinline__ void engine_step(Engine& e, const Args& a, bool start)
 {
-    const int done = e.o0.op;
-    if (done != kOpNone) {
+    if (e.o0.op != kOpNone) {
         wait_vmcnt_upto(e.vm - e.o0.vm_end);
         engine_consume(e, a, e.o0);
     }
     e.o0 = e.o1;
-    e.o1 = engine_issue(e, a);
-    return done;
+    e.o1 = engine_issue(e, a, start);
 }
 
-__device__ __forceinline__ bool engine_busy(const Engine& e)
+// Waits (device-scope polls, short sleeps) until own tile t is flagged.  The
+// first wait that exceeds the watchdog limit reports the tile and sets
+// gave_up; after that no wait blocks, so a drain never waits longer than one
+// watchdog period in total.
+__device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, bool& gave_up)
 {
-    return e.o0.op != kOpNone || e.o1.op != kOpNone || e.i_item >= 0 || e.i_park_n > 0 || e.next < e.nitems;
+    const int flag = a.g.rank * a.g.ts + t;
+    const uint32_t* f = a.flags + (int64_t)flag * a.flag_stride;
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
+    if (gave_up) return false;
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+        __builtin_amdgcn_s_sleep(2);
+        if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
+            gave_up = true;
+            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
+                atomicExch(&a.state->status[1], flag);
+            return false;
+        }
+    }
+    return true;
 }
 
-// After the last tile: finish the wave's items, waiting for flags.  A tile
-// whose flag does not arrive within the watchdog limit is reported and its
-// items are skipped; after one timeout the wave waits no more (a later tile
-// that is still not flagged is skipped at once), so a drain never waits longer
-// than one watchdog period in total.
+// The whole sum of one item with plain loads (drain): 7 peer chunks and the
+// local chunk, in the sum order.
+__device__ __forceinline__ void sum_item(const Engine& e, const Args& a, int item)
+{
+    uint32_t off, soff;
+    item_offsets(e, a, item, off, soff);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(a.dst[a.g.rank], 0, a.slice_bytes, kRsrcFlags);
+    u32x4 v[kPeers + 1];
+#pragma unroll
+    for (int s = 0; s < kPeers; ++s)
+        v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.peers[s] + off));
+    v[kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off * 2u, 0, kAuxSc1));
+    f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[s]);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
+    __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, soff, 0, kAuxNt);
+}
+
+// After the last tile: settle the operations in flight and the item being
+// summed (its tile is flagged), then sum the wave's remaining items two at a
+// time with plain loads, each once its tile is flagged.  A tile whose flag does
+// not arrive within the watchdog limit is reported and its items are skipped.
 __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
 {
-    uint64_t t0 = wall_clock64();
-    int last_anchor = -1;
-    uint64_t last_ready = 0;
+    while (e.o0.op != kOpNone || e.o1.op != kOpNone || e.i_item >= 0) engine_step(e, a, false);
+    wait_vmcnt<0>();
     bool gave_up = false;
-    while (engine_busy(e)) {
-        const int done = engine_step(e, a);
-        if (done != kOpPoll || e.o1.op != kOpPoll) {
-            t0 = wall_clock64();
-            continue;
-        }
-        // polling only: back off, and watch for progress
-        if (e.anchor != last_anchor || e.ready != last_ready) {
-            last_anchor = e.anchor;
-            last_ready = e.ready;
-            t0 = wall_clock64();
-            continue;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        if (gave_up || (int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
-            gave_up = true;
-            // settle both operations in flight, then give up on the oldest
-            // pending item's tile
-            wait_vmcnt<0>();
-            engine_consume(e, a, e.o0);
-            engine_consume(e, a, e.o1);
-            e.o0.op = kOpNone;
-            e.o1.op = kOpNone;
-            const int stuck = (e.i_park_n > 0 ? e.park_item[0] : (e.i_item >= 0 ? e.i_item : e.next)) >> e.ipt_log2;
-            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
-                atomicExch(&a.state->status[1], a.g.rank * a.g.ts + stuck);
-#pragma unroll
-            for (int p = 0; p < kPark; ++p)
-                if (e.i_park_n > 0 && (e.park_item[0] >> e.ipt_log2) == stuck) {
-                    park_item_pop(e);
-                    park_pop(e);
-                }
-            if (e.i_item >= 0 && (e.i_item >> e.ipt_log2) == stuck) e.i_item = -1;
-            while (e.i_item < 0 && e.i_park_n == 0 && e.next < e.nitems && (e.next >> e.ipt_log2) == stuck)
-                e.next += e.stride;
-            engine_reanchor(e);
-            t0 = wall_clock64();
+    for (int item = e.next; item < e.nitems; item += 2 * e.stride) {
+        const int item2 = item + e.stride;
+        const bool ok1 = wait_tile(a, e.epoch, item >> e.ipt_log2, gave_up);
+        const bool ok2 = item2 < e.nitems && wait_tile(a, e.epoch, item2 >> e.ipt_log2, gave_up);
+        if (ok1 && ok2) {
+            // both in one batch: sixteen loads in flight
+            sum_item(e, a, item);
+            sum_item(e, a, item2);
+        } else {
+            if (ok1) sum_item(e, a, item);
+            if (ok2) sum_item(e, a, item2);
         }
     }
 }
@@ -893,6 +835,7 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
 // Per-tile state shared by the K loop and the role loop.
 struct StepHooks {
     bool interleave; // engine waves run the reduce engine between MFMAs
+    int eng_countdown;  // K steps to the next engine slot
     bool stores;     // the previous tile's epilogue stores are still in flight
     int pend_q;      // slot of the previous tile, whose flag is still to be stored
     int pend_flag;
@@ -986,7 +929,10 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
             }
         }
         if constexpr (!LOADER) {
-            if (hk.interleave && kt % C::ENG_E == 0) engine_step(eng, a);
+            if (hk.interleave && --hk.eng_countdown == 0) {
+                hk.eng_countdown = a.engine_every;
+                engine_step(eng, a, true);
+            }
         }
         const int nxt = kt + C::NS - 1;
         kstep<C, LOADER>(job.lp, rx, rw, lds + (nxt % C::NS) * C::STAGE_BYTES, nxt * C::BK, K,
@@ -1043,7 +989,8 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
                     epoch);
     }
     StepHooks hk;
-    hk.interleave = interleave;
+    hk.interleave = interleave && a.engine_every > 0;
+    hk.eng_countdown = 1;
     hk.stores = false;
     hk.pend_q = -1;
     hk.pend_flag = -1;

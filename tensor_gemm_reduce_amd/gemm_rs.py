@@ -38,9 +38,6 @@ TILE_256x128 = 5
 TILE_256x256 = 6
 TILES = {"auto": 0, "16x64": 1, "64x128": 2, "128x128": 3, "128x256": 4, "256x128": 5, "256x256": 6}
 
-FLAG_WAVE_FENCE = 0
-FLAG_WG_RELEASE = 1
-
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
@@ -52,7 +49,7 @@ class gemm_rs_config(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K_local", ctypes.c_int32),
                 ("tp", ctypes.c_int32), ("rank", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("num_reducers", ctypes.c_int32),
-                ("flag_protocol", ctypes.c_int32), ("debug_flags", ctypes.c_int32),
+                ("engine_interval", ctypes.c_int32), ("debug_flags", ctypes.c_int32),
                 ("drop_flag", ctypes.c_int32), ("flag_stride", ctypes.c_int32),
                 ("watchdog_us", ctypes.c_int64)]
 
@@ -121,11 +118,11 @@ def _check(code: int, what: str) -> int:
 
 
 def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_reducers=-1,
-                flag_protocol=FLAG_WAVE_FENCE, debug_flags=0, drop_flag=-1, flag_stride=1,
+                engine_interval=0, debug_flags=0, drop_flag=-1, flag_stride=1,
                 watchdog_us=0) -> gemm_rs_config:
     if isinstance(tile, str):
         tile = TILES[tile]
-    return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers, flag_protocol,
+    return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers, engine_interval,
                           debug_flags, drop_flag, flag_stride, watchdog_us)
 
 

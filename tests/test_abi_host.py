@@ -68,7 +68,8 @@ def cfg(**kw):
     (dict(rank=-1), gr.ERR_INVALID_ARG),
     (dict(M=-8), gr.ERR_INVALID_ARG),
     (dict(tile=7), gr.ERR_INVALID_ARG),
-    (dict(flag_protocol=5), gr.ERR_INVALID_ARG),
+    (dict(engine_interval=-1), gr.ERR_INVALID_ARG),
+    (dict(engine_interval=4097), gr.ERR_INVALID_ARG),
     (dict(flag_stride=2), gr.ERR_INVALID_ARG),
     (dict(debug_flags=4), gr.ERR_INVALID_ARG),
     (dict(drop_flag=100000), gr.ERR_INVALID_ARG),

@@ -16,9 +16,12 @@ from gpu_util import (Buffers, SENTINEL, assert_close_partial, host, max_rel, or
 
 pytestmark = pytest.mark.gpu
 
-# reducers: 0 = the reduce engine inside the compute waves (default),
-# 8 = dedicated reducer workgroups
-REDUCERS = [0, 8]
+# how the slice is reduced: by the engine waves of the compute workgroups after
+# their last tile (default), by the engine waves between MFMAs (a slot every 1
+# or 3 K steps), or by 8 dedicated reducer workgroups
+REDUCE = {"engine_tail": dict(num_reducers=0), "engine_loop1": dict(num_reducers=0, engine_interval=1),
+          "engine_loop3": dict(num_reducers=0, engine_interval=3), "reducers8": dict(num_reducers=8)}
+REDUCERS = list(REDUCE)
 
 
 def _op(cfg, M=None, **kw):
@@ -41,7 +44,7 @@ def _full_compare(cfg, mode, rank, **kw):
 @pytest.mark.parametrize("rank", range(8))
 def test_tiny_integer_bit_exact_all_ranks(rank, red):
     cfg = synthetic.CONFIGS["tiny"]
-    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", rank, num_reducers=red)
+    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", rank, **REDUCE[red])
     for i in range(7):
         assert np.array_equal(host(b.send[i]), send_o[i]), f"send[{i}]"
     assert np.array_equal(host(b.local), local_o)
@@ -54,7 +57,7 @@ def test_every_tile_config_integer_bit_exact(tile, red):
     # ragged: S = 264 is not a multiple of any BM > 8 and N = 392 of no BN;
     # K_local = 136 leaves a partial last K step
     cfg = synthetic.Config("ragged", 5, 8 * 264, 392, 136)
-    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", 5, tile=tile, num_reducers=red)
+    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", 5, tile=tile, **REDUCE[red])
     for i in range(7):
         assert np.array_equal(host(b.send[i]), send_o[i]), f"send[{i}]"
     assert np.array_equal(host(b.local), local_o)
@@ -95,7 +98,7 @@ def test_reduce_scatter_invariant_consistent_peers():
 def test_full_compare_within_tolerance(name, mode, red):
     cfg = synthetic.CONFIGS[name]
     rank = 5
-    op, b, (x, w, peers), (send_o, local_o, out_o) = _full_compare(cfg, mode, rank, num_reducers=red)
+    op, b, (x, w, peers), (send_o, local_o, out_o) = _full_compare(cfg, mode, rank, **REDUCE[red])
     S = cfg.S
     rows = np.arange(S)
     for i in range(7):
@@ -112,15 +115,15 @@ def test_full_compare_within_tolerance(name, mode, red):
 
 # ------------------------------------------------------------------ full shapes, sampled rows
 
-@pytest.mark.parametrize("red", [-1, 8])
+@pytest.mark.parametrize("red", ["bench", "engine_loop3", "reducers8"])
 @pytest.mark.parametrize("name", ["o_proj", "down_proj", "mixtral_down", "large_prefill"])
 @pytest.mark.parametrize("mode", ["normal", "integer"])
 def test_benchmark_shapes_sampled_rows(name, mode, red):
-    # red=-1: the launch configuration the benchmark times
+    # "bench": the launch configuration the benchmark times
     cfg = synthetic.CONFIGS[name]
     rank = 5
     x, w, peers = synthetic.make_inputs(cfg, mode)
-    op = _op(cfg, rank=rank, num_reducers=red)
+    op = _op(cfg, rank=rank, **({} if red == "bench" else REDUCE[red]))
     b = Buffers(x, w, peers, cfg.S, cfg.N)
     run(op, b)
     rng = np.random.default_rng(1)
@@ -170,6 +173,7 @@ def test_modes_agree_bit_exactly():
     dict(flag_stride=32), dict(num_reducers=1), dict(num_reducers=64), dict(num_reducers=0, group_m=1),
     dict(num_reducers=0, tile="128x128", group_m=3), dict(num_reducers=0, tile="256x256"),
     dict(num_reducers=8, flag_stride=32, tile="128x256"),
+    dict(num_reducers=0, engine_interval=1, flag_stride=32), dict(num_reducers=0, engine_interval=5, tile="16x64"),
 ])
 def test_knobs_keep_results(kw):
     cfg = synthetic.CONFIGS["mixtral_down"]

@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
     ("mixtral_down", 2048, dict(tile="128x128", group_m=3)),
     ("down_proj", None, dict(flag_stride=32)),
     ("down_proj", None, dict(num_reducers=8)),
+    ("mixtral_down", 2048, dict(engine_interval=2)),
 ])
 def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
     cfg = synthetic.CONFIGS[name]
@@ -57,7 +58,8 @@ def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
             assert np.all(s[1:] >= s[:-1]), c
 
 
-@pytest.mark.parametrize("red", [0, 8])
+@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=0, engine_interval=1),
+                                 dict(num_reducers=8)], ids=["engine_tail", "engine_loop1", "reducers8"])
 def test_watchdog_reports_a_dropped_flag_and_kernel_exits(red):
     cfg = synthetic.CONFIGS["tiny"]
     rank = 2
@@ -65,8 +67,7 @@ def test_watchdog_reports_a_dropped_flag_and_kernel_exits(red):
     plan = gr.gemm_rs_plan(gr.make_config(cfg.M, cfg.N, cfg.K_local, rank=rank))
     sched = oracle.schedule(cfg.M, cfg.N, 8, rank, plan.bm, plan.bn, plan.group_m)
     dropped = int(sched["flag"][0])  # first tile of the own slice
-    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, drop_flag=dropped, watchdog_us=2000,
-                   num_reducers=red)
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, drop_flag=dropped, watchdog_us=2000, **red)
     b = Buffers(x, w, peers, cfg.S, cfg.N)
     run(op, b, check_status=False)
     assert op.status() == gr.ERR_TIMEOUT
@@ -100,7 +101,8 @@ def test_alternating_inputs_never_read_stale_tiles():
     bufs = [Buffers(x, w, p, base.S, base.N) for x, w, p in ins]
     shared_send, shared_local, shared_out = bufs[0].send, bufs[0].local, bufs[0].out
     for kw in (dict(num_reducers=0), dict(num_reducers=0, tile="128x128"), dict(num_reducers=8),
-               dict(num_reducers=1)):
+               dict(num_reducers=1), dict(num_reducers=0, engine_interval=1),
+               dict(num_reducers=0, engine_interval=2, tile="128x128")):
         op = gr.GemmRS(base.M, base.N, base.K_local, rank=rank, **kw)
         bad = 0
         for it in range(40):
@@ -115,7 +117,8 @@ def test_alternating_inputs_never_read_stale_tiles():
         assert bad == 0, (kw, bad)
 
 
-@pytest.mark.parametrize("red", [0, 8])
+@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=0, engine_interval=2),
+                                 dict(num_reducers=8)], ids=["engine_tail", "engine_loop2", "reducers8"])
 def test_graph_replays_match_eager(red):
     """Runs captured into a HIP graph and replayed are new runs each time (the
     epoch and counters live on the device): every replay, with eager runs and
@@ -124,7 +127,7 @@ def test_graph_replays_match_eager(red):
     rank = 6
     x, w, peers = synthetic.make_inputs(cfg, "integer")
     want = dev(oracle.gemm_rs(x, w, peers, 8, rank)[2])
-    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, num_reducers=red)
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, **red)
     b = Buffers(x, w, peers, cfg.S, cfg.N)
     fill = np.array(SENTINEL, np.uint16).view(np.int16).item()
     run(op, b)
