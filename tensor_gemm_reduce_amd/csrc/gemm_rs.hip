@@ -51,8 +51,9 @@ GEMM_RS_TILE(Tile256x256, 256, 256, 32, 4, 2, 4, 32)
 struct TileDesc {
     int bm, bn, bk;
     int threads;               // workgroup size
-    int engine_lds_bytes;      // fused kernel with the reduce engine: stages + engine areas
-    int lds_bytes;             // the other kernels: stages
+    int wgs_per_cu;            // workgroups per CU the kernels are built for
+    int engine_lds_bytes;      // fused kernel with in-loop engine slots: stages + engine areas
+    int lds_bytes;             // every other launch: stages
     const void* engine_kernel; // fused: compute waves run the reduce engine
     const void* kernel;        // fused: dedicated reducer workgroups
     const void* gemm_kernel;   // the same GEMM without flags or reduction
@@ -78,8 +79,10 @@ TileDesc desc()
     static_assert(C::LDS_BYTES == CE::LDS_BYTES && CE::EW > 0, "load splits of one shape");
     constexpr int elds = CE::LDS_BYTES + CE::ENG_LDS;
     static_assert(elds <= 160 * 1024 - 64, "LDS of one workgroup");
-    constexpr bool two = elds <= 80 * 1024 - 64;
-    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, elds, C::LDS_BYTES, kernel_for<CE, true, two>(),
+    // occupancy is set by the stages; in-loop engine slots may cost it
+    constexpr bool two = C::LDS_BYTES <= 80 * 1024 - 64;
+    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, elds, C::LDS_BYTES,
+                    kernel_for<CE, true, two>(),
                     kernel_for<C, true, two>(), kernel_for<C, false, two>()};
 }
 
@@ -92,7 +95,7 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr};
+    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr};
     }
 }
 
@@ -139,6 +142,7 @@ struct gemm_rs_handle {
     int device;
     int num_cus;
     int wgs_per_cu;
+    int fused_lds;
     int grid;
     int compute_wgs;
     int reducer_wgs;
@@ -318,12 +322,13 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
         e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     int occ = 0;
-    e = red_req == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.engine_kernel, h->td.threads,
-                                                                    h->td.engine_lds_bytes)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, h->td.kernel, h->td.threads,
-                                                                    h->td.lds_bytes);
+    h->fused_lds = red_req == 0 && c->engine_interval > 0 ? h->td.engine_lds_bytes : h->td.lds_bytes;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, red_req == 0 ? h->td.engine_kernel : h->td.kernel,
+                                                     h->td.threads, h->fused_lds);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
-    h->wgs_per_cu = occ < 1 ? 1 : occ;
+    // the persistent grid holds the workgroups per CU the kernel was built for
+    // (more would share a SIMD's registers between more waves than planned)
+    h->wgs_per_cu = occ < 1 ? 1 : (occ > h->td.wgs_per_cu ? h->td.wgs_per_cu : occ);
     // a whole number of workgroups per XCD group
     h->grid = (h->num_cus * h->wgs_per_cu) / kGroups * kGroups;
     if (h->grid < kGroups) h->grid = kGroups;
@@ -401,7 +406,7 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     void* params[] = {&a};
     const bool engine = fused && h->reducer_wgs == 0;
     HIP_TRY(hipLaunchKernel(engine ? h->td.engine_kernel : (fused ? h->td.kernel : h->td.gemm_kernel), dim3(h->grid),
-                            dim3(h->td.threads), params, engine ? h->td.engine_lds_bytes : h->td.lds_bytes, s));
+                            dim3(h->td.threads), params, fused ? h->fused_lds : h->td.lds_bytes, s));
     return GEMM_RS_OK;
 }
 
@@ -498,7 +503,7 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->reducer_wgs = h->reducer_wgs;
     info->num_cus = h->num_cus;
     info->wgs_per_cu = h->wgs_per_cu;
-    info->lds_bytes = h->reducer_wgs == 0 ? h->td.engine_lds_bytes : h->td.lds_bytes;
+    info->lds_bytes = h->fused_lds;
     info->reduce_grid = h->reduce_grid;
     info->xcd_split = h->strided;
     DeviceState ds;

@@ -82,10 +82,11 @@ constexpr int kEngAreas = 2;
 // Handle-owned device state, zeroed at creation.
 struct DeviceState {
     uint32_t epoch;           // epoch of the last completed fused run
-    uint32_t role[kGroups];   // per-group arrival tickets
+    uint32_t role[kGroups];   // per-group arrival tickets (dedicated reducers only)
     uint32_t unit;            // next reducer unit to claim
-    uint32_t done;            // workgroups that finished this launch
+    uint32_t done;            // groups whose workgroups have all finished this launch
     int32_t status[2];        // [0] error code, [1] flag index that timed out
+    uint32_t done_grp[kGroups];  // finished workgroups per group
     uint32_t pad[3];
 };
 
@@ -577,14 +578,58 @@ struct EngOp {
     uint32_t vm_end;  // the wave's vector-memory count right after the operation's issue
 };
 
+// Where an item lies: item i is chunk row (i % IPT) * RPI .. of own tile
+// i / IPT, tile t = tile row * tile columns + tile column.
+struct ItemMap {
+    int nitems;         // items of the slice
+    int ipt_log2;       // log2(items per tile)
+    int rpi;            // tile rows per item
+    int lane_row, lane_col, lane_off;  // this lane's place inside an item
+    uint32_t div_m;     // t / tile_cols = (umulhi(t, div_m) + t) >> div_l
+    int div_l;
+};
+
+__device__ __forceinline__ ItemMap item_map(const Args& a)
+{
+    ItemMap m;
+    const int lane = threadIdx.x & 63;
+    const int cpr = a.g.bn >> 3;  // 16-byte chunks per tile row (8 .. 32)
+    m.rpi = 64 / cpr;
+    m.ipt_log2 = __builtin_ctz(a.g.bm / m.rpi);
+    m.nitems = a.g.ts << m.ipt_log2;
+    m.lane_row = lane / cpr;
+    m.lane_col = (lane % cpr) * 8;
+    m.lane_off = m.lane_row * a.g.N + m.lane_col;
+    // multiply-shift division by the tile-column count d (exact for t < 2^31):
+    // l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1
+    const uint32_t d = (uint32_t)(a.g.tnc > 0 ? a.g.tnc : 1);
+    m.div_l = d == 1 ? 0 : 32 - __builtin_clz(d - 1);
+    m.div_m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << m.div_l) - d)) / d + 1);
+    return m;
+}
+
+// Byte offset of this lane's chunk of an item in the slice; kOob if the chunk
+// lies outside the possibly ragged tile or the item past the last one.
+__device__ __forceinline__ uint32_t item_boff(const ItemMap& m, const Args& a, int item)
+{
+    const uint32_t t = (uint32_t)(item >> m.ipt_log2);
+    const int j = item & ((1 << m.ipt_log2) - 1);
+    const int tml = (int)((__umulhi(t, m.div_m) + t) >> m.div_l);
+    const int tn = (int)t - tml * a.g.tnc;
+    const int row = j * m.rpi;
+    const int trows = min(a.g.bm, a.g.S - tml * a.g.bm);
+    const int tcols = min(a.g.bn, a.g.N - tn * a.g.bn);
+    const bool valid = item < m.nitems && row + m.lane_row < trows && m.lane_col < tcols;
+    const uint32_t base = (uint32_t)(tml * a.g.bm + row) * (uint32_t)a.g.N + (uint32_t)(tn * a.g.bn);
+    return valid ? (base + (uint32_t)m.lane_off) * 2u : kOob;
+}
+
 struct Engine {
     char* areas;    // kEngAreas LDS areas of kEngAreaBytes
+    ItemMap m;
     int next;       // next owned item not yet started
     int stride;     // engine waves W
-    int nitems;     // items of the slice
-    int ipt, ipt_log2;  // items per tile (a power of two)
-    int rpi;        // tile rows per item
-    int lane_row, lane_col, lane_off;  // this lane's place inside an item
+    int nitems, ipt, ipt_log2;  // copies of m's (items per tile: a power of two)
     // issue side
     int i_item;     // item being issued, -1 if none
     int i_step;     // its next step
@@ -604,36 +649,22 @@ struct Engine {
 
 // Element offset of this lane's chunk of an item in the slice (0 if the chunk
 // lies outside the possibly ragged tile) and its byte offset for a store
-// (kOob then).  Wave-uniform except for the lane's own place.
+// (kOob then).
 __device__ __forceinline__ void item_offsets(const Engine& e, const Args& a, int item, uint32_t& off,
                                              uint32_t& soff)
 {
-    const int t = item >> e.ipt_log2;
-    const int j = item & (e.ipt - 1);
-    const int tml = t / a.g.tnc;
-    const int tn = t - tml * a.g.tnc;
-    const int row = j * e.rpi;
-    const int trows = min(a.g.bm, a.g.S - tml * a.g.bm);
-    const int tcols = min(a.g.bn, a.g.N - tn * a.g.bn);
-    const bool valid = row + e.lane_row < trows && e.lane_col < tcols;
-    const uint32_t base = (uint32_t)(tml * a.g.bm + row) * (uint32_t)a.g.N + (uint32_t)(tn * a.g.bn);
-    off = valid ? base + (uint32_t)e.lane_off : 0u;
-    soff = valid ? (base + (uint32_t)e.lane_off) * 2u : kOob;
+    soff = item_boff(e.m, a, item);
+    off = soff == kOob ? 0u : soff >> 1;
 }
 
 __device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* areas, int gw, int waves,
                                             uint32_t epoch)
 {
-    const int lane = threadIdx.x & 63;
-    const int cpr = a.g.bn >> 3;  // 16-byte chunks per tile row (8 .. 32)
     e.areas = areas;
-    e.rpi = 64 / cpr;
-    e.ipt = a.g.bm / e.rpi;
-    e.ipt_log2 = __builtin_ctz(e.ipt);
-    e.nitems = a.g.ts * e.ipt;
-    e.lane_row = lane / cpr;
-    e.lane_col = (lane % cpr) * 8;
-    e.lane_off = e.lane_row * a.g.N + e.lane_col;
+    e.m = item_map(a);
+    e.ipt_log2 = e.m.ipt_log2;
+    e.ipt = 1 << e.ipt_log2;
+    e.nitems = e.m.nitems;
     e.next = uni(gw);
     e.stride = waves;
     e.i_item = -1;
@@ -787,47 +818,57 @@ __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, 
     return true;
 }
 
-// The whole sum of one item with plain loads (drain): 7 peer chunks and the
-// local chunk, in the sum order.
-__device__ __forceinline__ void sum_item(const Engine& e, const Args& a, int item)
+// Sums items first, first + stride, ... with plain loads (no LDS), BATCH items
+// at a time: a batch's peer chunks are loaded before its tiles' flags are
+// checked (they need none), then its local chunks, in the sum order.  A tile
+// whose flag does not arrive within the watchdog limit is reported and its
+// items are skipped.
+template <int BATCH>
+__device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int first, int stride, uint32_t epoch)
 {
-    uint32_t off, soff;
-    item_offsets(e, a, item, off, soff);
-    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(a.dst[a.g.rank], 0, a.slice_bytes, kRsrcFlags);
-    u32x4 v[kPeers + 1];
-#pragma unroll
-    for (int s = 0; s < kPeers; ++s)
-        v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.peers[s] + off));
-    v[kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off * 2u, 0, kAuxSc1));
-    f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[s]);
+    constexpr int kDrainBatch = BATCH;
+    bool gave_up = false;
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.dst[a.g.rank], 0, a.slice_bytes, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
-    __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, soff, 0, kAuxNt);
+    for (int base = first; base < m.nitems; base += kDrainBatch * stride) {
+        uint32_t boff[kDrainBatch];
+        u32x4 v[kDrainBatch][kPeers + 1];
+#pragma unroll
+        for (int b = 0; b < kDrainBatch; ++b) {
+            boff[b] = item_boff(m, a, base + b * stride);
+#pragma unroll
+            for (int s = 0; s < kPeers; ++s) {
+                const __amdgpu_buffer_rsrc_t rp =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)a.peers[s], 0, a.slice_bytes, kRsrcFlags);
+                v[b][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, boff[b], 0, kAuxNt));
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kDrainBatch; ++b) {
+            const int item = base + b * stride;
+            const bool ok = item < m.nitems && wait_tile(a, epoch, item >> m.ipt_log2, gave_up);
+            boff[b] = ok ? boff[b] : kOob;
+            v[b][kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, boff[b], 0, kAuxSc1));
+        }
+#pragma unroll
+        for (int b = 0; b < kDrainBatch; ++b) {
+            f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[b][s]);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, boff[b], 0, kAuxNt);
+        }
+    }
 }
 
-// After the last tile: settle the operations in flight and the item being
-// summed (its tile is flagged), then sum the wave's remaining items two at a
-// time with plain loads, each once its tile is flagged.  A tile whose flag does
-// not arrive within the watchdog limit is reported and its items are skipped.
+// After the last tile of an engine wave that ran in-loop slots: settle the
+// operations in flight and the item being summed (its tile is flagged), then
+// drain the wave's remaining items.
 __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
 {
     while (e.o0.op != kOpNone || e.o1.op != kOpNone || e.i_item >= 0) engine_step(e, a, false);
     wait_vmcnt<0>();
-    bool gave_up = false;
-    for (int item = e.next; item < e.nitems; item += 2 * e.stride) {
-        const int item2 = item + e.stride;
-        const bool ok1 = wait_tile(a, e.epoch, item >> e.ipt_log2, gave_up);
-        const bool ok2 = item2 < e.nitems && wait_tile(a, e.epoch, item2 >> e.ipt_log2, gave_up);
-        if (ok1 && ok2) {
-            // both in one batch: sixteen loads in flight
-            sum_item(e, a, item);
-            sum_item(e, a, item2);
-        } else {
-            if (ok1) sum_item(e, a, item);
-            if (ok2) sum_item(e, a, item2);
-        }
-    }
+    drain_items<2>(a, e.m, e.next, e.stride, e.epoch);
 }
 
 // ---------------------------------------------------------------- tile loop
@@ -1037,8 +1078,17 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         stage_barrier();
         if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
-    if constexpr (!LOADER) {
-        if (interleave) engine_drain(eng, a);
+    if (interleave) {
+        if (hk.interleave) {
+            // in-loop slots: the engine waves own the items
+            if constexpr (!LOADER) engine_drain(eng, a);
+        } else {
+            // every wave sums a share of the slice after its last tile
+            const int wave = uni((int)(threadIdx.x >> 6));
+            // (sixteen items in flight per CU)
+            drain_items<16 / C::WAVES / (C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64 ? 2 : 1)>(
+                a, item_map(a), pos * C::WAVES + wave, a.num_compute * C::WAVES, epoch);
+        }
     }
 }
 
@@ -1119,16 +1169,24 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
     }
 }
 
-// Role dispatch and end-of-launch bookkeeping.
+// Role dispatch and end-of-launch bookkeeping.  Without dedicated reducers
+// every workgroup computes and its position follows from its index: no device
+// atomics at the start.  With reducers, per-group arrival tickets hand out the
+// roles (a reducer exists only once its group's compute workgroups are all
+// resident).  A fused launch counts finished workgroups per group and then
+// finished groups (device atomics spread over nine addresses instead of one);
+// the last workgroup resets the counters and publishes the new epoch.  A
+// GEMM-only launch has no flags and needs none of this.
 template <class C, bool FUSED>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ uint32_t s_ticket, s_epoch;
     const int grp = blockIdx.x % kGroups;
+    const bool tickets = FUSED && a.num_reducers > 0;
     if (threadIdx.x == 0) {
-        s_ticket = atomicAdd(&a.state->role[grp], 1u);
-        s_epoch = __hip_atomic_load(&a.state->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_ticket = tickets ? atomicAdd(&a.state->role[grp], 1u) : (uint32_t)(blockIdx.x / kGroups);
+        s_epoch = FUSED ? __hip_atomic_load(&a.state->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     }
     __syncthreads();
     const uint32_t ticket = s_ticket;
@@ -1139,15 +1197,19 @@ __device__ __forceinline__ void fused_body(const Args& a)
     else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers)
         reducer_role(a, epoch);
 
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t finished = atomicAdd(&a.state->done, 1u);
-        if (finished == gridDim.x - 1) {
+    if constexpr (FUSED) {
+        __syncthreads();
+        if (threadIdx.x == 0 &&
+            atomicAdd(&a.state->done_grp[grp], 1u) == gridDim.x / kGroups - 1 &&
+            atomicAdd(&a.state->done, 1u) == kGroups - 1) {
             // every other workgroup has finished: reset for the next launch
-            for (int i = 0; i < kGroups; ++i) __hip_atomic_store(&a.state->role[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kGroups; ++i) {
+                __hip_atomic_store(&a.state->role[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.state->done_grp[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             __hip_atomic_store(&a.state->unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.state->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (FUSED) __hip_atomic_store(&a.state->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.state->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
