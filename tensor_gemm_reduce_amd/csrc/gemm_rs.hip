@@ -152,6 +152,7 @@ struct gemm_rs_handle {
     uint32_t* flags;
     DeviceState* state;
     uint32_t* trace;
+    uint32_t* finished;
     uint16_t* scratch;
     hipStream_t last_stream;
 };
@@ -285,6 +286,7 @@ static void free_state(gemm_rs_handle* h)
     if (h->flags) (void)hipFree(h->flags);
     if (h->state) (void)hipFree(h->state);
     if (h->trace) (void)hipFree(h->trace);
+    if (h->finished) (void)hipFree(h->finished);
     if (h->scratch) (void)hipFree(h->scratch);
 }
 
@@ -347,6 +349,7 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     if (hipMalloc(&h->flags, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->state, sizeof(DeviceState)) != hipSuccess ||
         hipMalloc(&h->trace, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->finished, (size_t)h->grid * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->scratch, (slice > 0 ? slice : 8) * sizeof(uint16_t)) != hipSuccess) {
         free_state(h);
         delete h;
@@ -355,6 +358,7 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     if (hipMemset(h->flags, 0, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
         hipMemset(h->state, 0, sizeof(DeviceState)) != hipSuccess ||
         hipMemset(h->trace, 0, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->finished, 0, (size_t)h->grid * sizeof(uint32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_state(h);
         delete h;
@@ -383,6 +387,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.flags = h->flags;
     a.state = h->state;
     a.trace = h->trace;
+    a.finished = h->finished;
     a.g = h->g;
     a.x_bytes = (uint32_t)((int64_t)h->g.M * h->g.K * 2);
     a.w_bytes = (uint32_t)((int64_t)h->g.N * h->g.K * 2);
@@ -506,10 +511,9 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->lds_bytes = h->fused_lds;
     info->reduce_grid = h->reduce_grid;
     info->xcd_split = h->strided;
-    DeviceState ds;
+    // every workgroup's finish mark holds the epoch of the last fused launch
     HIP_TRY(hipStreamSynchronize(h->last_stream));
-    HIP_TRY(hipMemcpy(&ds, h->state, sizeof ds, hipMemcpyDeviceToHost));
-    info->epoch = ds.epoch;
+    HIP_TRY(hipMemcpy(&info->epoch, h->finished, sizeof info->epoch, hipMemcpyDeviceToHost));
     return GEMM_RS_OK;
 }
 

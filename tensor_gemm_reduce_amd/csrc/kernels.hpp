@@ -30,9 +30,8 @@
 // one XCD work on tiles that share rows of X or columns of W in that XCD's L2.
 //
 // The run epoch, the tickets and the reducer work counter live in device
-// memory; the last workgroup to finish resets the counters and publishes the
-// new epoch, so a launch needs no host-side state and can be replayed from a
-// captured graph.
+// memory (see fused_body), so a launch needs no host-side state and can be
+// replayed from a captured graph.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -81,12 +80,11 @@ constexpr int kEngAreas = 2;
 
 // Handle-owned device state, zeroed at creation.
 struct DeviceState {
-    uint32_t epoch;           // epoch of the last completed fused run
+    uint32_t pad1;
     uint32_t role[kGroups];   // per-group arrival tickets (dedicated reducers only)
     uint32_t unit;            // next reducer unit to claim
-    uint32_t done;            // groups whose workgroups have all finished this launch
+    uint32_t pad0;
     int32_t status[2];        // [0] error code, [1] flag index that timed out
-    uint32_t done_grp[kGroups];  // finished workgroups per group
     uint32_t pad[3];
 };
 
@@ -99,6 +97,7 @@ struct Args {
     uint32_t* flags;         // ready flags, flag_stride words apart
     DeviceState* state;
     uint32_t* trace;         // 4 words per slot (debug)
+    uint32_t* finished;      // per workgroup: epoch of the last fused launch it finished
     Geometry g;
     uint32_t x_bytes, w_bytes;
     uint32_t slice_bytes;    // S * N * 2
@@ -1169,14 +1168,19 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
     }
 }
 
-// Role dispatch and end-of-launch bookkeeping.  Without dedicated reducers
-// every workgroup computes and its position follows from its index: no device
-// atomics at the start.  With reducers, per-group arrival tickets hand out the
-// roles (a reducer exists only once its group's compute workgroups are all
-// resident).  A fused launch counts finished workgroups per group and then
-// finished groups (device atomics spread over nine addresses instead of one);
-// the last workgroup resets the counters and publishes the new epoch.  A
-// GEMM-only launch has no flags and needs none of this.
+// Role dispatch and end-of-launch bookkeeping, with no device atomics on the
+// default path.  Without dedicated reducers every workgroup computes and its
+// position follows from its index.  With reducers, per-group arrival tickets
+// hand out the roles (a reducer exists only once its group's compute
+// workgroups are all resident), and workgroup 0 resets the tickets once every
+// workgroup has finished.
+//
+// The run epoch: each workgroup keeps, in its own word of `finished`, the
+// epoch of the last fused launch it finished.  A launch reads that word at
+// the start and uses the next value; every workgroup of the previous fused
+// launch stored the same value, so all workgroups of a launch agree on its
+// epoch without communicating (the words change only at kernel ends).  A
+// GEMM-only launch has no flags and touches none of this.
 template <class C, bool FUSED>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
@@ -1186,7 +1190,8 @@ __device__ __forceinline__ void fused_body(const Args& a)
     const bool tickets = FUSED && a.num_reducers > 0;
     if (threadIdx.x == 0) {
         s_ticket = tickets ? atomicAdd(&a.state->role[grp], 1u) : (uint32_t)(blockIdx.x / kGroups);
-        s_epoch = FUSED ? __hip_atomic_load(&a.state->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        s_epoch = FUSED ? __hip_atomic_load(a.finished + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : 0u;
     }
     __syncthreads();
     const uint32_t ticket = s_ticket;
@@ -1199,17 +1204,22 @@ __device__ __forceinline__ void fused_body(const Args& a)
 
     if constexpr (FUSED) {
         __syncthreads();
-        if (threadIdx.x == 0 &&
-            atomicAdd(&a.state->done_grp[grp], 1u) == gridDim.x / kGroups - 1 &&
-            atomicAdd(&a.state->done, 1u) == kGroups - 1) {
-            // every other workgroup has finished: reset for the next launch
-            for (int i = 0; i < kGroups; ++i) {
-                __hip_atomic_store(&a.state->role[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.state->done_grp[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.finished + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tickets && blockIdx.x == 0) {
+            // every finish mark arrives (each workgroup's own waits are
+            // bounded by the watchdog; this one is bounded too)
+            const uint64_t t0 = wall_clock64();
+            for (int i = threadIdx.x; i < (int)gridDim.x; i += blockDim.x)
+                while (__hip_atomic_load(a.finished + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch &&
+                       (int64_t)(wall_clock64() - t0) <= 2 * a.watchdog_ticks)
+                    __builtin_amdgcn_s_sleep(2);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                for (int i = 0; i < kGroups; ++i)
+                    __hip_atomic_store(&a.state->role[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.state->unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            __hip_atomic_store(&a.state->unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.state->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.state->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
