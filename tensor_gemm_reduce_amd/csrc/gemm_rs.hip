@@ -325,8 +325,9 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     int occ = 0;
     h->fused_lds = red_req == 0 && c->engine_interval > 0 ? h->td.engine_lds_bytes : h->td.lds_bytes;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, red_req == 0 ? h->td.engine_kernel : h->td.kernel,
-                                                     h->td.threads, h->fused_lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &occ, red_req == 0 && c->engine_interval > 0 ? h->td.engine_kernel : h->td.kernel, h->td.threads,
+        h->fused_lds);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
     // the persistent grid holds the workgroups per CU the kernel was built for
     // (more would share a SIMD's registers between more waves than planned)
@@ -409,7 +410,9 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // GEMM_ONLY has no reducers, so its groups always split evenly
     if (!fused) a.strided = h->strided;
     void* params[] = {&a};
-    const bool engine = fused && h->reducer_wgs == 0;
+    // in-loop engine slots need the kernel whose waves are split into stage
+    // loaders and engine waves; otherwise every wave loads stages
+    const bool engine = fused && h->reducer_wgs == 0 && h->cfg.engine_interval > 0;
     HIP_TRY(hipLaunchKernel(engine ? h->td.engine_kernel : (fused ? h->td.kernel : h->td.gemm_kernel), dim3(h->grid),
                             dim3(h->td.threads), params, fused ? h->fused_lds : h->td.lds_bytes, s));
     return GEMM_RS_OK;

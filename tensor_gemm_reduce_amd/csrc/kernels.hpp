@@ -1029,7 +1029,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
                     epoch);
     }
     StepHooks hk;
-    hk.interleave = interleave && a.engine_every > 0;
+    hk.interleave = interleave && C::EW > 0 && a.engine_every > 0;
     hk.eng_countdown = 1;
     hk.stores = false;
     hk.pend_q = -1;
@@ -1099,7 +1099,8 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
 {
     const int pos = a.strided ? (l * kGroups + grp) : (base + l);
     const uint32_t who = ((uint32_t)grp << 16) | (uint32_t)l;
-    const bool interleave = FUSED && C::EW > 0 && a.num_reducers == 0;
+    // without dedicated reducers the compute workgroups reduce the slice
+    const bool interleave = FUSED && a.num_reducers == 0;
     const int wave = uni((int)(threadIdx.x >> 6));
     if (wave < C::LW)
         compute_waves<C, FUSED, true>(a, lds, pos, who, epoch, interleave);
