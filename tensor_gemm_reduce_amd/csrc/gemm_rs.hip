@@ -45,7 +45,7 @@ GEMM_RS_TILE(Tile64x128, 64, 128, 64, 2, 2, 2, 32)
 GEMM_RS_TILE(Tile128x128, 128, 128, 32, 3, 2, 2, 32)
 GEMM_RS_TILE(Tile128x256, 128, 256, 32, 4, 2, 2, 32)
 GEMM_RS_TILE(Tile256x128, 256, 128, 32, 4, 2, 2, 32)
-GEMM_RS_TILE(Tile256x256, 256, 256, 32, 4, 2, 4, 32)
+GEMM_RS_TILE(Tile256x256, 256, 256, 64, 2, 2, 4, 32)
 #undef GEMM_RS_TILE
 
 struct TileDesc {
