@@ -57,6 +57,14 @@ def parse():
     p.add_argument("--engine-interval", type=int, default=0,
                    help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
     p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="run only a plain copy of known size and a few fused launches of --workload "
+                        "(the program a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass runs)")
+    p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                   help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn the counter_collection.csv of the two --traffic-probe passes into "
+                        "profiles/traffic_<workload>.json and exit (no GPU needed)")
     return p.parse_args()
 
 
@@ -298,8 +306,80 @@ def load_traffic(workload):
     return t
 
 
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
+TRAFFIC_LAUNCHES = 4
+
+
+def traffic_probe(args):
+    """A device-to-device copy of COPY_BYTES (the calibration kernel), then
+    TRAFFIC_LAUNCHES fused launches of the workload, each synchronized."""
+    import torch
+
+    from tensor_gemm_reduce_amd import gemm_rs as gr
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c = Case(args.workload, args)
+    for _ in range(TRAFFIC_LAUNCHES):
+        c.run(gr.MODE_FUSED)
+        torch.cuda.synchronize()
+    log(f"traffic probe done: copy {COPY_BYTES} B, {TRAFFIC_LAUNCHES} fused launches of {args.workload}")
+
+
+def traffic_from(args):
+    """HBM bytes per fused launch from the FETCH_SIZE and WRITE_SIZE passes,
+    each scaled by what the same counter reads for the copy of known size."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "fused_kernel" not in r["Kernel_Name"]]
+        fused = [float(r["Counter_Value"]) for r in rows if "fused_kernel" in r["Kernel_Name"]]
+        if not copy or not fused:
+            raise SystemExit(f"{path}: no {counter} rows for the copy and the fused kernel")
+        # the copy is the largest other dispatch; later launches of the fused
+        # kernel see warm caches, as in the timed runs
+        return max(copy), statistics.median(fused[1:] if len(fused) > 1 else fused)
+
+    copy_f, fused_f = per_kernel(args.traffic_from[0], "FETCH_SIZE")
+    copy_w, fused_w = per_kernel(args.traffic_from[1], "WRITE_SIZE")
+    # counters are in KiB; the copy reads and writes COPY_BYTES each
+    k_fetch = copy_f * 1024.0 / COPY_BYTES
+    k_write = copy_w * 1024.0 / COPY_BYTES
+    t = {"workload": args.workload, "source_digest": source_digest(),
+         "fetch_bytes": fused_f * 1024.0 / k_fetch, "write_bytes": fused_w * 1024.0 / k_write,
+         "fetch_kib_raw": fused_f, "write_kib_raw": fused_w,
+         "copy_fetch_factor": k_fetch, "copy_write_factor": k_write, "copy_bytes": COPY_BYTES}
+    out = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(out, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(t))
+
+
+def stats_summary(path):
+    """Markdown table of rocprofv3's per-kernel statistics (durations in us)."""
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    print("| kernel | calls | average us | min us | max us |")
+    print("|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+        print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} |")
+
+
 def main():
     args = parse()
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of a TP=8 layer on a single GPU; --gpus {args.gpus} "
               "is not supported (no multi-GPU path in this build).", file=sys.stderr)
@@ -315,6 +395,9 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
+    if args.traffic_probe:
+        traffic_probe(args)
+        return
     c = Case(args.workload, args)
     cfg = c.cfg
     check = check_case(c) if args.check else None
@@ -327,6 +410,11 @@ def main():
     for _ in range(max(1, -(-args.warmup // args.steps))):
         steps.replay()
     torch.cuda.synchronize()
+    # and at least 0.3 s of the same work, so that clocks have settled
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.3:
+        steps.replay()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

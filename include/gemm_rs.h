@@ -18,8 +18,11 @@
  *   compute workgroups  walk the tile schedule, run the MFMA main loop, round
  *                       each finished tile to BF16, store it into the buffer of
  *                       its destination slice and release its ready flag;
- *   reducer workgroups  wait for the flags of this rank's own slice and sum each
- *                       tile with the tp-1 peer partials into `out`.
+ *   reducers            wait for the flags of this rank's own slice and sum each
+ *                       tile with the tp-1 peer partials into `out`: by default
+ *                       the compute workgroups themselves after their last
+ *                       tile, optionally between MFMAs (engine_interval) or in
+ *                       dedicated workgroups (num_reducers).
  *
  * On one GPU the tp-1 peer partials are buffers already resident in HBM that
  * stand in for the other ranks' remote writes, and the tp-1 send buffers stand
@@ -38,7 +41,7 @@
  *                              is X_r * W_r with W_r = w^T)
  *   send[i], peers[i], out, local_slice: [S][N] with S = M / tp
  * Every pointer must be 16-byte aligned; K_local and N must be multiples of 8;
- * M * K_local and N * K_local must stay below 2^30 elements.
+ * M * K_local, N * K_local and S * N must stay below 2^30 elements.
  *
  * Errors: every function returns GEMM_RS_OK (0) or a negative GEMM_RS_ERR_*
  * code; nothing aborts and nothing throws across the ABI.  gemm_rs_strerror
@@ -49,7 +52,9 @@
  * the handle's device counters): issue them on one stream, or synchronise
  * between streams.  The run epoch and all counters live in device memory and
  * are advanced by the kernel itself, so runs may be captured into a HIP graph
- * and replayed; each replay is a new run.
+ * and replayed; each replay is a new run.  A fused run needs its whole grid
+ * resident at once (the grid is sized to the device: CUs x workgroups per CU),
+ * as a persistent kernel whose workgroups wait for each other's flags.
  */
 #ifndef GEMM_RS_H
 #define GEMM_RS_H
@@ -151,8 +156,9 @@ int gemm_rs_plan_slots(const gemm_rs_config *cfg, int32_t *slot_d, int32_t *slot
 
 /* Creates a handle on the current HIP device: validates cfg, checks that the
  * device is gfx950, and allocates the handle-owned device state (ready flags
- * zeroed, arrival ticket, status word, trace log, and a [S][N] BF16 scratch
- * used as the local slice when gemm_rs_run gets local_slice == NULL).
+ * and per-workgroup finish marks zeroed, arrival tickets, status word, trace
+ * log, and a [S][N] BF16 scratch used as the local slice when gemm_rs_run gets
+ * local_slice == NULL).
  * On success *out receives the handle; on failure *out is set to NULL. */
 int gemm_rs_create(const gemm_rs_config *cfg, gemm_rs_handle **out);
 
