@@ -343,8 +343,10 @@ __device__ __forceinline__ void mfma_substep(TileState<C>& st, const bf16x8 (&xf
 // One K step: a loader wave refills the buffer of stage kt-1 with stage
 // kt+NS-1; then the MFMAs of stage kt with the fragments of substep s+1 read
 // while substep s computes.  The scheduling groups place the substep-0 reads
-// first and then one LDS read or one direct load after each MFMA, so neither
-// waits on a full LDS round trip in the middle of the MFMA stream.
+// first, then every direct load of the refill (the earlier they are issued,
+// the longer they have to land before the next step waits for them:
+// measured 4% on the large shape), then one LDS read after each MFMA, so no
+// MFMA waits on a full LDS round trip.
 template <class C, bool LOADER>
 __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                                       char* refill, int k_refill, int K, const char* cur, TileState<C>& st)
@@ -360,10 +362,12 @@ __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsr
     constexpr int kMfmas = C::KSUB * C::FM * C::FN;
     constexpr int kFill = (C::KSUB - 1) * (C::FM + C::FN) + (LOADER ? C::LPS : 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FM + C::FN, 0);
+    if constexpr (LOADER) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, C::LPS, 0);
+    constexpr int kFillDs = (C::KSUB - 1) * (C::FM + C::FN);
 #pragma unroll
     for (int m = 0; m < kMfmas; ++m) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (m < kFill) __builtin_amdgcn_sched_group_barrier(kSchedDsRead | kSchedVmemRead, 1, 0);
+        if (m < kFillDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
 }
 
