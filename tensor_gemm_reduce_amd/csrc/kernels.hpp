@@ -157,6 +157,9 @@ struct TileCfg {
     static_assert(!STAGED_EPI || WAVES * EPI_AREA <= STAGE_BYTES, "epilogue staging fits one stage buffer");
     static_assert((NS - 2) * LPS + STORES <= 63, "vmcnt range");
     static constexpr int ENG_LDS = EW * kEngAreas * kEngAreaBytes;
+    // One wave per SIMD (four waves whose stages fit only once per CU) with
+    // every wave loading: the K loop is pipelined across steps.
+    static constexpr bool XP = WAVES == 4 && EW == 0 && LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
 };
 
 template <int MF> struct AccT;
@@ -278,7 +281,8 @@ template <class C>
 __device__ __forceinline__ void issue_stage(const LoadPlan<C>& lp, __amdgpu_buffer_rsrc_t rx,
                                             __amdgpu_buffer_rsrc_t rw, char* stage, int k0, int K)
 {
-    const int wave = threadIdx.x >> 6;
+    // (uniform: the LDS destination, and with it M0, is scalar arithmetic)
+    const int wave = uni((int)(threadIdx.x >> 6));
     const int lim = K - k0;  // chunks with k offset >= lim are past K
 #pragma unroll
     for (int i = 0; i < C::A_LD; ++i) {
@@ -305,7 +309,7 @@ template <class C>
 __device__ __forceinline__ void load_frags(const char* stage, int s, bf16x8 (&xf)[C::FM], bf16x8 (&wf)[C::FN])
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = uni((int)(threadIdx.x >> 6));
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const char* sa = stage;
     const char* sb = stage + C::A_BYTES;
@@ -387,7 +391,7 @@ __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st
                                            __amdgpu_buffer_rsrc_t rd, int row0, int rows, int n0, int cols)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = uni((int)(threadIdx.x >> 6));
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const uint32_t N = (uint32_t)a.g.N;
     if constexpr (C::STAGED_EPI) {
@@ -997,6 +1001,111 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
     }
 }
 
+// Wait until this wave's LDS reads (and other LGKM operations) have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
+// Publishes the previous tile's flag once a barrier has certified its stores.
+__device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
+{
+    hk.stores = false;
+    if (hk.pend_flag >= 0) {
+        if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
+        hk.pend_flag = -1;
+    }
+}
+
+// The K loop of a tile for kernels with one wave per SIMD (every wave loads),
+// pipelined across K steps.  No sibling wave covers the LDS round trip of a
+// step's first fragments there, so substep 0 of step kt+1 is read while the
+// last substep of step kt computes.  The step's wait and barrier therefore sit
+// before its last substep: they certify that every wave's loads of stage kt+1
+// have landed and that every wave has read all of stage kt (each wave waits for
+// its LDS reads first), whose buffer is refilled right after the barrier with
+// stage kt+NS.  The vector-memory wait counts follow tile_kloop: NS-2 younger
+// stages, plus the previous tile's stores while they are younger than the
+// stage waited for (stages of the prologue).  The first barrier that covers
+// those stores (the one waiting for stage NS-1, the first refill) publishes
+// the previous tile's flag.
+template <class C>
+__device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
+                                              StepHooks& hk)
+{
+    static_assert(C::KSUB % 2 == 0, "substep s of every step uses fragment buffer s % 2");
+    static_assert(C::EW == 0, "every wave loads stages");
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < AccT<C::MF>::N; ++e) st.acc[i][j][e] = 0.0f;
+
+    const int K = a.g.K;
+    const int nk = job.nk;
+    constexpr int B = (C::NS - 2) * C::LPS;
+    constexpr int kMf = C::FM * C::FN;   // MFMAs per substep
+    constexpr int kDs = C::FM + C::FN;   // fragment reads per substep
+    if (nk > 0) {
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
+        bf16x8 xf[2][C::FM], wf[2][C::FN];
+        // stage 0 came from the prologue, before the previous tile's stores
+        if (hk.stores)
+            wait_vmcnt<B + C::STORES>();
+        else
+            wait_vmcnt<B>();
+        stage_barrier();
+        issue_stage<C>(job.lp, rx, rw, lds + (C::NS - 1) * C::STAGE_BYTES, (C::NS - 1) * C::BK, K);
+        load_frags<C>(lds, 0, xf[0], wf[0]);
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            const char* cur = lds + (kt % C::NS) * C::STAGE_BYTES;
+#pragma unroll
+            for (int s = 0; s + 1 < C::KSUB; ++s) {
+                load_frags<C>(cur, s + 1, xf[(s + 1) & 1], wf[(s + 1) & 1]);
+                mfma_substep<C>(st, xf[s & 1], wf[s & 1]);
+            }
+#pragma unroll
+            for (int s = 0; s + 1 < C::KSUB; ++s)
+#pragma unroll
+                for (int m = 0; m < kMf; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+            if (hk.stores && kt + 1 < C::NS - 1)
+                wait_vmcnt<B + C::STORES>();
+            else
+                wait_vmcnt<B>();
+            wait_lgkm0();
+            stage_barrier();
+            if (kt + 1 == C::NS - 1) publish_pending(a, hk);
+            issue_stage<C>(job.lp, rx, rw, lds + (kt % C::NS) * C::STAGE_BYTES, (kt + C::NS) * C::BK, K);
+            load_frags<C>(lds + ((kt + 1) % C::NS) * C::STAGE_BYTES, 0, xf[0], wf[0]);
+            mfma_substep<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1]);
+            // the refill's loads one per MFMA (any excess first), then the
+            // next step's first fragments
+            if constexpr (C::LPS > kMf) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, C::LPS - kMf, 0);
+#pragma unroll
+            for (int m = 0; m < kMf; ++m) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                if (m < C::LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+                if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+        }
+        // the last step
+        const char* cur = lds + ((nk - 1) % C::NS) * C::STAGE_BYTES;
+#pragma unroll
+        for (int s = 0; s < C::KSUB; ++s) {
+            if (s + 1 < C::KSUB) load_frags<C>(cur, s + 1, xf[(s + 1) & 1], wf[(s + 1) & 1]);
+            mfma_substep<C>(st, xf[s & 1], wf[s & 1]);
+        }
+    }
+    // the zero-filling loads past the end drain; every wave finishes reading
+    // LDS before the next tile's loads overwrite it; a flag still pending
+    // (nk < NS) is published here
+    wait_vmcnt<0>();
+    stage_barrier();
+    publish_pending(a, hk);
+}
+
 // Every group holds G/8 workgroups; group x has R_x = R/8 + (x < R%8) reducers
 // and C_x = G/8 - R_x compute workgroups, so the groups' compute counts add up
 // to C = G - R whatever R is.
@@ -1050,7 +1159,10 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
                                  tile_cols(a.g, t));
     }
     while (q < a.g.tiles) {
-        tile_kloop<C, LOADER>(a, lds, st, job, hk, eng);
+        if constexpr (C::XP)
+            tile_kloop_xp<C>(a, lds, st, job, hk);
+        else
+            tile_kloop<C, LOADER>(a, lds, st, job, hk, eng);
         // issue the next tile's first stages before this tile's stores
         const int qn = q + Ctot;
         TileCoord tn = t;
@@ -1106,9 +1218,9 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
     // without dedicated reducers the compute workgroups reduce the slice
     const bool interleave = FUSED && a.num_reducers == 0;
     const int wave = uni((int)(threadIdx.x >> 6));
-    if (wave < C::LW)
+    if (C::EW == 0 || wave < C::LW)
         compute_waves<C, FUSED, true>(a, lds, pos, who, epoch, interleave);
-    else
+    else if constexpr (C::EW > 0)
         compute_waves<C, FUSED, false>(a, lds, pos, who, epoch, interleave);
 }
 

@@ -64,6 +64,18 @@ def test_every_tile_config_integer_bit_exact(tile, red):
     assert np.array_equal(host(b.out), out_o)
 
 
+@pytest.mark.parametrize("k_local", [8, 40, 72])
+@pytest.mark.parametrize("tile", ["16x64", "64x128", "128x128", "128x256", "256x128", "256x256"])
+def test_short_k_every_tile_integer_bit_exact(tile, k_local):
+    # one, two or three K steps, the last one partial (BK is 32, 64 or 128)
+    cfg = synthetic.Config("short_k", 5, 8 * 264, 392, k_local)
+    op, b, _, (send_o, local_o, out_o) = _full_compare(cfg, "integer", 2, tile=tile, num_reducers=0)
+    for i in range(7):
+        assert np.array_equal(host(b.send[i]), send_o[i]), f"send[{i}]"
+    assert np.array_equal(host(b.local), local_o)
+    assert np.array_equal(host(b.out), out_o)
+
+
 def test_reduce_scatter_invariant_consistent_peers():
     """Peers are the other ranks' real partials: out must equal slice `rank` of
     the unsharded product (exact with integer inputs)."""
