@@ -60,6 +60,10 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="run only a plain copy of known size and a few fused launches of --workload "
                         "(the program a rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass runs)")
+    p.add_argument("--split-sweep", metavar="OUT_JSON",
+                   help="time the fused launch of --workload over the compute/reducer split (dedicated "
+                        "reducer workgroups R), the flag padding and the in-loop reducer slots, write "
+                        "the table to OUT_JSON and exit")
     p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -359,6 +363,62 @@ def traffic_from(args):
     print(json.dumps(t))
 
 
+SPLIT_KNOBS = (
+    [dict(num_reducers=r) for r in (0, 2, 4, 8, 16, 32, 64)]
+    + [dict(num_reducers=r, flag_stride=32) for r in (0, 8, 64)]
+    + [dict(num_reducers=0, engine_interval=n) for n in (1, 4)]
+)
+
+
+def split_sweep(args):
+    """Fused launch times of one workload over the reducer placements and the
+    flag layout, side by side with the GEMM-only launch and the standalone
+    reduce (one set of buffers, one handle per setting).  Every setting's
+    `out` must equal the default setting's bit for bit (same sum order)."""
+    import torch
+
+    from tensor_gemm_reduce_amd import gemm_rs as gr
+
+    base = Case(args.workload, args)
+    cfg = base.cfg
+    ops = []
+    for kw in SPLIT_KNOBS:
+        op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=base.rank, tile=args.tile, **kw)
+        ops.append((kw, op))
+    run = lambda op, mode: op.run(mode, base.x, base.w, base.send, base.peers, base.out, base.local)
+    base.run(gr.MODE_FUSED)
+    torch.cuda.synchronize()
+    want = base.out.clone()
+    same = []
+    for kw, op in ops:
+        base.out.zero_()
+        run(op, gr.MODE_FUSED)
+        torch.cuda.synchronize()
+        same.append(bool(torch.equal(base.out, want)))
+    fns = {"gemm": lambda: base.run(gr.MODE_GEMM_ONLY), "reduce": lambda: base.run(gr.MODE_REDUCE_ONLY)}
+    for i, (kw, op) in enumerate(ops):
+        fns[f"k{i}"] = (lambda o: (lambda: run(o, gr.MODE_FUSED)))(op)
+    t = time_interleaved(fns, rounds=max(4, args.steps // 20))
+    tg, tr = statistics.median(t["gemm"]), statistics.median(t["reduce"])
+    rows = []
+    for i, (kw, op) in enumerate(ops):
+        st = op.status()
+        tf = statistics.median(t[f"k{i}"])
+        rows.append({**kw, "flag_stride": kw.get("flag_stride", 1), "engine_interval": kw.get("engine_interval", 0),
+                     "compute_wgs": op.info.compute_wgs, "reducer_wgs": op.info.reducer_wgs,
+                     "T_fused_us": tf, "fused_tflops": cfg.flops / tf * 1e-6,
+                     "overlap": 1.0 - (tf - tg) / tr, "out_matches_default": same[i],
+                     "status": gr.gemm_rs_strerror(st)})
+        log(f"[{args.workload}] {kw}: {tf:.1f} us, overlap {rows[-1]['overlap']:.2f}, same={same[i]}, "
+            f"status={rows[-1]['status']}")
+    res = {"workload": args.workload, "T_gemm_us": tg, "T_reduce_us": tr, "launch": base.op.info.as_dict(),
+           "rows": rows, "source_digest": source_digest()}
+    with open(args.split_sweep, "w") as f:
+        json.dump(res, f, indent=1)
+    if not all(same) or any(r["status"] != gr.gemm_rs_strerror(gr.OK) for r in rows):
+        raise RuntimeError("a setting changed the result or reported an error")
+
+
 def stats_summary(path):
     """Markdown table of rocprofv3's per-kernel statistics (durations in us)."""
     import csv
@@ -397,6 +457,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(args)
+        return
+    if args.split_sweep:
+        split_sweep(args)
         return
     c = Case(args.workload, args)
     cfg = c.cfg
