@@ -157,9 +157,9 @@ struct TileCfg {
     static_assert(!STAGED_EPI || WAVES * EPI_AREA <= STAGE_BYTES, "epilogue staging fits one stage buffer");
     static_assert((NS - 2) * LPS + STORES <= 63, "vmcnt range");
     static constexpr int ENG_LDS = EW * kEngAreas * kEngAreaBytes;
-    // One wave per SIMD (four waves whose stages fit only once per CU) with
-    // every wave loading: the K loop is pipelined across steps.
-    static constexpr bool XP = WAVES == 4 && EW == 0 && LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
+    // One workgroup per CU (four waves whose stages fit only once, or eight
+    // waves) with every wave loading: the K loop is pipelined across steps.
+    static constexpr bool XP = EW == 0 && LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
 };
 
 template <int MF> struct AccT;
@@ -1014,10 +1014,11 @@ __device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
     }
 }
 
-// The K loop of a tile for kernels with one wave per SIMD (every wave loads),
-// pipelined across K steps.  No sibling wave covers the LDS round trip of a
-// step's first fragments there, so substep 0 of step kt+1 is read while the
-// last substep of step kt computes.  The step's wait and barrier therefore sit
+// The K loop of a tile for kernels with one workgroup per CU (every wave
+// loads), pipelined across K steps: substep 0 of step kt+1 is read while the
+// last substep of step kt computes, so no wave starts a step with an LDS round
+// trip (with one wave per SIMD no sibling covers it; with two, both waves of a
+// SIMD leave the same barrier together).  The step's wait and barrier therefore sit
 // before its last substep: they certify that every wave's loads of stage kt+1
 // have landed and that every wave has read all of stage kt (each wave waits for
 // its LDS reads first), whose buffer is refilled right after the barrier with
