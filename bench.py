@@ -237,7 +237,8 @@ def measure_case(c: Case, warmup, iters):
 
 
 def check_case(c: Case, rows_per=3):
-    """Untimed parity check on sampled rows against the oracle."""
+    """Untimed parity check on sampled rows against the oracle, and the local
+    slice's error against the unfused path's (no worse than 1.1x)."""
     import numpy as np
 
     import oracle
@@ -255,9 +256,14 @@ def check_case(c: Case, rows_per=3):
     out = host(c.out)[rows]
     want_out = oracle.slice_sum(local, [p[rows] for p in peers], tp=8)
     ref = oracle.ref_f64(x, w, None, tp=8, rank=c.rank, rows=rows)
-    err_local = float(np.max(np.abs(oracle.bf16_to_f32(local) - ref)) / np.max(np.abs(ref)))
-    ok = bool(np.array_equal(out, want_out)) and err_local <= 1e-2
-    return {"ok": ok, "rows": int(rows.size), "local_max_rel_err": err_local}
+    err = lambda bits: float(np.max(np.abs(oracle.bf16_to_f32(bits) - ref)) / np.max(np.abs(ref)))
+    err_local = err(local)
+    # the unfused path's local slice: the vendor GEMM with BF16 output
+    y = c.matmul()[c.rank * cfg.S + torch.from_numpy(rows).cuda()]
+    err_unfused = err(y.view(torch.int16).cpu().numpy().view(np.uint16))
+    ok = bool(np.array_equal(out, want_out)) and err_local <= 1e-2 and err_local <= 1.1 * err_unfused
+    return {"ok": ok, "rows": int(rows.size), "local_max_rel_err": err_local,
+            "unfused_local_max_rel_err": err_unfused}
 
 
 def cpu_baseline(c: Case, seconds):

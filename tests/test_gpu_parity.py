@@ -125,6 +125,39 @@ def test_full_compare_within_tolerance(name, mode, red):
     assert max_rel(out_o, ref) <= 1e-2
 
 
+@pytest.mark.parametrize("name", ["tiny", "o_proj", "down_proj"])
+@pytest.mark.parametrize("mode", ["normal", "balanced"])
+def test_error_within_1p1x_of_unfused_path(name, mode):
+    """Fused `out` and local slice against the FP64 reference: no worse than
+    1.1x the error of the unfused path (the vendor GEMM with BF16 output,
+    then the standalone reduce kernel over its slice), same statistic."""
+    import torch
+
+    cfg = synthetic.CONFIGS[name]
+    rank = 3
+    x, w, peers = synthetic.make_inputs(cfg, mode)
+    op = _op(cfg, rank=rank)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    run(op, b)
+    fused_out, fused_local = host(b.out), host(b.local)
+    S = cfg.S
+    y = torch.nn.functional.linear(b.x.view(torch.bfloat16), b.w.view(torch.bfloat16))
+    b.local.copy_(y[rank * S:(rank + 1) * S].view(torch.int16))
+    b.out.fill_(np.array(SENTINEL, np.uint16).view(np.int16).item())
+    run(op, b, gr.MODE_REDUCE_ONLY)
+    unfused_out, unfused_local = host(b.out), host(b.local)
+    rows = np.arange(S) if S <= 256 else sample_rows(S, op.info.bm, np.random.default_rng(2), extra=6)
+    ref_out = oracle.ref_f64(x, w, peers, tp=8, rank=rank, rows=rows)
+    ref_local = oracle.ref_f64(x, w, None, tp=8, rank=rank, rows=rows)
+    e_fused = max_rel(fused_out[rows], ref_out)
+    e_unfused = max_rel(unfused_out[rows], ref_out)
+    assert e_fused <= 1e-2
+    assert e_fused <= 1.1 * e_unfused, (e_fused, e_unfused)
+    l_fused = max_rel(fused_local[rows], ref_local)
+    l_unfused = max_rel(unfused_local[rows], ref_local)
+    assert l_fused <= 1.1 * l_unfused, (l_fused, l_unfused)
+
+
 # ------------------------------------------------------------------ full shapes, sampled rows
 
 @pytest.mark.parametrize("red", ["bench", "engine_loop3", "reducers8"])
