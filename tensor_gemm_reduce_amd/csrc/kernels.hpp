@@ -1078,6 +1078,10 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
             wait_lgkm0();
             stage_barrier();
             if (kt + 1 == C::NS - 1) publish_pending(a, hk);
+            // raised issue priority from the barrier to the end of the step,
+            // while the wave issues the refill (measured: ~1% faster than
+            // without, and than raising it over the MFMA-only part)
+            __builtin_amdgcn_s_setprio(1);
             issue_stage<C>(job.lp, rx, rw, lds + (kt % C::NS) * C::STAGE_BYTES, (kt + C::NS) * C::BK, K);
             load_frags<C>(lds + ((kt + 1) % C::NS) * C::STAGE_BYTES, 0, xf[0], wf[0]);
             mfma_substep<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1]);
@@ -1090,6 +1094,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
                 if (m < C::LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
                 if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         // the last step
         const char* cur = lds + ((nk - 1) % C::NS) * C::STAGE_BYTES;
