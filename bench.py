@@ -64,6 +64,10 @@ def parse():
                    help="time the fused launch of --workload over the compute/reducer split (dedicated "
                         "reducer workgroups R), the flag padding and the in-loop reducer slots, write "
                         "the table to OUT_JSON and exit")
+    p.add_argument("--allreduce-sweep", metavar="OUT_JSON",
+                   help="time GEMM + all-reduce (gemm_rs_run_allreduce: the reduce-scatter whose sum also "
+                        "replicates the reduced slice to the 7 peers) on every benchmark shape, write "
+                        "OUT_JSON and exit")
     p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -425,6 +429,52 @@ def split_sweep(args):
         raise RuntimeError("a setting changed the result or reported an error")
 
 
+def allreduce_sweep(args):
+    """GEMM + all-reduce per benchmark shape: the fused launch with the gather
+    stores, side by side with the GEMM-only launch, the standalone reduce with
+    the gather stores, the reduce-scatter alone (fused, no gather) and
+    hipBLASLt's GEMM.  Algorithmic bytes of the all-reduce's sum: 8 reads and
+    1 + 7 writes of 2 bytes per slice element, 4*M*N."""
+    import torch
+
+    rows = {}
+    for name in (DEFAULT_WORKLOAD,) + SWEEP:
+        c = Case(name, args)
+        cfg = c.cfg
+        gr = c.gr
+        gather = [torch.empty_like(c.out) for _ in range(7)]
+        ar = lambda mode: c.op.run(mode, c.x, c.w, c.send, c.peers, c.out, c.local, gather=gather)
+        ar(gr.MODE_FUSED)
+        torch.cuda.synchronize()
+        same = all(torch.equal(g, c.out) for g in gather)
+        t = time_interleaved({"fused_ar": lambda: ar(gr.MODE_FUSED), "gemm": lambda: c.run(gr.MODE_GEMM_ONLY),
+                              "reduce_ar": lambda: ar(gr.MODE_REDUCE_ONLY), "fused_rs": lambda: c.run(gr.MODE_FUSED),
+                              "matmul": c.matmul}, rounds=max(4, args.steps // 20))
+        st = c.op.status()
+        med = {k: statistics.median(v) for k, v in t.items()}
+        ar_bytes = 4.0 * cfg.M * cfg.N
+        rows[name] = {
+            "shape": {"M": cfg.M, "N": cfg.N, "K_local": cfg.K_local},
+            "T_fused_ar_us": med["fused_ar"], "T_gemm_us": med["gemm"], "T_reduce_ar_us": med["reduce_ar"],
+            "T_fused_rs_us": med["fused_rs"], "T_torch_linear_us": med["matmul"],
+            "fused_ar_tflops": cfg.flops / med["fused_ar"] * 1e-6,
+            "fused_ar_pct_peak": 100.0 * cfg.flops / med["fused_ar"] * 1e-6 / PEAK_BF16_TFLOPS,
+            "reduce_ar_gbs": ar_bytes / med["reduce_ar"] * 1e-3,
+            "overlap_ar": 1.0 - (med["fused_ar"] - med["gemm"]) / med["reduce_ar"],
+            "speedup_vs_unfused": (med["matmul"] + med["reduce_ar"]) / med["fused_ar"],
+            "gather_equals_out": same, "status": gr.gemm_rs_strerror(st),
+        }
+        log(f"[{name}] all-reduce: " + json.dumps({k: rows[name][k] for k in
+                                                   ("T_fused_ar_us", "T_gemm_us", "T_reduce_ar_us", "overlap_ar",
+                                                    "gather_equals_out")}))
+        del c, gather
+        torch.cuda.empty_cache()
+    with open(args.allreduce_sweep, "w") as f:
+        json.dump({"rows": rows, "source_digest": source_digest()}, f, indent=1)
+    if not all(r["gather_equals_out"] and r["status"] == "success" for r in rows.values()):
+        raise RuntimeError("an all-reduce run reported an error or a gather buffer differs from out")
+
+
 def stats_summary(path):
     """Markdown table of rocprofv3's per-kernel statistics (durations in us)."""
     import csv
@@ -466,6 +516,9 @@ def main():
         return
     if args.split_sweep:
         split_sweep(args)
+        return
+    if args.allreduce_sweep:
+        allreduce_sweep(args)
         return
     c = Case(args.workload, args)
     cfg = c.cfg

@@ -180,6 +180,26 @@ int gemm_rs_run(gemm_rs_handle *h, int32_t mode, const void *x, const void *w,
                 void *const *send, const void *const *peers, void *out,
                 void *local_slice, void *stream);
 
+/* GEMM + all-reduce for one node (mKernel, "mKernel: Fast Multi-GPU,
+ * Multi-Node Fused Kernels", Sections 3.1 and 4: the local reduction is followed
+ * by replication, each GPU sending its reduced eighth of the output to the
+ * others).  The same run as gemm_rs_run, and every chunk of the reduced slice
+ * that the sum stores into `out` is also stored, in the same launch, into
+ * gather[0..tp-2]:
+ *   gather       host array of tp-1 device pointers, each [S][N] BF16, 16-byte
+ *                aligned; gather[i] receives this rank's reduced slice for peer
+ *                rank p_i (the all-gather's send to that peer: rows
+ *                rank*S .. rank*S+S-1 of the peer's M x N result).  Required
+ *                (GEMM_RS_ERR_INVALID_ARG if NULL) except for GEMM_ONLY, which
+ *                writes no reduced slice and ignores it.
+ * In a caller that passes for `out` the rows rank*S .. of its own M x N
+ * result, that buffer holds this rank's part of the all-reduce; the other
+ * ranks' parts are what they send.  Same ownership and error behaviour as
+ * gemm_rs_run; REDUCE_ONLY and SEQUENTIAL fill gather[] too. */
+int gemm_rs_run_allreduce(gemm_rs_handle *h, int32_t mode, const void *x, const void *w,
+                          void *const *send, const void *const *peers, void *out,
+                          void *local_slice, void *const *gather, void *stream);
+
 /* Waits for the handle's last run and returns its device status:
  * GEMM_RS_OK, or GEMM_RS_ERR_TIMEOUT if a reducer gave up waiting for a ready
  * flag (the kernel still exits; `out` is then incomplete).  Reading the status

@@ -186,6 +186,32 @@ def gemm_rs(x: np.ndarray, w: np.ndarray, peers, tp: int, rank: int):
     return send, local, out
 
 
+def gemm_allreduce(x: np.ndarray, w: np.ndarray, peers, tp: int, rank: int):
+    """GEMM + all-reduce for one rank of one node ("mKernel: Fast Multi-GPU,
+    Multi-Node Fused Kernels", Sections 3.1 and 4: the local reduction, then
+    replication of each GPU's reduced eighth to the others).  The reduction is
+    gemm_rs's; the all-gather moves values without arithmetic, so gather[i],
+    what peer rank peer_rank(rank, i) receives, is a copy of out.
+    Returns (send[tp-1], local, out, gather[tp-1]), all BF16 bits."""
+    send, local, out = gemm_rs(x, w, peers, tp, rank)
+    return send, local, out, [out.copy() for _ in range(tp - 1)]
+
+
+def allreduce_result(outs, gathers, rank: int) -> np.ndarray:
+    """The M x N all-reduce result held by `rank` after the all-gather: its own
+    rows r*S.. from its reduced slice, every other rank q's rows from what q sent
+    it (q's gather entry for `rank`).  outs[q], gathers[q] as gemm_allreduce."""
+    tp = len(outs)
+    rows = []
+    for q in range(tp):
+        if q == rank:
+            rows.append(outs[q])
+        else:
+            slot = rank if rank < q else rank - 1  # slot of `rank` in q's peer list
+            rows.append(gathers[q][slot])
+    return np.concatenate(rows, axis=0)
+
+
 def ref_f64(x: np.ndarray, w: np.ndarray, peers, tp: int, rank: int, rows=None) -> np.ndarray:
     """FP64 value of this rank's slice sum with no BF16 rounding of the local partial.
 

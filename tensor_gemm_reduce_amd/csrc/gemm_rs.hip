@@ -371,7 +371,7 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
 }
 
 static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, void* const* send,
-                      const void* const* peers, void* out, uint16_t* local)
+                      const void* const* peers, void* out, uint16_t* local, void* const* gather)
 {
     memset(&a, 0, sizeof a);
     a.x = static_cast<const uint16_t*>(x);
@@ -385,6 +385,8 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     }
     for (int i = 0; i < kPeers; ++i) a.peers[i] = peers ? static_cast<const uint16_t*>(peers[i]) : nullptr;
     a.out = static_cast<uint16_t*>(out);
+    a.gather_on = gather ? 1 : 0;
+    for (int i = 0; i < kPeers; ++i) a.gather[i] = gather ? static_cast<uint16_t*>(gather[i]) : nullptr;
     a.flags = h->flags;
     a.state = h->state;
     a.trace = h->trace;
@@ -430,8 +432,8 @@ static int launch_reduce(gemm_rs_handle* h, Args& a, hipStream_t s)
     return GEMM_RS_OK;
 }
 
-int gemm_rs_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
-                const void* const* peers, void* out, void* local_slice, void* stream)
+static int run_impl(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                    const void* const* peers, void* out, void* local_slice, void* const* gather, void* stream)
 {
     if (!h) return GEMM_RS_ERR_INVALID_ARG;
     if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
@@ -459,13 +461,19 @@ int gemm_rs_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, v
             if (!peers[i]) return GEMM_RS_ERR_INVALID_ARG;
             if (!aligned16(peers[i])) return GEMM_RS_ERR_MISALIGNED;
         }
+        if (gather) {
+            for (int i = 0; i < kPeers; ++i) {
+                if (!gather[i]) return GEMM_RS_ERR_INVALID_ARG;
+                if (!aligned16(gather[i])) return GEMM_RS_ERR_MISALIGNED;
+            }
+        }
     }
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
     if (dev != h->device) return GEMM_RS_ERR_INVALID_ARG;
 
     Args a;
-    fill_args(h, a, x, w, send, peers, out, local);
+    fill_args(h, a, x, w, send, peers, out, local, needs_sum ? gather : nullptr);
     int rc = GEMM_RS_OK;
     switch (mode) {
     case GEMM_RS_MODE_FUSED: rc = launch_gemm(h, a, true, s); break;
@@ -477,6 +485,20 @@ int gemm_rs_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, v
         break;
     }
     return rc;
+}
+
+int gemm_rs_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                const void* const* peers, void* out, void* local_slice, void* stream)
+{
+    return run_impl(h, mode, x, w, send, peers, out, local_slice, nullptr, stream);
+}
+
+int gemm_rs_run_allreduce(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                          const void* const* peers, void* out, void* local_slice, void* const* gather,
+                          void* stream)
+{
+    if (mode != GEMM_RS_MODE_GEMM_ONLY && !gather) return GEMM_RS_ERR_INVALID_ARG;
+    return run_impl(h, mode, x, w, send, peers, out, local_slice, gather, stream);
 }
 
 int gemm_rs_status(gemm_rs_handle* h)

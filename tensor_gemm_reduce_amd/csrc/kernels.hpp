@@ -94,6 +94,8 @@ struct Args {
     uint16_t* dst[8];        // destination slice buffers by destination rank
     const uint16_t* peers[kPeers];
     uint16_t* out;           // [S][N]
+    uint16_t* gather[kPeers];  // all-reduce runs: [S][N] copies of out, one per peer
+    int32_t gather_on;       // 1: every summed chunk is also stored into gather[]
     uint32_t* flags;         // ready flags, flag_stride words apart
     DeviceState* state;
     uint32_t* trace;         // 4 words per slot (debug)
@@ -496,6 +498,22 @@ __device__ __forceinline__ u32x4 pack8(const f32x8& acc)
     return o;
 }
 
+// Stores one summed 16-byte chunk at byte offset boff of the slice: into
+// `out` and, in an all-reduce run, also into the 7 gather buffers (the
+// all-gather that follows the reduce-scatter replicates this rank's reduced
+// slice to every peer).  Returns the number of store instructions issued.
+__device__ __forceinline__ int store_sum(const Args& a, const u32x4& v, uint32_t boff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags),
+                                           boff, 0, kAuxNt);
+    if (!a.gather_on) return 1;
+#pragma unroll
+    for (int i = 0; i < kPeers; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, __builtin_amdgcn_make_buffer_rsrc(a.gather[i], 0, a.slice_bytes, kRsrcFlags), boff, 0, kAuxNt);
+    return 1 + kPeers;
+}
+
 template <int AUX>
 __device__ __forceinline__ void lds_load16(const uint16_t* g, const char* slot)
 {
@@ -524,6 +542,10 @@ __device__ __forceinline__ void sum_chunk(const Args& a, const uint16_t* local, 
     }
     const u32x4 o = pack8(acc);
     *reinterpret_cast<uint4*>(a.out + off) = make_uint4(o.x, o.y, o.z, o.w);
+    if (a.gather_on) {
+#pragma unroll
+        for (int i = 0; i < kPeers; ++i) *reinterpret_cast<uint4*>(a.gather[i] + off) = make_uint4(o.x, o.y, o.z, o.w);
+    }
 }
 
 // Sum a rows x cols block of the slice starting at (row0, col0), 16-byte
@@ -724,9 +746,7 @@ __device__ __forceinline__ void engine_consume(Engine& e, const Args& a, const E
         if (o.step < 3) {
             e.acc = acc;
         } else {
-            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
-            __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, o.soff, 0, kAuxNt);
-            e.vm += 1;
+            e.vm += store_sum(a, pack8(acc), o.soff);
         }
     } else if (o.op == kOpPoll) {
         const int lane = threadIdx.x & 63;
@@ -837,7 +857,6 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
     bool gave_up = false;
     const __amdgpu_buffer_rsrc_t rl =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.dst[a.g.rank], 0, a.slice_bytes, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags);
     for (int base = first; base < m.nitems; base += kDrainBatch * stride) {
         uint32_t boff[kDrainBatch];
         u32x4 v[kDrainBatch][kPeers + 1];
@@ -863,7 +882,7 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
             f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[b][s]);
-            __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), ro, boff[b], 0, kAuxNt);
+            store_sum(a, pack8(acc), boff[b]);
         }
     }
 }
@@ -1286,7 +1305,12 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
             f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[s]);
-            __builtin_nontemporal_store(pack8(acc), reinterpret_cast<u32x4*>(a.out + off));
+            const u32x4 o = pack8(acc);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + off));
+            if (a.gather_on) {
+#pragma unroll
+                for (int i = 0; i < kPeers; ++i) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.gather[i] + off));
+            }
         }
     }
 }

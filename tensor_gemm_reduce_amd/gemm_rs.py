@@ -41,7 +41,7 @@ TILES = {"auto": 0, "16x64": 1, "64x128": 2, "128x128": 3, "128x256": 4, "256x12
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-           "gemm_rs_run", "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read",
+           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read",
            "gemm_rs_destroy", "gemm_rs_strerror")
 
 
@@ -91,6 +91,8 @@ def lib():
         L.gemm_rs_create.argtypes = [cfgp, ctypes.POINTER(vp)]
         L.gemm_rs_run.argtypes = [vp, ctypes.c_int32, vp, vp, ctypes.POINTER(vp),
                                   ctypes.POINTER(vp), vp, vp, vp]
+        L.gemm_rs_run_allreduce.argtypes = [vp, ctypes.c_int32, vp, vp, ctypes.POINTER(vp),
+                                            ctypes.POINTER(vp), vp, vp, ctypes.POINTER(vp), vp]
         L.gemm_rs_status.argtypes = [vp]
         L.gemm_rs_query.argtypes = [vp, infop]
         L.gemm_rs_debug_read.argtypes = [vp, u32p, ctypes.c_size_t, u32p, ctypes.c_size_t]
@@ -99,7 +101,8 @@ def lib():
         L.gemm_rs_strerror.argtypes = [ctypes.c_int]
         L.gemm_rs_strerror.restype = ctypes.c_char_p
         for name in ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-                     "gemm_rs_run", "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read"):
+                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_status", "gemm_rs_query",
+                     "gemm_rs_debug_read"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -165,6 +168,16 @@ def gemm_rs_run(h, mode: int, x: int, w: int, send, peers, out: int, local: int 
     return lib().gemm_rs_run(h, mode, x, w, send_arr, peer_arr, out, local, stream)
 
 
+def gemm_rs_run_allreduce(h, mode: int, x: int, w: int, send, peers, out: int, local: int | None,
+                          gather, stream: int | None) -> int:
+    """As gemm_rs_run, plus gather: a list of 7 device addresses (or None)."""
+    vp = ctypes.c_void_p
+    send_arr = (vp * 7)(*send) if send is not None else None
+    peer_arr = (vp * 7)(*peers) if peers is not None else None
+    gather_arr = (vp * 7)(*gather) if gather is not None else None
+    return lib().gemm_rs_run_allreduce(h, mode, x, w, send_arr, peer_arr, out, local, gather_arr, stream)
+
+
 def gemm_rs_status(h) -> int:
     return lib().gemm_rs_status(h)
 
@@ -228,7 +241,10 @@ class GemmRS:
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
 
-    def run(self, mode, x=None, w=None, send=None, peers=None, out=None, local=None, stream=None):
+    def run(self, mode, x=None, w=None, send=None, peers=None, out=None, local=None, stream=None,
+            gather=None):
+        """One run; with `gather` (7 [S][N] tensors) the all-reduce variant, whose
+        sum also stores the reduced slice into every gather buffer."""
         import torch
 
         c = self.cfg
@@ -246,18 +262,25 @@ class GemmRS:
             for i, p in enumerate(peers):
                 self._check_tensor(p, SN, f"peers[{i}]")
             self._check_tensor(out, SN, "out")
+            if gather is not None:
+                if len(gather) != c.tp - 1:
+                    raise ValueError("gather: need tp-1 buffers")
+                for i, g in enumerate(gather):
+                    self._check_tensor(g, SN, f"gather[{i}]")
         if local is not None:
             self._check_tensor(local, SN, "local")
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
-        rc = gemm_rs_run(
-            self.h, mode,
-            _ptr(x) if x is not None else None, _ptr(w) if w is not None else None,
-            [_ptr(s) for s in send] if send is not None else None,
-            [_ptr(p) for p in peers] if peers is not None else None,
-            _ptr(out) if out is not None else None,
-            _ptr(local) if local is not None else None, stream)
-        _check(rc, "gemm_rs_run")
+        args = (self.h, mode,
+                _ptr(x) if x is not None else None, _ptr(w) if w is not None else None,
+                [_ptr(s) for s in send] if send is not None else None,
+                [_ptr(p) for p in peers] if peers is not None else None,
+                _ptr(out) if out is not None else None,
+                _ptr(local) if local is not None else None)
+        if gather is None:
+            _check(gemm_rs_run(*args, stream), "gemm_rs_run")
+        else:
+            _check(gemm_rs_run_allreduce(*args, [_ptr(g) for g in gather], stream), "gemm_rs_run_allreduce")
 
     def status(self) -> int:
         return gemm_rs_status(self.h)

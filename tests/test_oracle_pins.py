@@ -235,6 +235,32 @@ def test_reduce_scatter_invariant_consistent_peers(rank):
     assert np.array_equal(oracle.bf16_to_f32(out).astype(np.int64), full[rank * S:(rank + 1) * S])
 
 
+def test_allreduce_gives_every_rank_the_unsharded_product():
+    """All-reduce invariant: after the reduce-scatter and the all-gather, every
+    one of the 8 ranks holds the whole unsharded product X * W^T, rounded once
+    to BF16 (exact with integer inputs), and all 8 results are identical."""
+    cfg = synthetic.Config("ar_inv", 0, 64, 48, 16)
+    shards = synthetic.make_shards(cfg, integer=True)
+    S = cfg.S
+    parts = {}
+    for p, (xp, wp) in enumerate(shards):
+        zero = [np.zeros((S, cfg.N), np.uint16)] * 7
+        send, local, _ = oracle.gemm_rs(xp, wp, zero, tp=8, rank=p)
+        parts[p] = send
+    outs, gathers = [], []
+    for r, (xr, wr) in enumerate(shards):
+        peers = [parts[q][r if r < q else r - 1] for q in (oracle.peer_rank(r, i) for i in range(7))]
+        _, _, out, gather = oracle.gemm_allreduce(xr, wr, peers, tp=8, rank=r)
+        outs.append(out)
+        gathers.append(gather)
+    X = np.concatenate([oracle.bf16_to_f32(s[0]).astype(np.int64) for s in shards], axis=1)
+    W = np.concatenate([oracle.bf16_to_f32(s[1]).astype(np.int64) for s in shards], axis=1)
+    want = oracle.f32_to_bf16((X @ W.T).astype(np.float32))
+    results = [oracle.allreduce_result(outs, gathers, r) for r in range(8)]
+    for r in range(8):
+        assert np.array_equal(results[r], want), r
+
+
 def test_zero_x_gives_sum_of_peers():
     cfg = synthetic.CONFIGS["tiny"]
     x, w, peers = synthetic.make_inputs(cfg, "zero_x")
