@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tile", default="auto")
     p.add_argument("--reducers", type=int, default=-1)
+    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "stream"],
+                   help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--engine-interval", type=int, default=0,
                    help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
     p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
@@ -103,11 +105,22 @@ class Case:
         self.local = z()
         self.out = z()
         self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
-                            num_reducers=args.reducers, engine_interval=args.engine_interval)
+                            num_reducers=args.reducers, engine_interval=args.engine_interval,
+                            reduce_mode=args.reduce_mode)
+        # where the fused launch streams the sum through the K loop, the same
+        # launch with the sum after the last tile is timed beside it
+        self.op_tail = None
+        if self.op.info.reduce_mode == gr.REDUCE_STREAM:
+            self.op_tail = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
+                                     num_reducers=args.reducers, engine_interval=args.engine_interval,
+                                     reduce_mode="tail")
         self.gr = gr
 
     def run(self, mode):
         self.op.run(mode, self.x, self.w, self.send, self.peers, self.out, self.local)
+
+    def run_tail(self):
+        self.op_tail.run(self.gr.MODE_FUSED, self.x, self.w, self.send, self.peers, self.out, self.local)
 
     def matmul(self):
         import torch
@@ -213,18 +226,25 @@ def summary(us):
 def measure_case(c: Case, warmup, iters):
     gr = c.gr
     cfg = c.cfg
-    t = time_interleaved({
+    fns = {
         "fused": lambda: c.run(gr.MODE_FUSED),
         "gemm": lambda: c.run(gr.MODE_GEMM_ONLY),
         "reduce": lambda: c.run(gr.MODE_REDUCE_ONLY),
         "seq": lambda: c.run(gr.MODE_SEQUENTIAL),
         "matmul": c.matmul,
-    }, rounds=max(4, -(-iters // 10)))
+    }
+    if c.op_tail is not None:
+        fns["fused_tail"] = c.run_tail
+    t = time_interleaved(fns, rounds=max(4, -(-iters // 10)))
     fused, gemm, red, seq, mm = (summary(t[k]) for k in ("fused", "gemm", "reduce", "seq", "matmul"))
     st = c.op.status()
     if st != gr.OK:
         raise RuntimeError(f"{c.name}: device status {gr.gemm_rs_strerror(st)}")
     tf, tg, tr = fused["median_us"], gemm["median_us"], red["median_us"]
+    extra = {}
+    if c.op_tail is not None:
+        tail = summary(t["fused_tail"])
+        extra = {"T_fused_tail_us": tail, "overlap_tail": 1.0 - (tail["median_us"] - tg) / tr}
     return {
         "shape": {"M": cfg.M, "N": cfg.N, "K_local": cfg.K_local, "tp": cfg.tp},
         "launch": c.op.info.as_dict(),
@@ -237,6 +257,8 @@ def measure_case(c: Case, warmup, iters):
         "reduce_pct_hbm": 100.0 * cfg.reduce_bytes / tr * 1e-3 / PEAK_HBM_GBS,
         "overlap": 1.0 - (tf - tg) / tr,
         "speedup_vs_sequential": seq["median_us"] / tf,
+        "reduce_mode": {0: "auto", 1: "tail", 2: "stream"}[c.op.info.reduce_mode],
+        **extra,
     }
 
 
@@ -598,6 +620,9 @@ def main():
         "T_fused_us": m["T_fused_us"]["median_us"], "T_gemm_us": m["T_gemm_us"]["median_us"],
         "T_reduce_us": m["T_reduce_us"]["median_us"],
         "reduce_gbs": m["reduce_gbs"],
+        "reduce_mode": m["reduce_mode"],
+        "T_fused_tail_us": (m.get("T_fused_tail_us") or {}).get("median_us"),
+        "overlap_tail": m.get("overlap_tail"),
         "parity": check,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -607,6 +632,9 @@ def main():
                        "T_reduce_us": v.get("T_reduce_us", {}).get("median_us"),
                        "reduce_gbs": v.get("reduce_gbs"),
                        "T_torch_linear_us": v.get("T_torch_linear_us", {}).get("median_us"),
+                       "reduce_mode": v.get("reduce_mode"),
+                       "T_fused_tail_us": (v.get("T_fused_tail_us") or {}).get("median_us"),
+                       "overlap_tail": v.get("overlap_tail"),
                        "parity_ok": (v.get("parity") or {}).get("ok")} if "error" not in v else v)
                   for k, v in sweep.items()},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

@@ -92,6 +92,14 @@ extern "C" {
 #define GEMM_RS_TILE_256x256 6
 #define GEMM_RS_TILE_COUNT 7
 
+/* ---- where the slice sum runs without dedicated reducers or engine slots -- */
+#define GEMM_RS_REDUCE_AUTO 0   /* TAIL (measured faster on every benchmark shape)  */
+#define GEMM_RS_REDUCE_TAIL 1   /* each compute workgroup sums its share of the
+                                   slice after its last tile                      */
+#define GEMM_RS_REDUCE_STREAM 2 /* every wave streams its share through the K loop:
+                                   one load or store of the sum per K step, issued
+                                   behind the stage refill (256x256 tile only)    */
+
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
                                  the compute workgroup and a release timestamp */
@@ -115,6 +123,8 @@ typedef struct gemm_rs_config {
     int32_t flag_stride;  /* 32-bit words between ready flags (1 or 32)       */
     int64_t watchdog_us;  /* reducer wait limit per tile in microseconds;
                              0 = default (2 000 000)                          */
+    int32_t reduce_mode;  /* GEMM_RS_REDUCE_*; STREAM needs num_reducers <= 0,
+                             engine_interval == 0 and the 256x256 tile        */
 } gemm_rs_config;
 
 typedef struct gemm_rs_info {
@@ -134,6 +144,8 @@ typedef struct gemm_rs_info {
                                  0 contiguous blocks, 1 every 8th slot         */
     uint32_t epoch;           /* value the last FUSED run stored in its flags
                                  (read from the device; waits for the stream) */
+    int32_t reduce_mode;      /* resolved GEMM_RS_REDUCE_* of a FUSED run with
+                                 no dedicated reducers and no engine slots    */
 } gemm_rs_info;
 
 typedef struct gemm_rs_handle gemm_rs_handle;

@@ -55,6 +55,8 @@ struct TileDesc {
     int engine_lds_bytes;      // fused kernel with in-loop engine slots: stages + engine areas
     int lds_bytes;             // every other launch: stages
     const void* engine_kernel; // fused: compute waves run the reduce engine
+    const void* stream_kernel; // fused: the waves stream the sum through the K loop (or null)
+    int stream_lds_bytes;      // its LDS: stages + the streaming waves' slots
     const void* kernel;        // fused: dedicated reducer workgroups
     const void* gemm_kernel;   // the same GEMM without flags or reduction
 };
@@ -81,8 +83,14 @@ TileDesc desc()
     static_assert(elds <= 160 * 1024 - 64, "LDS of one workgroup");
     // occupancy is set by the stages; in-loop engine slots may cost it
     constexpr bool two = C::LDS_BYTES <= 80 * 1024 - 64;
+    // the reduce stream runs in the two-stage pipelined K loop of eight-wave tiles
+    constexpr bool stream = C::XP && C::NS == 2 && C::WAVES == 8;
+    constexpr int slds = C::LDS_BYTES + C::WAVES / kStreamOps * kStreamLds;
+    static_assert(!stream || slds <= 160 * 1024 - 64, "LDS of one workgroup");
+    const void* sk = nullptr;
+    if constexpr (stream) sk = reinterpret_cast<const void*>(&fused_kernel_8w<C, true, true>);
     return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, elds, C::LDS_BYTES,
-                    kernel_for<CE, true, two>(),
+                    kernel_for<CE, true, two>(), sk, stream ? slds : 0,
                     kernel_for<C, true, two>(), kernel_for<C, false, two>()};
 }
 
@@ -95,7 +103,7 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr};
+    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, 0, nullptr, nullptr};
     }
 }
 
@@ -118,6 +126,20 @@ int auto_tile(const gemm_rs_config& c)
 }
 
 int resolve_tile(const gemm_rs_config& c) { return c.tile == GEMM_RS_TILE_AUTO ? auto_tile(c) : c.tile; }
+
+// Tiles whose fused kernel can stream the slice sum through the K loop.
+bool stream_tile(int id) { return id == GEMM_RS_TILE_256x256; }
+
+// Where the slice sum of a fused run without dedicated reducers or engine
+// slots runs.
+int resolve_reduce_mode(const gemm_rs_config& c)
+{
+    if (c.num_reducers > 0 || c.engine_interval > 0) return GEMM_RS_REDUCE_TAIL;
+    // automatic: the sum after the last tile, measured faster than the stream
+    // on every benchmark shape
+    if (c.reduce_mode == GEMM_RS_REDUCE_AUTO) return GEMM_RS_REDUCE_TAIL;
+    return c.reduce_mode;
+}
 
 Geometry geometry_of(const gemm_rs_config& c)
 {
@@ -143,6 +165,7 @@ struct gemm_rs_handle {
     int num_cus;
     int wgs_per_cu;
     int fused_lds;
+    int reduce_mode;       // resolved GEMM_RS_REDUCE_* (TAIL when reducers or engine slots run the sum)
     int grid;
     int compute_wgs;
     int reducer_wgs;
@@ -207,6 +230,10 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
     if (c->watchdog_us < 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_STREAM)
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM && (c->num_reducers > 0 || c->engine_interval > 0))
+        return GEMM_RS_ERR_INVALID_ARG;
     if (c->tp != 8) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->M % c->tp != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->N % 8 != 0 || c->K_local % 8 != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
@@ -228,6 +255,7 @@ int gemm_rs_validate(const gemm_rs_config* c)
     const int64_t tiles = (int64_t)c->tp * ((S + bm - 1) / bm) * (((int64_t)c->N + bn - 1) / bn);
     if (tiles > (1 << 30)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->drop_flag >= 0 && c->drop_flag >= tiles) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM && !stream_tile(resolve_tile(*c))) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return GEMM_RS_OK;
 }
 
@@ -246,6 +274,7 @@ int gemm_rs_plan(const gemm_rs_config* c, gemm_rs_info* info)
     info->tiles_per_slice = g.ts;
     info->tile_rows_per_slice = g.tms;
     info->tile_cols = g.tnc;
+    info->reduce_mode = resolve_reduce_mode(*c);
     return GEMM_RS_OK;
 }
 
@@ -322,12 +351,22 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
         e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
     if (e == hipSuccess)
         e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+    if (e == hipSuccess && h->td.stream_kernel)
+        e = hipFuncSetAttribute(h->td.stream_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                h->td.stream_lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
+    h->reduce_mode = resolve_reduce_mode(*c);
     int occ = 0;
-    h->fused_lds = red_req == 0 && c->engine_interval > 0 ? h->td.engine_lds_bytes : h->td.lds_bytes;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ, red_req == 0 && c->engine_interval > 0 ? h->td.engine_kernel : h->td.kernel, h->td.threads,
-        h->fused_lds);
+    const void* fk = h->td.kernel;
+    h->fused_lds = h->td.lds_bytes;
+    if (red_req == 0 && c->engine_interval > 0) {
+        fk = h->td.engine_kernel;
+        h->fused_lds = h->td.engine_lds_bytes;
+    } else if (h->reduce_mode == GEMM_RS_REDUCE_STREAM) {
+        fk = h->td.stream_kernel;
+        h->fused_lds = h->td.stream_lds_bytes;
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, h->td.threads, h->fused_lds);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
     // the persistent grid holds the workgroups per CU the kernel was built for
     // (more would share a SIMD's registers between more waves than planned)
@@ -414,9 +453,14 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     void* params[] = {&a};
     // in-loop engine slots need the kernel whose waves are split into stage
     // loaders and engine waves; otherwise every wave loads stages
+    // (the reduce stream: every wave loads stages and streams its share of the sum)
     const bool engine = fused && h->reducer_wgs == 0 && h->cfg.engine_interval > 0;
-    HIP_TRY(hipLaunchKernel(engine ? h->td.engine_kernel : (fused ? h->td.kernel : h->td.gemm_kernel), dim3(h->grid),
-                            dim3(h->td.threads), params, fused ? h->fused_lds : h->td.lds_bytes, s));
+    const bool stream = fused && h->reducer_wgs == 0 && h->reduce_mode == GEMM_RS_REDUCE_STREAM;
+    const void* k = engine ? h->td.engine_kernel
+                  : stream ? h->td.stream_kernel
+                  : fused  ? h->td.kernel
+                           : h->td.gemm_kernel;
+    HIP_TRY(hipLaunchKernel(k, dim3(h->grid), dim3(h->td.threads), params, fused ? h->fused_lds : h->td.lds_bytes, s));
     return GEMM_RS_OK;
 }
 
@@ -536,6 +580,7 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->lds_bytes = h->fused_lds;
     info->reduce_grid = h->reduce_grid;
     info->xcd_split = h->strided;
+    info->reduce_mode = h->reduce_mode;
     // every workgroup's finish mark holds the epoch of the last fused launch
     HIP_TRY(hipStreamSynchronize(h->last_stream));
     HIP_TRY(hipMemcpy(&info->epoch, h->finished, sizeof info->epoch, hipMemcpyDeviceToHost));

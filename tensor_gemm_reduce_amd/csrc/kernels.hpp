@@ -897,6 +897,241 @@ __device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
     drain_items<2>(a, e.m, e.next, e.stride, e.epoch);
 }
 
+// ---------------------------------------------------------------- reduce stream
+//
+// The slice sum streamed through the cross-step pipelined K loop (eight-wave
+// workgroups, two stages).  With kStreamOps = 1 every wave streams; with 2
+// one wave per SIMD (waves 0..3) does, at twice the rate, so that the sibling
+// wave on its SIMD keeps the matrix core fed while the streaming wave runs the
+// sum's bookkeeping (measured: no better).  Streaming wave gw of TW owns a
+// contiguous range of items, [gw * n / TW, (gw + 1) * n / TW) of n, and per K
+// step issues at most kStreamOps vector-memory instructions of the sum, right
+// after its stage refill.  With two stages the next step's wait then lets
+// those instructions stay outstanding (and only those), so an operation issued
+// at step k has completed by the wait of step k + 2, where it is consumed: the
+// sum adds nothing to the stage waits.  Loads land in the wave's LDS slots
+// (LDS-direct loads), so nothing but the running FP32 sum is held in registers
+// while they fly.
+//
+// Per item, in the sum order: poll the tile's ready flag (unless the wave has
+// already seen that tile flagged), load peers 0..6 (they need no flag), load
+// the local chunk once the flag has been seen, then store the rounded sum into
+// `out` and, in an all-reduce run, into the 7 gather buffers, one store per
+// step.  A poll that finds the tile not yet flagged is repeated only after
+// kStreamBackoff steps; a step with nothing to issue and nothing in flight
+// runs no stream code at all.  Items a streaming wave has not finished when
+// the workgroup's last tile is done are summed by drain_items, split between
+// that wave and the waves that do not stream on its SIMD.
+
+constexpr int kStreamOps = 1;                      // per streaming wave and K step
+constexpr int kStreamQueue = 2 * kStreamOps;       // operations in flight (two steps)
+constexpr int kStreamSlots = kStreamQueue + 1;     // 1 KiB LDS slots per streaming wave
+constexpr int kStreamLds = kStreamSlots * 1024;
+constexpr int kStreamBackoff = 8;                  // K steps between polls of one tile
+
+enum StreamOp { kSoNone = 0, kSoPeer = 1, kSoPoll = 2, kSoLocal = 3 };
+
+struct Stream {
+    char* slots;          // this wave's kStreamSlots LDS slots
+    const uint16_t* local;
+    ItemMap m;
+    int item, end;        // next item to finish, end of the wave's range
+    int phase;            // 0..6: load peer `phase`; 7: load local; 8: local in flight; 9..: stores
+    int nst;              // stores per item (1, or 8 in an all-reduce run)
+    int ready_tile;       // the last tile seen flagged (-1: none)
+    int poll_tile;        // tile of the poll in flight (-1: none)
+    int poll_wait;        // steps before the next poll may be issued
+    int slot;             // slot of the next operation
+    int q[kStreamQueue];  // operations in flight, oldest first (kSoNone: none)
+    int nissued;          // vector-memory instructions the last step issued
+    uint32_t soff;        // this lane's byte offset of the item's chunk (kOob: none)
+    uint32_t epoch;
+    int gw0, tw;          // the workgroup's first streaming wave, streaming waves in all
+    f32x8 acc;
+};
+
+// arr[i] for a wave-uniform i in 0..6, as a chain of selects: a switch would
+// merge the pointers through control flow, which the compiler may keep in
+// vector registers (and then wrap every buffer access of the loop in a
+// per-lane loop over its resource).
+template <class T>
+__device__ __forceinline__ T pick7(T const (&arr)[kPeers], int i)
+{
+    T r = arr[0];
+#pragma unroll
+    for (int k = 1; k < kPeers; ++k) r = i == k ? arr[k] : r;
+    return r;
+}
+
+__device__ __forceinline__ void stream_item_start(Stream& s, const Args& a)
+{
+    s.phase = 0;
+    s.soff = s.item < s.end ? item_boff(s.m, a, s.item) : kOob;
+}
+
+// Streaming wave gw of tw (gw0: the workgroup's first); a wave that does not
+// stream passes active = false and gets an empty range.
+__device__ __forceinline__ void stream_init(Stream& s, const Args& a, char* slots, int gw0, int gw, int tw,
+                                            bool active, uint32_t epoch)
+{
+    s.slots = slots;
+    s.local = a.dst[a.g.rank];
+    s.m = item_map(a);
+    s.gw0 = gw0;
+    s.tw = tw;
+    const int64_t n = s.m.nitems;
+    s.item = active ? uni((int)(n * gw / tw)) : 0;
+    s.end = active ? uni((int)(n * (gw + 1) / tw)) : 0;
+    s.nst = a.gather_on ? 1 + kPeers : 1;
+    s.ready_tile = -1;
+    s.poll_tile = -1;
+    s.poll_wait = 0;
+    s.slot = 0;
+#pragma unroll
+    for (int i = 0; i < kStreamQueue; ++i) s.q[i] = kSoNone;
+    s.nissued = 0;
+    // (the epoch comes from an LDS read: make it provably uniform, so that
+    // the whole stream state stays in scalar registers)
+    s.epoch = (uint32_t)uni((int)epoch);
+    s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    stream_item_start(s, a);
+}
+
+// Operation code: kind | slot << 4 | peer << 8.
+__device__ __forceinline__ void stream_consume(Stream& s, int code)
+{
+    const int kind = code & 15;
+    if (kind == kSoNone) return;
+    const char* slot = s.slots + ((code >> 4) & 7) * 1024;
+    if (kind == kSoPoll) {
+        const uint32_t f = (uint32_t)uni((int)*reinterpret_cast<const uint32_t*>(slot));
+        if (f == s.epoch)
+            s.ready_tile = s.poll_tile;
+        else
+            s.poll_wait = kStreamBackoff;
+        s.poll_tile = -1;
+        return;
+    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(slot + (threadIdx.x & 63) * 16);
+    if (kind == kSoPeer && (code >> 8) == 0) s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    s.acc = add8(s.acc, v);
+    if (kind == kSoLocal) s.phase = 9;
+}
+
+// Issues the next operation, if any; returns its code (kSoNone when nothing
+// was issued).
+__device__ __forceinline__ int stream_issue(Stream& s, const Args& a)
+{
+    char* slot = s.slots + s.slot * 1024;
+    const uint32_t off = s.soff == kOob ? 0u : s.soff >> 1;  // element offset of a valid chunk
+    int code = kSoNone;
+    bool issued = false;
+    if (s.item < s.end) {
+        const int tile = s.item >> s.m.ipt_log2;
+        const bool ready = tile == s.ready_tile;
+        if (!ready && s.poll_tile < 0 && s.poll_wait == 0 && (s.phase == 0 || s.phase == 7)) {
+            lds_load_flag(a.flags + (int64_t)(a.g.rank * a.g.ts + tile) * a.flag_stride, slot);
+            s.poll_tile = tile;
+            code = kSoPoll;
+            issued = true;
+        } else if (s.phase < 7) {
+            lds_load16<kAuxNt>(pick7(a.peers, s.phase) + off, slot);
+            code = kSoPeer | (s.phase << 8);
+            ++s.phase;
+            issued = true;
+        } else if (s.phase == 7 && ready) {
+            lds_load16<kAuxSc1>(s.local + off, slot);
+            code = kSoLocal;
+            s.phase = 8;
+            issued = true;
+        } else if (s.phase >= 9) {
+            const u32x4 v = pack8(s.acc);
+            uint16_t* dst = s.phase == 9 ? a.out : pick7(a.gather, s.phase - 10);
+            __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(dst, 0, a.slice_bytes, kRsrcFlags),
+                                                   s.soff, 0, kAuxNt);
+            issued = true;
+            if (++s.phase == 9 + s.nst) {
+                ++s.item;
+                stream_item_start(s, a);
+            }
+        }
+    }
+    if (!issued) return kSoNone;
+    ++s.nissued;
+    code |= s.slot << 4;
+    s.slot = s.slot == kStreamSlots - 1 ? 0 : s.slot + 1;
+    return code;
+}
+
+// One K step of the stream, after the step's refill: kStreamOps times,
+// consume the operation issued two steps ago and issue the next.  Nothing
+// runs once the wave's items are done and nothing is in flight.
+__device__ __forceinline__ void stream_step(Stream& s, const Args& a)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    bool busy = s.item < s.end;
+#pragma unroll
+    for (int i = 0; i < kStreamQueue; ++i) busy = busy || s.q[i] != kSoNone;
+    s.nissued = 0;
+    if (busy) {
+        if (s.poll_wait > 0) --s.poll_wait;
+#pragma unroll
+        for (int k = 0; k < kStreamOps; ++k) {
+            stream_consume(s, s.q[0]);
+#pragma unroll
+            for (int i = 0; i + 1 < kStreamQueue; ++i) s.q[i] = s.q[i + 1];
+            s.q[kStreamQueue - 1] = stream_issue(s, a);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait for the stage refill issued by the previous step, letting the stream
+// instructions issued after it stay in flight.
+template <int B>
+__device__ __forceinline__ void stream_wait(const Stream& s)
+{
+    static_assert(kStreamOps <= 2, "wait counts below");
+    if (s.nissued == 0)
+        wait_vmcnt<B>();
+    else if (s.nissued == 1)
+        wait_vmcnt<B + 1>();
+    else
+        wait_vmcnt<B + 2>();
+}
+
+// After a wait for every vector-memory instruction: consume what is in flight.
+__device__ __forceinline__ void stream_settle(Stream& s)
+{
+#pragma unroll
+    for (int i = 0; i < kStreamQueue; ++i) {
+        stream_consume(s, s.q[i]);
+        s.q[i] = kSoNone;
+    }
+    s.nissued = 0;
+}
+
+// After the last tile, in every wave of the workgroup: the items the streaming
+// waves have not finished (an item in progress restarts) are split between
+// each streaming wave w and the waves w + SW, w + 2 SW, ... on its SIMD.
+// `progress` is an LDS array of SW entries; called by all waves, it holds one
+// workgroup barrier.
+template <int WAVES>
+__device__ __forceinline__ void stream_drain(const Stream& s, const Args& a, int wave, int* progress)
+{
+    constexpr int SW = WAVES / kStreamOps;
+    if (wave < SW && (threadIdx.x & 63) == 0) progress[wave] = s.item;
+    __syncthreads();
+    const int w = wave % SW, part = wave / SW;
+    const int64_t n = s.m.nitems;
+    const int gw = s.gw0 + w;
+    const int end = (int)(n * (gw + 1) / s.tw);
+    const int cur = uni(progress[w]);
+    ItemMap m = s.m;
+    m.nitems = cur + (end - cur) * (part + 1) / kStreamOps;
+    drain_items<2>(a, m, cur + (end - cur) * part / kStreamOps, 1, s.epoch);
+}
+
 // ---------------------------------------------------------------- tile loop
 
 // Per-tile state shared by the K loop and the role loop.
@@ -1046,12 +1281,18 @@ __device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
 // stage waited for (stages of the prologue).  The first barrier that covers
 // those stores (the one waiting for stage NS-1, the first refill) publishes
 // the previous tile's flag.
-template <class C>
+//
+// With STREAM every step also runs one step of the reduce stream after its
+// refill (and its sched barriers keep those instructions younger than every
+// load of the refill), so a step's wait allows as many more outstanding
+// instructions as the previous step's stream issued.
+template <class C, bool STREAM>
 __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
-                                              StepHooks& hk)
+                                              StepHooks& hk, Stream& rs)
 {
     static_assert(C::KSUB % 2 == 0, "substep s of every step uses fragment buffer s % 2");
     static_assert(C::EW == 0, "every wave loads stages");
+    static_assert(!STREAM || C::NS == 2, "the reduce stream's wait counts assume two stages");
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -1090,10 +1331,14 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
                 }
-            if (hk.stores && kt + 1 < C::NS - 1)
+            if constexpr (STREAM) {
+                // (the previous step's stream instructions may stay in flight)
+                stream_wait<B>(rs);
+            } else if (hk.stores && kt + 1 < C::NS - 1) {
                 wait_vmcnt<B + C::STORES>();
-            else
+            } else {
                 wait_vmcnt<B>();
+            }
             wait_lgkm0();
             stage_barrier();
             if (kt + 1 == C::NS - 1) publish_pending(a, hk);
@@ -1114,6 +1359,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
                 if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
             __builtin_amdgcn_s_setprio(0);
+            if constexpr (STREAM) stream_step(rs, a);
         }
         // the last step
         const char* cur = lds + ((nk - 1) % C::NS) * C::STAGE_BYTES;
@@ -1128,6 +1374,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
     // (nk < NS) is published here
     wait_vmcnt<0>();
     stage_barrier();
+    if constexpr (STREAM) stream_settle(rs);
     publish_pending(a, hk);
 }
 
@@ -1154,13 +1401,19 @@ __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int gr
 // the next tile's waits have covered the tile's stores: publishing costs no
 // extra wait.  Loader and engine waves run the same loop (the same barriers);
 // engine waves also run the reduce engine.
-template <class C, bool FUSED, bool LOADER>
+template <class C, bool FUSED, bool LOADER, bool STREAM>
 __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos, uint32_t who, uint32_t epoch,
                                               bool interleave)
 {
     const int Ctot = a.num_compute;
     const int wave = uni((int)(threadIdx.x >> 6));
     Engine eng;
+    Stream rs;
+    if constexpr (STREAM) {
+        constexpr int SW = C::WAVES / kStreamOps;  // streaming waves
+        stream_init(rs, a, lds + C::LDS_BYTES + (wave % SW) * kStreamLds, pos * SW, pos * SW + wave % SW,
+                    Ctot * SW, wave < SW, epoch);
+    }
     if constexpr (!LOADER) {
         const int ew = wave - C::LW;
         engine_init(eng, a, lds + C::LDS_BYTES + ew * kEngAreas * kEngAreaBytes, pos * C::EW + ew, Ctot * C::EW,
@@ -1185,7 +1438,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     }
     while (q < a.g.tiles) {
         if constexpr (C::XP)
-            tile_kloop_xp<C>(a, lds, st, job, hk);
+            tile_kloop_xp<C, STREAM>(a, lds, st, job, hk, rs);
         else
             tile_kloop<C, LOADER>(a, lds, st, job, hk, eng);
         // issue the next tile's first stages before this tile's stores
@@ -1218,7 +1471,11 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         stage_barrier();
         if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
-    if (interleave) {
+    if constexpr (STREAM) {
+        // the items the stream has not finished
+        __shared__ int s_progress[C::WAVES / kStreamOps];
+        stream_drain<C::WAVES>(rs, a, wave, s_progress);
+    } else if (interleave) {
         if (hk.interleave) {
             // in-loop slots: the engine waves own the items
             if constexpr (!LOADER) engine_drain(eng, a);
@@ -1235,18 +1492,18 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
 // Compute role of the l-th compute workgroup of group grp: its position in a
 // round is either the group's block offset + l (contiguous split) or
 // l * 8 + grp (strided, used when all C_x are equal).
-template <class C, bool FUSED>
+template <class C, bool FUSED, bool STREAM>
 __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, int l, uint32_t epoch, int base)
 {
-    const int pos = a.strided ? (l * kGroups + grp) : (base + l);
+    const int pos = uni(a.strided ? (l * kGroups + grp) : (base + l));
     const uint32_t who = ((uint32_t)grp << 16) | (uint32_t)l;
     // without dedicated reducers the compute workgroups reduce the slice
     const bool interleave = FUSED && a.num_reducers == 0;
     const int wave = uni((int)(threadIdx.x >> 6));
     if (C::EW == 0 || wave < C::LW)
-        compute_waves<C, FUSED, true>(a, lds, pos, who, epoch, interleave);
+        compute_waves<C, FUSED, true, STREAM>(a, lds, pos, who, epoch, interleave);
     else if constexpr (C::EW > 0)
-        compute_waves<C, FUSED, false>(a, lds, pos, who, epoch, interleave);
+        compute_waves<C, FUSED, false, false>(a, lds, pos, who, epoch, interleave);
 }
 
 // Dedicated reducer role (used when reducers are requested): claim own-slice
@@ -1328,7 +1585,7 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
 // launch stored the same value, so all workgroups of a launch agree on its
 // epoch without communicating (the words change only at kernel ends).  A
 // GEMM-only launch has no flags and touches none of this.
-template <class C, bool FUSED>
+template <class C, bool FUSED, bool STREAM = false>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1341,11 +1598,13 @@ __device__ __forceinline__ void fused_body(const Args& a)
                         : 0u;
     }
     __syncthreads();
-    const uint32_t ticket = s_ticket;
-    const uint32_t epoch = s_epoch + 1u;  // value this run's flags carry
-    const GroupSplit split = group_split((int)gridDim.x, a.num_reducers, grp);
+    // (read through readfirstlane so that the compiler sees them uniform: the
+    // tile loop and the reduce stream then stay in scalar registers)
+    const uint32_t ticket = (uint32_t)uni((int)s_ticket);
+    const uint32_t epoch = (uint32_t)uni((int)s_epoch) + 1u;  // value this run's flags carry
+    const GroupSplit split = group_split((int)gridDim.x, uni(a.num_reducers), grp);
     if (ticket < (uint32_t)split.compute)
-        compute_role<C, FUSED>(a, lds, grp, (int)ticket, epoch, split.base);
+        compute_role<C, FUSED, STREAM>(a, lds, grp, (int)ticket, epoch, split.base);
     else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers)
         reducer_role(a, epoch);
 
@@ -1380,10 +1639,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // Eight-wave workgroups (one per CU): two waves per SIMD, so one wave's
 // MFMAs run while its sibling waits on LDS, a barrier or the reduce engine.
-template <class C, bool FUSED>
+template <class C, bool FUSED, bool STREAM = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel_8w(Args a)
 {
-    fused_body<C, FUSED>(a);
+    fused_body<C, FUSED, STREAM>(a);
 }
 
 // Large tiles run one workgroup (one wave per SIMD) per CU: let the compiler

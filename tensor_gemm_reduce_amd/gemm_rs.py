@@ -38,6 +38,11 @@ TILE_256x128 = 5
 TILE_256x256 = 6
 TILES = {"auto": 0, "16x64": 1, "64x128": 2, "128x128": 3, "128x256": 4, "256x128": 5, "256x256": 6}
 
+REDUCE_AUTO = 0
+REDUCE_TAIL = 1
+REDUCE_STREAM = 2
+REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2}
+
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
@@ -51,14 +56,15 @@ class gemm_rs_config(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("num_reducers", ctypes.c_int32),
                 ("engine_interval", ctypes.c_int32), ("debug_flags", ctypes.c_int32),
                 ("drop_flag", ctypes.c_int32), ("flag_stride", ctypes.c_int32),
-                ("watchdog_us", ctypes.c_int64)]
+                ("watchdog_us", ctypes.c_int64), ("reduce_mode", ctypes.c_int32)]
 
 
 class gemm_rs_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bm", "bn", "bk", "group_m", "tiles", "tiles_per_slice", "tile_rows_per_slice",
         "tile_cols", "grid", "compute_wgs", "reducer_wgs", "num_cus", "wgs_per_cu",
-        "lds_bytes", "reduce_grid", "xcd_split")] + [("epoch", ctypes.c_uint32)]
+        "lds_bytes", "reduce_grid", "xcd_split")] + [("epoch", ctypes.c_uint32),
+                                                     ("reduce_mode", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -122,11 +128,13 @@ def _check(code: int, what: str) -> int:
 
 def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_reducers=-1,
                 engine_interval=0, debug_flags=0, drop_flag=-1, flag_stride=1,
-                watchdog_us=0) -> gemm_rs_config:
+                watchdog_us=0, reduce_mode=REDUCE_AUTO) -> gemm_rs_config:
     if isinstance(tile, str):
         tile = TILES[tile]
+    if isinstance(reduce_mode, str):
+        reduce_mode = REDUCE_MODES[reduce_mode]
     return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers, engine_interval,
-                          debug_flags, drop_flag, flag_stride, watchdog_us)
+                          debug_flags, drop_flag, flag_stride, watchdog_us, reduce_mode)
 
 
 # ---- C names ------------------------------------------------------------------

@@ -75,6 +75,14 @@ def cfg(**kw):
     (dict(drop_flag=100000), gr.ERR_INVALID_ARG),
     (dict(num_reducers=-2), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=3), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=-1), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream"), gr.OK),
+    (dict(reduce_mode="tail"), gr.OK),
+    (dict(reduce_mode="stream", num_reducers=8), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream", engine_interval=2), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream", tile="128x128"), gr.ERR_UNSUPPORTED_SHAPE),
+    (dict(reduce_mode="stream", M=512, K_local=1024), gr.ERR_UNSUPPORTED_SHAPE),
     (dict(M=0), gr.OK),
     (dict(K_local=0), gr.OK),
 ])
@@ -124,6 +132,19 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
         assert 0 <= r0 and r0 + rows <= (d + 1) * S <= M
         assert 0 <= tml * bm and tml * bm + rows <= S   # rows of the slice buffer
         assert 0 <= tn * bn and tn * bn + cols <= N
+
+
+@pytest.mark.parametrize("kw,mode", [
+    (dict(), gr.REDUCE_TAIL),                        # automatic: the sum after the last tile
+    (dict(reduce_mode="stream"), gr.REDUCE_STREAM),  # 256x256 tile
+    (dict(reduce_mode="tail"), gr.REDUCE_TAIL),
+    (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
+    (dict(engine_interval=2), gr.REDUCE_TAIL),
+    (dict(tile="128x128"), gr.REDUCE_TAIL),           # no stream for this tile
+    (dict(M=512, K_local=1024), gr.REDUCE_TAIL),     # o_proj: 64x128 tile
+])
+def test_plan_resolves_reduce_mode(kw, mode):
+    assert gr.gemm_rs_plan(cfg(**kw)).reduce_mode == mode
 
 
 def test_plan_resolves_auto_tile():

@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 REDUCE = {"engine_tail": dict(num_reducers=0), "engine_loop1": dict(num_reducers=0, engine_interval=1),
           "engine_loop3": dict(num_reducers=0, engine_interval=3), "reducers8": dict(num_reducers=8)}
 REDUCERS = list(REDUCE)
+# the sum streamed through the K loop (256x256 tile only; the automatic choice
+# sums after the last tile)
+REDUCE["stream"] = dict(num_reducers=0, reduce_mode="stream")
 
 
 def _op(cfg, M=None, **kw):
@@ -160,12 +163,14 @@ def test_error_within_1p1x_of_unfused_path(name, mode):
 
 # ------------------------------------------------------------------ full shapes, sampled rows
 
-@pytest.mark.parametrize("red", ["bench", "engine_loop3", "reducers8"])
+@pytest.mark.parametrize("red", ["bench", "stream", "engine_loop3", "reducers8"])
 @pytest.mark.parametrize("name", ["o_proj", "down_proj", "mixtral_down", "large_prefill"])
 @pytest.mark.parametrize("mode", ["normal", "integer"])
 def test_benchmark_shapes_sampled_rows(name, mode, red):
     # "bench": the launch configuration the benchmark times
     cfg = synthetic.CONFIGS[name]
+    if red == "stream" and name == "o_proj":
+        pytest.skip("the reduce stream needs the 256x256 tile (o_proj has 64-row slices)")
     rank = 5
     x, w, peers = synthetic.make_inputs(cfg, mode)
     op = _op(cfg, rank=rank, **({} if red == "bench" else REDUCE[red]))
