@@ -99,6 +99,13 @@ extern "C" {
 #define GEMM_RS_REDUCE_STREAM 2 /* every wave streams its share through the K loop:
                                    one load or store of the sum per K step, issued
                                    behind the stage refill (256x256 tile only)    */
+#define GEMM_RS_REDUCE_CORESIDENT 3 /* one reducer workgroup per CU beside the
+                                   compute workgroups (tiles whose kernel fits one
+                                   more workgroup per CU, else gemm_rs_create gives
+                                   GEMM_RS_ERR_UNSUPPORTED_SHAPE); each reducer wave
+                                   sums the peers of its items while the GEMM runs,
+                                   then adds the local chunk once the tile's flag
+                                   is set                                          */
 
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
@@ -123,8 +130,9 @@ typedef struct gemm_rs_config {
     int32_t flag_stride;  /* 32-bit words between ready flags (1 or 32)       */
     int64_t watchdog_us;  /* reducer wait limit per tile in microseconds;
                              0 = default (2 000 000)                          */
-    int32_t reduce_mode;  /* GEMM_RS_REDUCE_*; STREAM needs num_reducers <= 0,
-                             engine_interval == 0 and the 256x256 tile        */
+    int32_t reduce_mode;  /* GEMM_RS_REDUCE_*; STREAM and CORESIDENT need
+                             num_reducers <= 0 and engine_interval == 0;
+                             STREAM needs the 256x256 tile                    */
 } gemm_rs_config;
 
 typedef struct gemm_rs_info {

@@ -165,6 +165,7 @@ struct gemm_rs_handle {
     int num_cus;
     int wgs_per_cu;
     int fused_lds;
+    int gemm_grid;         // workgroups of a GEMM-only launch
     int reduce_mode;       // resolved GEMM_RS_REDUCE_* (TAIL when reducers or engine slots run the sum)
     int grid;
     int compute_wgs;
@@ -230,9 +231,10 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
     if (c->watchdog_us < 0) return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_STREAM)
+    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_CORESIDENT)
         return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM && (c->num_reducers > 0 || c->engine_interval > 0))
+    if ((c->reduce_mode == GEMM_RS_REDUCE_STREAM || c->reduce_mode == GEMM_RS_REDUCE_CORESIDENT) &&
+        (c->num_reducers > 0 || c->engine_interval > 0))
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->tp != 8) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->M % c->tp != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
@@ -374,7 +376,15 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     // a whole number of workgroups per XCD group
     h->grid = (h->num_cus * h->wgs_per_cu) / kGroups * kGroups;
     if (h->grid < kGroups) h->grid = kGroups;
+    h->gemm_grid = h->grid;
     int red = red_req;
+    if (h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT) {
+        // one more workgroup per CU, which must fit beside the compute ones
+        if (occ < h->wgs_per_cu + 1) { delete h; return GEMM_RS_ERR_UNSUPPORTED_SHAPE; }
+        red = h->num_cus / kGroups * kGroups;
+        h->grid += red;
+        h->wgs_per_cu += 1;
+    }
     if (red >= h->grid) red = h->grid - 1;
     h->reducer_wgs = red;
     h->compute_wgs = h->grid - red;
@@ -441,6 +451,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.drop_flag = h->cfg.drop_flag;
     a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
     a.engine_every = h->cfg.engine_interval;
+    a.coresident = h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT ? 1 : 0;
 }
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
@@ -460,7 +471,11 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
                   : stream ? h->td.stream_kernel
                   : fused  ? h->td.kernel
                            : h->td.gemm_kernel;
-    HIP_TRY(hipLaunchKernel(k, dim3(h->grid), dim3(h->td.threads), params, fused ? h->fused_lds : h->td.lds_bytes, s));
+    // (a GEMM-only launch runs on the compute workgroups' grid: the
+    // co-resident reducers' extra workgroup per CU is not part of the GEMM)
+    if (!fused) a.num_compute = h->gemm_grid;
+    HIP_TRY(hipLaunchKernel(k, dim3(fused ? h->grid : h->gemm_grid), dim3(h->td.threads), params,
+                            fused ? h->fused_lds : h->td.lds_bytes, s));
     return GEMM_RS_OK;
 }
 

@@ -112,6 +112,8 @@ struct Args {
     int32_t drop_flag;
     int32_t trace_on;
     int32_t engine_every;    // K steps between reduce-engine slots (0: reduce after the last tile)
+    int32_t coresident;      // 1: the reducer workgroups sit beside the compute workgroups of
+                             // their CUs and sum a static share of items (peers first)
 };
 
 // BM x BN output tile, BK deep stages, NS stages in LDS, WAVES_M x WAVES_N
@@ -826,6 +828,7 @@ __device__ __forceinline__ void engine_step(Engine& e, const Args& a, bool start
 // first wait that exceeds the watchdog limit reports the tile and sets
 // gave_up; after that no wait blocks, so a drain never waits longer than one
 // watchdog period in total.
+template <int SLEEP = 2>
 __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, bool& gave_up)
 {
     const int flag = a.g.rank * a.g.ts + t;
@@ -834,7 +837,7 @@ __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, 
     if (gave_up) return false;
     const uint64_t t0 = wall_clock64();
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(SLEEP);
         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
             gave_up = true;
             if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
@@ -850,7 +853,8 @@ __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, 
 // checked (they need none), then its local chunks, in the sum order.  A tile
 // whose flag does not arrive within the watchdog limit is reported and its
 // items are skipped.
-template <int BATCH>
+// SLEEP: s_sleep argument between flag polls (64 clocks each).
+template <int BATCH, int SLEEP = 2>
 __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int first, int stride, uint32_t epoch)
 {
     constexpr int kDrainBatch = BATCH;
@@ -873,7 +877,7 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
 #pragma unroll
         for (int b = 0; b < kDrainBatch; ++b) {
             const int item = base + b * stride;
-            const bool ok = item < m.nitems && wait_tile(a, epoch, item >> m.ipt_log2, gave_up);
+            const bool ok = item < m.nitems && wait_tile<SLEEP>(a, epoch, item >> m.ipt_log2, gave_up);
             boff[b] = ok ? boff[b] : kOob;
             v[b][kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, boff[b], 0, kAuxSc1));
         }
@@ -1383,6 +1387,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
 // to C = G - R whatever R is.
 struct GroupSplit {
     int compute, reducers, base;  // base: first position of the group in a round
+    int rbase;                    // index of the group's first reducer among all R
 };
 
 __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int grp)
@@ -1393,6 +1398,7 @@ __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int gr
     s.reducers = rq + (grp < rr ? 1 : 0);
     s.compute = gq - s.reducers;
     s.base = grp * (gq - rq) - (grp < rr ? grp : rr);
+    s.rbase = grp * rq + (grp < rr ? grp : rr);
     return s;
 }
 
@@ -1591,7 +1597,10 @@ __device__ __forceinline__ void fused_body(const Args& a)
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ uint32_t s_ticket, s_epoch;
     const int grp = blockIdx.x % kGroups;
-    const bool tickets = FUSED && a.num_reducers > 0;
+    // co-resident reducers take their role from their index (the whole grid
+    // fits on the device at once, and compute workgroups never wait for
+    // reducers), so they need no tickets
+    const bool tickets = FUSED && a.num_reducers > 0 && !a.coresident;
     if (threadIdx.x == 0) {
         s_ticket = tickets ? atomicAdd(&a.state->role[grp], 1u) : (uint32_t)(blockIdx.x / kGroups);
         s_epoch = FUSED ? __hip_atomic_load(a.finished + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
@@ -1605,8 +1614,18 @@ __device__ __forceinline__ void fused_body(const Args& a)
     const GroupSplit split = group_split((int)gridDim.x, uni(a.num_reducers), grp);
     if (ticket < (uint32_t)split.compute)
         compute_role<C, FUSED, STREAM>(a, lds, grp, (int)ticket, epoch, split.base);
-    else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers)
-        reducer_role(a, epoch);
+    else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers) {
+        if (a.coresident) {
+            // reducer r of R owns items r*W + wave, + R*W, ...: its peer chunks
+            // are loaded and summed while the GEMM runs, before the flags are
+            // checked; once a tile is flagged only its local chunks remain
+            const int r = split.rbase + (int)(ticket - (uint32_t)split.compute);
+            const int wave = uni((int)(threadIdx.x >> 6));
+            drain_items<2, 1>(a, item_map(a), r * C::WAVES + wave, uni(a.num_reducers) * C::WAVES, epoch);
+        } else {
+            reducer_role(a, epoch);
+        }
+    }
 
     if constexpr (FUSED) {
         __syncthreads();

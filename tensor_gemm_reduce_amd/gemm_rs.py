@@ -41,7 +41,8 @@ TILES = {"auto": 0, "16x64": 1, "64x128": 2, "128x128": 3, "128x256": 4, "256x12
 REDUCE_AUTO = 0
 REDUCE_TAIL = 1
 REDUCE_STREAM = 2
-REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2}
+REDUCE_CORESIDENT = 3
+REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2, "coresident": 3}
 
 DEBUG_TRACE = 1
 

@@ -75,7 +75,10 @@ def cfg(**kw):
     (dict(drop_flag=100000), gr.ERR_INVALID_ARG),
     (dict(num_reducers=-2), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode=3), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=4), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="coresident"), gr.OK),
+    (dict(reduce_mode="coresident", num_reducers=8), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="coresident", engine_interval=1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=-1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="stream"), gr.OK),
     (dict(reduce_mode="tail"), gr.OK),
@@ -138,6 +141,7 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
     (dict(), gr.REDUCE_TAIL),                        # automatic: the sum after the last tile
     (dict(reduce_mode="stream"), gr.REDUCE_STREAM),  # 256x256 tile
     (dict(reduce_mode="tail"), gr.REDUCE_TAIL),
+    (dict(reduce_mode="coresident"), gr.REDUCE_CORESIDENT),
     (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
     (dict(engine_interval=2), gr.REDUCE_TAIL),
     (dict(tile="128x128"), gr.REDUCE_TAIL),           # no stream for this tile
