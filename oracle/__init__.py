@@ -244,3 +244,28 @@ def schedule(M: int, N: int, tp: int, rank: int, bm: int, bn: int, group_m: int)
                                  _ptr(out["tm"], _i32p), _ptr(out["tn"], _i32p),
                                  _ptr(out["flag"], _i32p)), "oracle_schedule")
     return out
+
+
+def gemm_ag(x_slices, w: np.ndarray):
+    """AllGather + GEMM for one rank of a column-parallel linear layer.
+
+    FLUX ("FLUX: Fast Software-based Communication Overlap On GPUs Through
+    Kernel Fusion", TL;DR) fuses the all-gather into the GEMM as its prologue;
+    mKernel ("mKernel: Fast Multi-GPU, Multi-Node Fused Kernels", Section 4)
+    computes the local shard's tiles first and the other shards as they
+    arrive.  Neither changes what is computed: every rank gathers the tp row
+    slices of the activations, rank d's slice at rows d*S .. d*S + S - 1, and
+    multiplies the gathered matrix by its own column shard of the weight.
+
+    x_slices: tp arrays [S][K] (BF16 bits) in source-rank order; w: [N][K]
+    (this rank's column shard, K contiguous).  Returns (x_gathered [tp*S][K],
+    y [tp*S][N]) with y = RNE_bf16(x_gathered * w^T), FP32 accumulation with k
+    ascending (gemm_f32acc)."""
+    xs = [_c(x, np.uint16) for x in x_slices]
+    S, K = xs[0].shape
+    for x in xs:
+        if x.shape != (S, K):
+            raise ValueError("row slices differ in shape")
+    xg = np.concatenate(xs, axis=0)
+    y = f32_to_bf16(gemm_f32acc(xg, w))
+    return xg, y

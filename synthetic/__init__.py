@@ -166,3 +166,74 @@ def small_case(M: int, N: int, K_local: int, tp: int = 8, mode: str = "normal", 
     """Inputs for an arbitrary small shape (odd sizes, ragged tails) with a fixed seed."""
     cfg = Config(f"case_{M}x{N}x{K_local}", 90 + (s % 9), M, N, K_local, tp)
     return cfg, make_inputs(cfg, mode)
+
+
+# ---- all-gather + GEMM (the column-parallel layer before the row-parallel one)
+
+@dataclasses.dataclass(frozen=True)
+class AgConfig:
+    """One rank's share of a column-parallel layer at TP degree tp: the
+    gathered activations are M x K (tp row slices of S = M / tp rows), the
+    weight shard is N x K (N = this rank's output columns)."""
+    name: str
+    index: int
+    M: int
+    N: int
+    K: int
+    tp: int = 8
+    description: str = ""
+
+    @property
+    def S(self) -> int:
+        return self.M // self.tp
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def gather_bytes(self) -> int:
+        # the tp-1 peer slices read and written into the gathered buffer, BF16
+        return 2 * (self.tp - 1) * self.S * self.K * 2
+
+
+# The layers that feed each benchmark shape's row-parallel layer in the same
+# model: Llama-3-70B's fused q/k/v projection (64 query and 2 x 8 key/value
+# heads of 128: N = 10240 / 8) before o_proj, its fused gate/up projection
+# (2 x 28672 / 8) before down_proj, and Mixtral-8x22B's expert w1/w3
+# (2 x 16384 / 8) before its down projection.
+AG_CONFIGS = {
+    c.name: c
+    for c in [
+        AgConfig("ag_tiny", 10, 128, 512, 256,
+                 description="tiny all-gather + GEMM: M=128 N=512 K=256, spans several tiles"),
+        AgConfig("ag_qkv", 11, 512, 1280, 8192,
+                 description="Llama-3-70B q/k/v projection column-parallel, one rank of TP=8"),
+        AgConfig("ag_gate_up", 12, 2048, 7168, 8192,
+                 description="Llama-3-70B gate/up projection column-parallel, one rank of TP=8"),
+        AgConfig("ag_mixtral_w13", 13, 8192, 4096, 6144,
+                 description="Mixtral-8x22B-shaped expert w1/w3 column-parallel, one rank of TP=8"),
+        AgConfig("ag_large_prefill", 14, 32768, 7168, 8192,
+                 description="large prefill, Llama-3-70B gate/up shape, one rank of TP=8"),
+    ]
+}
+
+
+def make_ag_inputs(cfg: AgConfig, mode: str = "normal", M: int | None = None):
+    """(x_slices, w): tp row slices [S][K] in source-rank order and this rank's
+    column shard [N][K] of the weight.  Normal mode: N(0, 1) / sqrt(K) for
+    both; integer mode: uniform in {-2..2}.  Seeds: tid 60 + d for slice d,
+    tid 70 for the weight."""
+    M = cfg.M if M is None else M
+    S = M // cfg.tp
+    if mode == "integer":
+        xs = [_ints(seed(cfg, 60 + d), (S, cfg.K), -2, 2) for d in range(cfg.tp)]
+        w = _ints(seed(cfg, 70), (cfg.N, cfg.K), -2, 2)
+    elif mode == "normal":
+        scale = 1.0 / math.sqrt(cfg.K)
+        xs = [_normal(seed(cfg, 60 + d), (S, cfg.K), scale) for d in range(cfg.tp)]
+        w = _normal(seed(cfg, 70), (cfg.N, cfg.K), scale)
+    else:
+        raise ValueError(mode)
+    return xs, w
+
