@@ -220,6 +220,33 @@ int gemm_rs_run_allreduce(gemm_rs_handle *h, int32_t mode, const void *x, const 
                           void *const *send, const void *const *peers, void *out,
                           void *local_slice, void *const *gather, void *stream);
 
+/* All-gather + GEMM: the column-parallel linear layer that precedes the
+ * row-parallel one, with the all-gather fused as the GEMM's prologue (FLUX,
+ * "FLUX: Fast Software-based Communication Overlap On GPUs Through Kernel
+ * Fusion", TL;DR; mKernel, "mKernel: Fast Multi-GPU, Multi-Node Fused
+ * Kernels", Section 4: the local shard's tiles first, the others as their rows
+ * arrive).  The handle's config is read as: M gathered rows (tp row slices of
+ * S = M / tp), N this rank's output columns, K_local the layer's reduction
+ * length K (the activations are not sharded along K).
+ *   x_slices    host array of tp device pointers, in source-rank order, each
+ *               [S][K] BF16: x_slices[rank] is this rank's own row slice, the
+ *               others stand in for what the peers send.
+ *   w           [N][K] BF16, this rank's column shard of the weight.
+ *   x_gathered  [M][K] BF16 output: the gathered activations, slice d at rows
+ *               d*S .. d*S + S - 1.
+ *   y           [M][N] BF16 output: RNE(x_gathered * w^T), FP32 accumulation.
+ * Modes: FUSED is one persistent launch: every workgroup copies its share of
+ * the slices into x_gathered (in the order the tiles need them) and bumps a
+ * per-block counter, then runs the GEMM; tiles of this rank's slice start at
+ * once, the others wait for their rows.  GEMM_ONLY runs the GEMM over an
+ * already complete x_gathered (only x_slices[rank] is read); REDUCE_ONLY runs
+ * the standalone all-gather copy alone; SEQUENTIAL runs the copy then the
+ * GEMM.  M * N * 2 must stay below 2^31 (else GEMM_RS_ERR_UNSUPPORTED_SHAPE).
+ * Ownership, alignment and errors as gemm_rs_run; a FUSED all-gather run may
+ * not overlap another run of the same handle on the device. */
+int gemm_rs_run_allgather(gemm_rs_handle *h, int32_t mode, const void *const *x_slices, const void *w,
+                          void *x_gathered, void *y, void *stream);
+
 /* Waits for the handle's last run and returns its device status:
  * GEMM_RS_OK, or GEMM_RS_ERR_TIMEOUT if a reducer gave up waiting for a ready
  * flag (the kernel still exits; `out` is then incomplete).  Reading the status

@@ -59,6 +59,8 @@ struct TileDesc {
     int stream_lds_bytes;      // its LDS: stages + the streaming waves' slots
     const void* kernel;        // fused: dedicated reducer workgroups
     const void* gemm_kernel;   // the same GEMM without flags or reduction
+    const void* ag_kernel;     // all-gather + GEMM: copy phase, then the GEMM waiting for rows
+    const void* ag_gemm_kernel;  // the same GEMM over an already gathered buffer
 };
 
 // Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
@@ -73,6 +75,17 @@ const void* kernel_for()
         return reinterpret_cast<const void*>(&fused_kernel<C, FUSED>);
     else
         return reinterpret_cast<const void*>(&fused_kernel_1w<C, FUSED>);
+}
+
+template <class C, bool FUSED, bool TWO_PER_CU>
+const void* ag_kernel_for()
+{
+    if constexpr (C::WAVES == 8)
+        return reinterpret_cast<const void*>(&ag_kernel_8w<C, FUSED>);
+    else if constexpr (TWO_PER_CU)
+        return reinterpret_cast<const void*>(&ag_kernel<C, FUSED>);
+    else
+        return reinterpret_cast<const void*>(&ag_kernel_1w<C, FUSED>);
 }
 
 template <class C, class CE>
@@ -91,7 +104,8 @@ TileDesc desc()
     if constexpr (stream) sk = reinterpret_cast<const void*>(&fused_kernel_8w<C, true, true>);
     return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, elds, C::LDS_BYTES,
                     kernel_for<CE, true, two>(), sk, stream ? slds : 0,
-                    kernel_for<C, true, two>(), kernel_for<C, false, two>()};
+                    kernel_for<C, true, two>(), kernel_for<C, false, two>(),
+                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>()};
 }
 
 TileDesc tile_desc(int id)
@@ -103,7 +117,7 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, 0, nullptr, nullptr};
+    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
     }
 }
 
@@ -166,6 +180,13 @@ struct gemm_rs_handle {
     int wgs_per_cu;
     int fused_lds;
     int gemm_grid;         // workgroups of a GEMM-only launch
+    // all-gather + GEMM runs
+    uint32_t* agflags;     // tp * tile rows per slice copy counters
+    uint32_t* agfinished;  // per workgroup of ag_grid
+    int ag_grid;
+    int ag_strided;
+    int ag_units;
+    uint32_t ag_unit_bytes;
     int reduce_mode;       // resolved GEMM_RS_REDUCE_* (TAIL when reducers or engine slots run the sum)
     int grid;
     int compute_wgs;
@@ -319,6 +340,8 @@ static void free_state(gemm_rs_handle* h)
     if (h->trace) (void)hipFree(h->trace);
     if (h->finished) (void)hipFree(h->finished);
     if (h->scratch) (void)hipFree(h->scratch);
+    if (h->agflags) (void)hipFree(h->agflags);
+    if (h->agfinished) (void)hipFree(h->agfinished);
 }
 
 int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
@@ -394,9 +417,35 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
                       xcd_footprint(h->g, h->grid, h->reducer_wgs, false))
                      ? 1 : 0;
 
+    // all-gather + GEMM launches: the compute grid of the same tile (no reducers)
+    for (const void* k : {h->td.ag_kernel, h->td.ag_gemm_kernel}) {
+        e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+        if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
+    }
+    int ag_occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&ag_occ, h->td.ag_kernel, h->td.threads, h->td.lds_bytes);
+    if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
+    {
+        const int per_cu = ag_occ < 1 ? 1 : (ag_occ > h->td.wgs_per_cu ? h->td.wgs_per_cu : ag_occ);
+        h->ag_grid = (h->num_cus * per_cu) / kGroups * kGroups;
+        if (h->ag_grid < kGroups) h->ag_grid = kGroups;
+    }
+    h->ag_strided = (h->g.tiles > 0 && xcd_footprint(h->g, h->ag_grid, 0, true) <
+                                           xcd_footprint(h->g, h->ag_grid, 0, false)) ? 1 : 0;
+    // copy units of 64 KiB: a tile-row block of BM rows is split into ag_units
+    h->ag_unit_bytes = 64u << 10;
+    {
+        const int64_t blk = (int64_t)h->g.bm * h->g.K * 2;
+        h->ag_units = (int)((blk + h->ag_unit_bytes - 1) / h->ag_unit_bytes);
+        if (h->ag_units < 1) h->ag_units = 1;
+    }
+    const size_t agblocks = (size_t)h->g.tp * (size_t)(h->g.tms > 0 ? h->g.tms : 1);
+
     const size_t tiles = (size_t)(h->g.tiles > 0 ? h->g.tiles : 1);
     const size_t slice = (size_t)h->g.S * (size_t)h->g.N;
-    if (hipMalloc(&h->flags, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
+    if (hipMalloc(&h->agflags, agblocks * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->agfinished, (size_t)h->ag_grid * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->flags, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->state, sizeof(DeviceState)) != hipSuccess ||
         hipMalloc(&h->trace, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->finished, (size_t)h->grid * sizeof(uint32_t)) != hipSuccess ||
@@ -405,7 +454,9 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
         delete h;
         return GEMM_RS_ERR_NO_MEMORY;
     }
-    if (hipMemset(h->flags, 0, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
+    if (hipMemset(h->agflags, 0, agblocks * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->agfinished, 0, (size_t)h->ag_grid * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->flags, 0, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
         hipMemset(h->state, 0, sizeof(DeviceState)) != hipSuccess ||
         hipMemset(h->trace, 0, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
         hipMemset(h->finished, 0, (size_t)h->grid * sizeof(uint32_t)) != hipSuccess ||
@@ -558,6 +609,73 @@ int gemm_rs_run_allreduce(gemm_rs_handle* h, int32_t mode, const void* x, const 
 {
     if (mode != GEMM_RS_MODE_GEMM_ONLY && !gather) return GEMM_RS_ERR_INVALID_ARG;
     return run_impl(h, mode, x, w, send, peers, out, local_slice, gather, stream);
+}
+
+int gemm_rs_run_allgather(gemm_rs_handle* h, int32_t mode, const void* const* x_slices, const void* w,
+                          void* x_gathered, void* y, void* stream)
+{
+    if (!h) return GEMM_RS_ERR_INVALID_ARG;
+    if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    h->last_stream = s;
+    if (h->g.S == 0) return GEMM_RS_OK;
+    // y [M][N] is written through a buffer resource with 31-bit byte offsets
+    if ((int64_t)h->g.M * h->g.N * 2 >= ((int64_t)1 << 31)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    const bool needs_copy = mode != GEMM_RS_MODE_GEMM_ONLY;
+    const bool needs_gemm = mode != GEMM_RS_MODE_REDUCE_ONLY;
+    if (!x_slices || !x_gathered) return GEMM_RS_ERR_INVALID_ARG;
+    if (!aligned16(x_gathered)) return GEMM_RS_ERR_MISALIGNED;
+    for (int d = 0; d < h->g.tp; ++d) {
+        // GEMM_ONLY reads only this rank's own slice (the rest from x_gathered)
+        if (!needs_copy && d != h->g.rank) continue;
+        if (!x_slices[d] && h->g.K > 0) return GEMM_RS_ERR_INVALID_ARG;
+        if (!aligned16(x_slices[d])) return GEMM_RS_ERR_MISALIGNED;
+    }
+    if (needs_gemm) {
+        if (!y || (!w && h->g.K > 0)) return GEMM_RS_ERR_INVALID_ARG;
+        if (!aligned16(y) || !aligned16(w)) return GEMM_RS_ERR_MISALIGNED;
+    }
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != h->device) return GEMM_RS_ERR_INVALID_ARG;
+
+    Args a;
+    memset(&a, 0, sizeof a);
+    a.w = static_cast<const uint16_t*>(w);
+    for (int d = 0; d < h->g.tp; ++d) a.xsrc[d] = static_cast<const uint16_t*>(x_slices[d]);
+    a.xg = static_cast<uint16_t*>(x_gathered);
+    a.y = static_cast<uint16_t*>(y);
+    a.agflags = h->agflags;
+    a.agfinished = h->agfinished;
+    a.state = h->state;
+    a.g = h->g;
+    a.x_bytes = (uint32_t)((int64_t)h->g.M * h->g.K * 2);
+    a.w_bytes = (uint32_t)((int64_t)h->g.N * h->g.K * 2);
+    a.xs_bytes = (uint32_t)((int64_t)h->g.S * h->g.K * 2);
+    a.y_bytes = (uint32_t)((int64_t)h->g.M * h->g.N * 2);
+    a.strided = h->ag_strided;
+    const int64_t us = h->cfg.watchdog_us > 0 ? h->cfg.watchdog_us : 2000000;
+    a.watchdog_ticks = us * 100;
+    a.ag_units = h->ag_units;
+    a.ag_unit_bytes = h->ag_unit_bytes;
+    a.num_compute = h->ag_grid;
+    void* params[] = {&a};
+    if (mode == GEMM_RS_MODE_FUSED) {
+        HIP_TRY(hipLaunchKernel(h->td.ag_kernel, dim3(h->ag_grid), dim3(h->td.threads), params, h->td.lds_bytes, s));
+        return GEMM_RS_OK;
+    }
+    if (needs_copy) {
+        const int64_t chunks = (int64_t)h->g.S * h->g.K / 8;
+        int64_t want = (chunks + kReduceThreads - 1) / kReduceThreads;
+        int grid = (int)(want < h->reduce_grid ? want : h->reduce_grid);
+        if (grid < 1) grid = 1;
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&ag_copy_kernel), dim3(grid), dim3(kReduceThreads),
+                                params, 0, s));
+    }
+    if (needs_gemm)
+        HIP_TRY(hipLaunchKernel(h->td.ag_gemm_kernel, dim3(h->ag_grid), dim3(h->td.threads), params, h->td.lds_bytes,
+                                s));
+    return GEMM_RS_OK;
 }
 
 int gemm_rs_status(gemm_rs_handle* h)

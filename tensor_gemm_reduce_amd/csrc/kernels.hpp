@@ -114,6 +114,17 @@ struct Args {
     int32_t engine_every;    // K steps between reduce-engine slots (0: reduce after the last tile)
     int32_t coresident;      // 1: the reducer workgroups sit beside the compute workgroups of
                              // their CUs and sum a static share of items (peers first)
+    // all-gather + GEMM runs (the column-parallel layer): M x K gathered
+    // activations times this rank's N x K weight shard
+    const uint16_t* xsrc[8];  // row slice [S][K] of source rank d; xsrc[rank] is this rank's own
+    uint16_t* xg;            // gathered activations [M][K] (x_bytes long)
+    uint16_t* y;             // output [M][N]
+    uint32_t* agflags;       // per (source rank, tile row): copy units done, summed over runs
+    uint32_t* agfinished;    // per workgroup: count of all-gather launches it finished
+    uint32_t y_bytes;        // M * N * 2
+    uint32_t xs_bytes;       // S * K * 2
+    uint32_t ag_unit_bytes;  // bytes of one copy unit
+    int32_t ag_units;        // copy units per tile-row block (BM rows of one slice)
 };
 
 // BM x BN output tile, BK deep stages, NS stages in LDS, WAVES_M x WAVES_N
@@ -1174,17 +1185,22 @@ template <class C>
 struct TileJob {
     LoadPlan<C> lp;
     int nk;
+    const void* xp;    // the buffer the tile's X rows come from, and its bytes
+    uint32_t xbytes;
 };
 
+// X rows come from `xp` (xbytes long, row0 counted in it); by default from a.x.
 template <class C, bool LOADER>
 __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<C>& job, int row0, int rows,
-                                              int n0, int cols)
+                                              int n0, int cols, const void* xp = nullptr, uint32_t xbytes = 0)
 {
     const int K = a.g.K;
     job.nk = (K + C::BK - 1) / C::BK;
+    job.xp = xp ? xp : (const void*)a.x;
+    job.xbytes = xp ? xbytes : a.x_bytes;
     if constexpr (LOADER) {
         if (job.nk == 0) return;
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)job.xp, 0, job.xbytes, kRsrcFlags);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
         make_plan<C>(a, job.lp, row0, rows, n0, cols);
 #pragma unroll
@@ -1219,7 +1235,7 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
 
     const int K = a.g.K;
     const int nk = job.nk;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)job.xp, 0, job.xbytes, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
     for (int kt = 0; kt < nk; ++kt) {
         if constexpr (LOADER)
@@ -1310,7 +1326,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
     constexpr int kMf = C::FM * C::FN;   // MFMAs per substep
     constexpr int kDs = C::FM + C::FN;   // fragment reads per substep
     if (nk > 0) {
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, a.x_bytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)job.xp, 0, job.xbytes, kRsrcFlags);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
         bf16x8 xf[2][C::FM], wf[2][C::FN];
         // stage 0 came from the prologue, before the previous tile's stores
@@ -1677,6 +1693,203 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Args a)
 {
     sum_block(a, 0, a.g.S, 0, a.g.N, blockIdx.x * kReduceThreads + threadIdx.x, gridDim.x * kReduceThreads);
+}
+
+// ---------------------------------------------------------------- all-gather + GEMM
+//
+// The column-parallel linear layer that precedes the row-parallel one, with
+// the all-gather fused as the GEMM's prologue (TL;DR of "FLUX: Fast
+// Software-based Communication Overlap On GPUs Through Kernel Fusion";
+// "mKernel: Fast Multi-GPU, Multi-Node Fused Kernels", Section 4: the local
+// shard's tiles first, the others as their rows arrive).  Rank r holds its
+// activation row slice; the other tp-1 slices arrive from the peers.  On one
+// GPU they are resident buffers, and the copy phase below stands in for the
+// peers' writes into this rank's gathered buffer: every workgroup first
+// copies its share of copy units (in the order the tiles need them: slice
+// r+1 first, this rank's own slice last), each unit followed by one
+// device-scope increment of its tile-row block's counter.  The GEMM then runs
+// the reduce-scatter's tile schedule (own slice first, then rotated by rank):
+// an own tile reads the local slice directly; any other tile waits until its
+// block's counter reaches runs * units (counters are never reset, so a launch
+// can be replayed from a graph), then reads the gathered buffer.  Before its
+// first such read a wave invalidates its caches (agent-scope acquire): lines
+// of the gathered buffer left in this XCD's L2 by an earlier run would be
+// stale.  Output tiles go to y [M][N]; there is no reduction.
+
+// Copies units first, first + stride, ... (all threads of the workgroup).
+template <class C>
+__device__ __forceinline__ void ag_copy(const Args& a, int first, int stride)
+{
+    const int tp = a.g.tp, r = a.g.rank, S = a.g.S, K = a.g.K, tms = a.g.tms;
+    const int U = a.ag_units;
+    const uint32_t UB = a.ag_unit_bytes;
+    const int nunits = tp * tms * U;
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)a.xg, 0, a.x_bytes, kRsrcFlags);
+    const uint32_t tid16 = threadIdx.x * 16u;
+    constexpr uint32_t kPass = (uint32_t)C::THREADS * 16u;
+    for (int gu = first; gu < nunits; gu += stride) {
+        const int blk = gu / U, u = gu - blk * U;
+        const int k = blk / tms, tml = blk - k * tms;
+        const int d = uni((r + 1 + k) % tp);  // this rank's own slice last
+        const int rows = min(C::BM, S - tml * C::BM);
+        const uint32_t blk_bytes = (uint32_t)rows * (uint32_t)K * 2u;
+        const uint32_t src0 = (uint32_t)(tml * C::BM) * (uint32_t)K * 2u;
+        const uint32_t dst0 = (uint32_t)(d * S + tml * C::BM) * (uint32_t)K * 2u;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)a.xsrc[d], 0, a.xs_bytes, kRsrcFlags);
+        const uint32_t u0 = (uint32_t)u * UB;
+        const uint32_t u1 = min(u0 + UB, blk_bytes);
+        for (uint32_t o = u0 + tid16; o < u1; o += 4 * kPass) {
+            u32x4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t oi = o + (uint32_t)i * kPass;
+                v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, oi < u1 ? src0 + oi : kOob, 0, kAuxNt));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t oi = o + (uint32_t)i * kPass;
+                __builtin_amdgcn_raw_buffer_store_b128(v[i], rd, oi < u1 ? dst0 + oi : kOob, 0, kStoreDevice);
+            }
+        }
+        // every wave's stores of the unit have completed (device scope, written
+        // through to the memory side) before the block's counter moves
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0 && d != r)
+            __hip_atomic_fetch_add(a.agflags + d * tms + tml, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Waits (device-scope polls) until block `blk`'s counter reaches `target`;
+// reports a timeout through the status word and returns false.
+__device__ __forceinline__ bool ag_wait(const Args& a, int blk, uint32_t target)
+{
+    const uint32_t* f = a.agflags + blk;
+    if ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) >= 0) return true;
+    const uint64_t t0 = wall_clock64();
+    while ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
+            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
+                atomicExch(&a.state->status[1], blk);
+            return false;
+        }
+    }
+    return true;
+}
+
+// Issues the first stages of tile t: X rows from the local slice (own tile)
+// or from the gathered buffer once the block has arrived (FUSED) or because
+// the buffer is already complete (GEMM only).
+template <class C, bool FUSED>
+__device__ __forceinline__ void ag_prologue(const Args& a, char* lds, TileJob<C>& job, const TileCoord& t,
+                                            uint32_t target, bool& acquired)
+{
+    const int rows = tile_rows(a.g, t), cols = tile_cols(a.g, t);
+    if (t.d == a.g.rank) {
+        tile_prologue<C, true>(a, lds, job, t.tml * C::BM, rows, t.tn * C::BN, cols, a.xsrc[a.g.rank], a.xs_bytes);
+        return;
+    }
+    if constexpr (FUSED) {
+        ag_wait(a, t.d * a.g.tms + t.tml, target);
+        if (!acquired) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            acquired = true;
+        }
+    }
+    tile_prologue<C, true>(a, lds, job, t.d * a.g.S + t.tml * C::BM, rows, t.tn * C::BN, cols, a.xg, a.x_bytes);
+}
+
+template <class C, bool FUSED>
+__device__ __forceinline__ void ag_body(const Args& a)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ uint32_t s_runs;
+    if (threadIdx.x == 0)
+        s_runs = FUSED ? __hip_atomic_load(a.agfinished + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    __syncthreads();
+    const uint32_t run = (uint32_t)uni((int)s_runs) + 1u;  // this launch's count
+    const int grp = blockIdx.x % kGroups;
+    const int l = blockIdx.x / kGroups;
+    const int G = (int)gridDim.x;
+    const int pos = uni(a.strided ? (l * kGroups + grp) : (grp * (G / kGroups) + l));
+    if constexpr (FUSED) ag_copy<C>(a, pos, G);
+    const uint32_t target = run * (uint32_t)a.ag_units;
+
+    StepHooks hk;
+    hk.interleave = false;
+    hk.eng_countdown = 1;
+    hk.stores = false;
+    hk.pend_q = -1;
+    hk.pend_flag = -1;
+    hk.who = 0;
+    hk.epoch = run;
+    Engine eng;
+    Stream rs;
+    TileState<C> st;
+    TileJob<C> job;
+    bool acquired = false;
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void*)a.y, 0, a.y_bytes, kRsrcFlags);
+    int q = pos;
+    TileCoord t;
+    if (q < a.g.tiles) {
+        t = decode_slot(a.g, q);
+        ag_prologue<C, FUSED>(a, lds, job, t, target, acquired);
+    }
+    while (q < a.g.tiles) {
+        if constexpr (C::XP)
+            tile_kloop_xp<C, false>(a, lds, st, job, hk, rs);
+        else
+            tile_kloop<C, true>(a, lds, st, job, hk, eng);
+        const int qn = q + G;
+        TileCoord tn = t;
+        if (qn < a.g.tiles) {
+            tn = decode_slot(a.g, qn);
+            ag_prologue<C, FUSED>(a, lds, job, tn, target, acquired);
+        }
+        store_tile<C>(a, st, lds + (C::NS - 1) * C::STAGE_BYTES, ry, t.d * a.g.S + t.tml * C::BM, tile_rows(a.g, t),
+                      t.tn * C::BN, tile_cols(a.g, t));
+        hk.stores = true;
+        q = qn;
+        t = tn;
+    }
+    if constexpr (FUSED) {
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.agfinished + blockIdx.x, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <class C, bool FUSED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ag_kernel(Args a)
+{
+    ag_body<C, FUSED>(a);
+}
+
+template <class C, bool FUSED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void ag_kernel_8w(Args a)
+{
+    ag_body<C, FUSED>(a);
+}
+
+template <class C, bool FUSED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void ag_kernel_1w(Args a)
+{
+    ag_body<C, FUSED>(a);
+}
+
+// Standalone all-gather: copies the tp slices into the gathered buffer,
+// grid-stride over 16-byte chunks of each slice in turn (no counters).
+__global__ __launch_bounds__(kReduceThreads) void ag_copy_kernel(Args a)
+{
+    const int64_t chunks = (int64_t)a.g.S * a.g.K / 8;  // per slice
+    for (int d = 0; d < a.g.tp; ++d) {
+        const uint16_t* src = a.xsrc[d];
+        uint16_t* dst = a.xg + (int64_t)d * a.g.S * a.g.K;
+        for (int64_t c = blockIdx.x * (int64_t)kReduceThreads + threadIdx.x; c < chunks;
+             c += (int64_t)gridDim.x * kReduceThreads)
+            *reinterpret_cast<uint4*>(dst + c * 8) = *reinterpret_cast<const uint4*>(src + c * 8);
+    }
 }
 
 }  // namespace gemm_rs

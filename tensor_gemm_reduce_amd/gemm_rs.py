@@ -47,8 +47,8 @@ REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2, "coresident": 3}
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read",
-           "gemm_rs_destroy", "gemm_rs_strerror")
+           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather", "gemm_rs_status", "gemm_rs_query",
+           "gemm_rs_debug_read", "gemm_rs_destroy", "gemm_rs_strerror")
 
 
 class gemm_rs_config(ctypes.Structure):
@@ -100,6 +100,7 @@ def lib():
                                   ctypes.POINTER(vp), vp, vp, vp]
         L.gemm_rs_run_allreduce.argtypes = [vp, ctypes.c_int32, vp, vp, ctypes.POINTER(vp),
                                             ctypes.POINTER(vp), vp, vp, ctypes.POINTER(vp), vp]
+        L.gemm_rs_run_allgather.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(vp), vp, vp, vp, vp]
         L.gemm_rs_status.argtypes = [vp]
         L.gemm_rs_query.argtypes = [vp, infop]
         L.gemm_rs_debug_read.argtypes = [vp, u32p, ctypes.c_size_t, u32p, ctypes.c_size_t]
@@ -108,8 +109,8 @@ def lib():
         L.gemm_rs_strerror.argtypes = [ctypes.c_int]
         L.gemm_rs_strerror.restype = ctypes.c_char_p
         for name in ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_status", "gemm_rs_query",
-                     "gemm_rs_debug_read"):
+                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather", "gemm_rs_status",
+                     "gemm_rs_query", "gemm_rs_debug_read"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -185,6 +186,14 @@ def gemm_rs_run_allreduce(h, mode: int, x: int, w: int, send, peers, out: int, l
     peer_arr = (vp * 7)(*peers) if peers is not None else None
     gather_arr = (vp * 7)(*gather) if gather is not None else None
     return lib().gemm_rs_run_allreduce(h, mode, x, w, send_arr, peer_arr, out, local, gather_arr, stream)
+
+
+def gemm_rs_run_allgather(h, mode: int, x_slices, w: int | None, x_gathered: int, y: int | None,
+                          stream: int | None) -> int:
+    """All-gather + GEMM; x_slices: a list of tp device addresses in source-rank order."""
+    vp = ctypes.c_void_p
+    xs = (vp * len(x_slices))(*x_slices) if x_slices is not None else None
+    return lib().gemm_rs_run_allgather(h, mode, xs, w, x_gathered, y, stream)
 
 
 def gemm_rs_status(h) -> int:
@@ -290,6 +299,27 @@ class GemmRS:
             _check(gemm_rs_run(*args, stream), "gemm_rs_run")
         else:
             _check(gemm_rs_run_allreduce(*args, [_ptr(g) for g in gather], stream), "gemm_rs_run_allreduce")
+
+    def run_allgather(self, mode, x_slices, w, x_gathered, y, stream=None):
+        """All-gather + GEMM with this handle's M (gathered rows), N (output
+        columns) and K_local read as the layer's K: x_slices are tp [S][K]
+        tensors in source-rank order, w [N][K], x_gathered [M][K], y [M][N]."""
+        import torch
+
+        c = self.cfg
+        if len(x_slices) != c.tp:
+            raise ValueError("x_slices: need tp row slices")
+        for i, t in enumerate(x_slices):
+            self._check_tensor(t, (self.S, c.K_local), f"x_slices[{i}]")
+        self._check_tensor(x_gathered, (c.M, c.K_local), "x_gathered")
+        if mode != MODE_REDUCE_ONLY:
+            self._check_tensor(w, (c.N, c.K_local), "w")
+            self._check_tensor(y, (c.M, c.N), "y")
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        _check(gemm_rs_run_allgather(self.h, mode, [_ptr(t) for t in x_slices],
+                                     _ptr(w) if w is not None else None, _ptr(x_gathered),
+                                     _ptr(y) if y is not None else None, stream), "gemm_rs_run_allgather")
 
     def status(self) -> int:
         return gemm_rs_status(self.h)
