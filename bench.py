@@ -70,6 +70,8 @@ def parse():
                    help="time GEMM + all-reduce (gemm_rs_run_allreduce: the reduce-scatter whose sum also "
                         "replicates the reduced slice to the 7 peers) on every benchmark shape, write "
                         "OUT_JSON and exit")
+    p.add_argument("--allgather-sweep", metavar="OUT_JSON",
+                   help="time all-gather + GEMM (the column-parallel layer) per layer shape, write OUT_JSON")
     p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -497,6 +499,64 @@ def allreduce_sweep(args):
         raise RuntimeError("an all-reduce run reported an error or a gather buffer differs from out")
 
 
+AG_SWEEP = ("ag_qkv", "ag_gate_up", "ag_mixtral_w13", "ag_large_prefill")
+
+
+def allgather_sweep(args):
+    """All-gather + GEMM (the column-parallel layer) per layer shape: the fused
+    launch side by side with the GEMM over an already gathered buffer, the
+    standalone all-gather copy, the two in sequence and hipBLASLt's GEMM on
+    the gathered activations.  Algorithmic bytes of the all-gather: the tp-1
+    peer slices read and written, 2 * (tp-1) * S * K * 2."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    from tensor_gemm_reduce_amd import gemm_rs as gr
+
+    rows = {}
+    for name in AG_SWEEP:
+        cfg = synthetic.AG_CONFIGS[name]
+        xs, w = synthetic.make_ag_inputs(cfg, "normal")
+        d = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+        xs_d = [d(x) for x in xs]
+        w_d = d(w)
+        xg = torch.empty((cfg.M, cfg.K), dtype=torch.int16, device="cuda")
+        y = torch.empty((cfg.M, cfg.N), dtype=torch.int16, device="cuda")
+        op = gr.GemmRS(cfg.M, cfg.N, cfg.K, rank=0, tile=args.tile)
+        run = lambda mode: op.run_allgather(mode, xs_d, w_d, xg, y)
+        run(gr.MODE_FUSED)
+        torch.cuda.synchronize()
+        gathered_ok = all(torch.equal(xg[i * cfg.S:(i + 1) * cfg.S], xs_d[i]) for i in range(cfg.tp))
+        mm = lambda: torch.nn.functional.linear(xg.view(torch.bfloat16), w_d.view(torch.bfloat16))
+        t = time_interleaved({"fused": lambda: run(gr.MODE_FUSED), "gemm": lambda: run(gr.MODE_GEMM_ONLY),
+                              "copy": lambda: run(gr.MODE_REDUCE_ONLY), "seq": lambda: run(gr.MODE_SEQUENTIAL),
+                              "matmul": mm}, rounds=max(4, args.steps // 20))
+        st = op.status()
+        med = {k: statistics.median(v) for k, v in t.items()}
+        rows[name] = {
+            "shape": {"M": cfg.M, "N": cfg.N, "K": cfg.K}, "launch": op.info.as_dict(),
+            "T_fused_us": med["fused"], "T_gemm_us": med["gemm"], "T_copy_us": med["copy"], "T_seq_us": med["seq"],
+            "T_torch_linear_us": med["matmul"],
+            "fused_tflops": cfg.flops / med["fused"] * 1e-6,
+            "fused_pct_peak": 100.0 * cfg.flops / med["fused"] * 1e-6 / PEAK_BF16_TFLOPS,
+            "copy_gbs": cfg.gather_bytes / med["copy"] * 1e-3,
+            "overlap": 1.0 - (med["fused"] - med["gemm"]) / med["copy"],
+            "speedup_vs_sequential": med["seq"] / med["fused"],
+            "gathered_ok": gathered_ok, "status": gr.gemm_rs_strerror(st),
+        }
+        log(f"[{name}] all-gather: " + json.dumps({k: rows[name][k] for k in
+                                                   ("T_fused_us", "T_gemm_us", "T_copy_us", "overlap",
+                                                    "gathered_ok")}))
+        op.close()
+        del xs_d, w_d, xg, y
+        torch.cuda.empty_cache()
+    with open(args.allgather_sweep, "w") as f:
+        json.dump({"rows": rows, "source_digest": source_digest()}, f, indent=1)
+    if not all(r["gathered_ok"] and r["status"] == "success" for r in rows.values()):
+        raise RuntimeError("an all-gather run reported an error or gathered wrong rows")
+
+
 def stats_summary(path):
     """Markdown table of rocprofv3's per-kernel statistics (durations in us)."""
     import csv
@@ -541,6 +601,9 @@ def main():
         return
     if args.allreduce_sweep:
         allreduce_sweep(args)
+        return
+    if args.allgather_sweep:
+        allgather_sweep(args)
         return
     c = Case(args.workload, args)
     cfg = c.cfg

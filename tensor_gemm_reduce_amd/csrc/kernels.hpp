@@ -1711,10 +1711,12 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Args a)
 // the reduce-scatter's tile schedule (own slice first, then rotated by rank):
 // an own tile reads the local slice directly; any other tile waits until its
 // block's counter reaches runs * units (counters are never reset, so a launch
-// can be replayed from a graph), then reads the gathered buffer.  Before its
-// first such read a wave invalidates its caches (agent-scope acquire): lines
-// of the gathered buffer left in this XCD's L2 by an earlier run would be
-// stale.  Output tiles go to y [M][N]; there is no reduction.
+// can be replayed from a graph), then reads the gathered buffer.  Lines of the
+// gathered buffer left in an XCD's L2 by an earlier run would be stale, so
+// every workgroup invalidates its caches once at its start (agent-scope
+// acquire), before anything of this run is cached; later lines of the buffer
+// can only come from reads made after their rows were copied.  Output tiles
+// go to y [M][N]; there is no reduction.
 
 // Copies units first, first + stride, ... (all threads of the workgroup).
 template <class C>
@@ -1738,15 +1740,17 @@ __device__ __forceinline__ void ag_copy(const Args& a, int first, int stride)
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)a.xsrc[d], 0, a.xs_bytes, kRsrcFlags);
         const uint32_t u0 = (uint32_t)u * UB;
         const uint32_t u1 = min(u0 + UB, blk_bytes);
-        for (uint32_t o = u0 + tid16; o < u1; o += 4 * kPass) {
-            u32x4 v[4];
+        // (eight 16-byte loads in flight per thread: a workgroup's copy is
+        // bound by how much it has in flight)
+        for (uint32_t o = u0 + tid16; o < u1; o += 8 * kPass) {
+            u32x4 v[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 const uint32_t oi = o + (uint32_t)i * kPass;
                 v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, oi < u1 ? src0 + oi : kOob, 0, kAuxNt));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 const uint32_t oi = o + (uint32_t)i * kPass;
                 __builtin_amdgcn_raw_buffer_store_b128(v[i], rd, oi < u1 ? dst0 + oi : kOob, 0, kStoreDevice);
             }
@@ -1783,20 +1787,14 @@ __device__ __forceinline__ bool ag_wait(const Args& a, int blk, uint32_t target)
 // the buffer is already complete (GEMM only).
 template <class C, bool FUSED>
 __device__ __forceinline__ void ag_prologue(const Args& a, char* lds, TileJob<C>& job, const TileCoord& t,
-                                            uint32_t target, bool& acquired)
+                                            uint32_t target)
 {
     const int rows = tile_rows(a.g, t), cols = tile_cols(a.g, t);
     if (t.d == a.g.rank) {
         tile_prologue<C, true>(a, lds, job, t.tml * C::BM, rows, t.tn * C::BN, cols, a.xsrc[a.g.rank], a.xs_bytes);
         return;
     }
-    if constexpr (FUSED) {
-        ag_wait(a, t.d * a.g.tms + t.tml, target);
-        if (!acquired) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            acquired = true;
-        }
-    }
+    if constexpr (FUSED) ag_wait(a, t.d * a.g.tms + t.tml, target);
     tile_prologue<C, true>(a, lds, job, t.d * a.g.S + t.tml * C::BM, rows, t.tn * C::BN, cols, a.xg, a.x_bytes);
 }
 
@@ -1805,15 +1803,22 @@ __device__ __forceinline__ void ag_body(const Args& a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ uint32_t s_runs;
-    if (threadIdx.x == 0)
-        s_runs = FUSED ? __hip_atomic_load(a.agfinished + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    if (threadIdx.x < 64) {
+        // drop lines an earlier run left in this CU's L1 and this XCD's L2
+        if constexpr (FUSED) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (threadIdx.x == 0)
+            s_runs = FUSED ? __hip_atomic_load(a.agfinished + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0u;
+    }
     __syncthreads();
     const uint32_t run = (uint32_t)uni((int)s_runs) + 1u;  // this launch's count
     const int grp = blockIdx.x % kGroups;
     const int l = blockIdx.x / kGroups;
     const int G = (int)gridDim.x;
     const int pos = uni(a.strided ? (l * kGroups + grp) : (grp * (G / kGroups) + l));
-    if constexpr (FUSED) ag_copy<C>(a, pos, G);
+    // copy units go to the workgroups from the last position down: those
+    // hold the fewest tiles (a round's last positions), or none
+    if constexpr (FUSED) ag_copy<C>(a, G - 1 - pos, G);
     const uint32_t target = run * (uint32_t)a.ag_units;
 
     StepHooks hk;
@@ -1828,13 +1833,12 @@ __device__ __forceinline__ void ag_body(const Args& a)
     Stream rs;
     TileState<C> st;
     TileJob<C> job;
-    bool acquired = false;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void*)a.y, 0, a.y_bytes, kRsrcFlags);
     int q = pos;
     TileCoord t;
     if (q < a.g.tiles) {
         t = decode_slot(a.g, q);
-        ag_prologue<C, FUSED>(a, lds, job, t, target, acquired);
+        ag_prologue<C, FUSED>(a, lds, job, t, target);
     }
     while (q < a.g.tiles) {
         if constexpr (C::XP)
@@ -1845,7 +1849,7 @@ __device__ __forceinline__ void ag_body(const Args& a)
         TileCoord tn = t;
         if (qn < a.g.tiles) {
             tn = decode_slot(a.g, qn);
-            ag_prologue<C, FUSED>(a, lds, job, tn, target, acquired);
+            ag_prologue<C, FUSED>(a, lds, job, tn, target);
         }
         store_tile<C>(a, st, lds + (C::NS - 1) * C::STAGE_BYTES, ry, t.d * a.g.S + t.tml * C::BM, tile_rows(a.g, t),
                       t.tn * C::BN, tile_cols(a.g, t));
