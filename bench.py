@@ -54,7 +54,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tile", default="auto")
     p.add_argument("--reducers", type=int, default=-1)
-    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "stream", "coresident"],
+    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "stream", "coresident", "epilogue"],
                    help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--engine-interval", type=int, default=0,
                    help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
@@ -112,7 +112,7 @@ class Case:
         # where the fused launch streams the sum through the K loop, the same
         # launch with the sum after the last tile is timed beside it
         self.op_tail = None
-        if self.op.info.reduce_mode in (gr.REDUCE_STREAM, gr.REDUCE_CORESIDENT):
+        if self.op.info.reduce_mode in (gr.REDUCE_STREAM, gr.REDUCE_CORESIDENT, gr.REDUCE_EPILOGUE):
             self.op_tail = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
                                      num_reducers=args.reducers, engine_interval=args.engine_interval,
                                      reduce_mode="tail")
@@ -259,7 +259,7 @@ def measure_case(c: Case, warmup, iters):
         "reduce_pct_hbm": 100.0 * cfg.reduce_bytes / tr * 1e-3 / PEAK_HBM_GBS,
         "overlap": 1.0 - (tf - tg) / tr,
         "speedup_vs_sequential": seq["median_us"] / tf,
-        "reduce_mode": {0: "auto", 1: "tail", 2: "stream", 3: "coresident"}[c.op.info.reduce_mode],
+        "reduce_mode": {0: "auto", 1: "tail", 2: "stream", 3: "coresident", 4: "epilogue"}[c.op.info.reduce_mode],
         **extra,
     }
 

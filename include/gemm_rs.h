@@ -106,6 +106,10 @@ extern "C" {
                                    sums the peers of its items while the GEMM runs,
                                    then adds the local chunk once the tile's flag
                                    is set                                          */
+#define GEMM_RS_REDUCE_EPILOGUE 4 /* the workgroup that computes an own-slice tile
+                                   sums it in its epilogue from its accumulators
+                                   and the tile's peer values, loaded ahead of the
+                                   tile's first stage (16x64 and 64x128 tiles)   */
 
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
@@ -130,9 +134,10 @@ typedef struct gemm_rs_config {
     int32_t flag_stride;  /* 32-bit words between ready flags (1 or 32)       */
     int64_t watchdog_us;  /* reducer wait limit per tile in microseconds;
                              0 = default (2 000 000)                          */
-    int32_t reduce_mode;  /* GEMM_RS_REDUCE_*; STREAM and CORESIDENT need
+    int32_t reduce_mode;  /* GEMM_RS_REDUCE_*; all but AUTO and TAIL need
                              num_reducers <= 0 and engine_interval == 0;
-                             STREAM needs the 256x256 tile                    */
+                             STREAM needs the 256x256 tile, EPILOGUE the
+                             16x64 or 64x128 tile                            */
 } gemm_rs_config;
 
 typedef struct gemm_rs_info {

@@ -61,6 +61,7 @@ struct TileDesc {
     const void* gemm_kernel;   // the same GEMM without flags or reduction
     const void* ag_kernel;     // all-gather + GEMM: copy phase, then the GEMM waiting for rows
     const void* ag_gemm_kernel;  // the same GEMM over an already gathered buffer
+    const void* epi_kernel;    // fused: own tiles summed in their producer's epilogue (or null)
 };
 
 // Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
@@ -88,6 +89,17 @@ const void* ag_kernel_for()
         return reinterpret_cast<const void*>(&ag_kernel_1w<C, FUSED>);
 }
 
+// The epilogue sum keeps a tile's peer values in registers: four-wave tiles
+// with at most 32 accumulators per lane (16x64, 64x128).
+template <class C>
+const void* epi_kernel_for()
+{
+    if constexpr (C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64 && C::FM * C::FN * AccT<C::MF>::N <= 32)
+        return reinterpret_cast<const void*>(&fused_kernel<C, true, true>);
+    else
+        return nullptr;
+}
+
 template <class C, class CE>
 TileDesc desc()
 {
@@ -105,7 +117,7 @@ TileDesc desc()
     return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, elds, C::LDS_BYTES,
                     kernel_for<CE, true, two>(), sk, stream ? slds : 0,
                     kernel_for<C, true, two>(), kernel_for<C, false, two>(),
-                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>()};
+                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), epi_kernel_for<C>()};
 }
 
 TileDesc tile_desc(int id)
@@ -117,7 +129,7 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
+    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
     }
 }
 
@@ -143,6 +155,9 @@ int resolve_tile(const gemm_rs_config& c) { return c.tile == GEMM_RS_TILE_AUTO ?
 
 // Tiles whose fused kernel can stream the slice sum through the K loop.
 bool stream_tile(int id) { return id == GEMM_RS_TILE_256x256; }
+
+// Tiles whose fused kernel can sum own tiles in the epilogue.
+bool epilogue_tile(int id) { return id == GEMM_RS_TILE_16x64 || id == GEMM_RS_TILE_64x128; }
 
 // Where the slice sum of a fused run without dedicated reducers or engine
 // slots runs.
@@ -252,9 +267,9 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
     if (c->watchdog_us < 0) return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_CORESIDENT)
+    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_EPILOGUE)
         return GEMM_RS_ERR_INVALID_ARG;
-    if ((c->reduce_mode == GEMM_RS_REDUCE_STREAM || c->reduce_mode == GEMM_RS_REDUCE_CORESIDENT) &&
+    if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL &&
         (c->num_reducers > 0 || c->engine_interval > 0))
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->tp != 8) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
@@ -279,6 +294,8 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (tiles > (1 << 30)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->drop_flag >= 0 && c->drop_flag >= tiles) return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode == GEMM_RS_REDUCE_STREAM && !stream_tile(resolve_tile(*c))) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    if (c->reduce_mode == GEMM_RS_REDUCE_EPILOGUE && !epilogue_tile(resolve_tile(*c)))
+        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return GEMM_RS_OK;
 }
 
@@ -379,6 +396,8 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     if (e == hipSuccess && h->td.stream_kernel)
         e = hipFuncSetAttribute(h->td.stream_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 h->td.stream_lds_bytes);
+    if (e == hipSuccess && h->td.epi_kernel)
+        e = hipFuncSetAttribute(h->td.epi_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     h->reduce_mode = resolve_reduce_mode(*c);
     int occ = 0;
@@ -390,6 +409,8 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     } else if (h->reduce_mode == GEMM_RS_REDUCE_STREAM) {
         fk = h->td.stream_kernel;
         h->fused_lds = h->td.stream_lds_bytes;
+    } else if (h->reduce_mode == GEMM_RS_REDUCE_EPILOGUE) {
+        fk = h->td.epi_kernel;
     }
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, h->td.threads, h->fused_lds);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
@@ -518,8 +539,10 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // (the reduce stream: every wave loads stages and streams its share of the sum)
     const bool engine = fused && h->reducer_wgs == 0 && h->cfg.engine_interval > 0;
     const bool stream = fused && h->reducer_wgs == 0 && h->reduce_mode == GEMM_RS_REDUCE_STREAM;
+    const bool epi = fused && h->reducer_wgs == 0 && h->reduce_mode == GEMM_RS_REDUCE_EPILOGUE;
     const void* k = engine ? h->td.engine_kernel
                   : stream ? h->td.stream_kernel
+                  : epi    ? h->td.epi_kernel
                   : fused  ? h->td.kernel
                            : h->td.gemm_kernel;
     // (a GEMM-only launch runs on the compute workgroups' grid: the

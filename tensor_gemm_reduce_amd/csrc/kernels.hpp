@@ -1147,6 +1147,99 @@ __device__ __forceinline__ void stream_drain(const Stream& s, const Args& a, int
     drain_items<2>(a, m, cur + (end - cur) * part / kStreamOps, 1, s.epoch);
 }
 
+
+// ---------------------------------------------------------------- sum in the epilogue
+//
+// reduce_mode EPILOGUE (four-wave tiles small enough to keep a tile's peer
+// chunks in registers): the workgroup that computes an own-slice tile sums it
+// in its epilogue, from its accumulators, the way FLUX fuses the
+// reduce-scatter into the GEMM epilogue (TL;DR of "FLUX: Fast Software-based
+// Communication Overlap On GPUs Through Kernel Fusion").  Each lane loads the
+// 7 peers' values of exactly the output elements its accumulators hold (the
+// same element map as the unstaged tile store) before the tile's first stage
+// loads, so they arrive with the first stage; the epilogue forms
+// (((0 + p_0) + ...) + p_6) + RNE_bf16(acc) in FP32, the oracle's order, and
+// stores it rounded to `out` (and the gather buffers in an all-reduce run).
+// No flag is polled: the producer sums its own tile.
+
+template <class C>
+struct PeerFrag {
+    static constexpr int G = C::MF == 32 ? 4 : 1;  // groups of four columns per MFMA block
+    u32x2 v[kPeers][C::FM][C::FN][G];
+};
+
+// Loads the peer values of tile (srow0.., n0..) that this lane's accumulators
+// hold; elements outside the (ragged) tile read as zero.
+template <class C>
+__device__ __forceinline__ void epi_load_peers(const Args& a, PeerFrag<C>& pf, int srow0, int rows, int n0, int cols)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = uni((int)(threadIdx.x >> 6));
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const uint32_t N = (uint32_t)a.g.N;
+#pragma unroll
+    for (int s = 0; s < kPeers; ++s) {
+        const __amdgpu_buffer_rsrc_t rp =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a.peers[s], 0, a.slice_bytes, kRsrcFlags);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int m = wm * C::WTM + i * C::MF + (lane % C::MF);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int grp = 0; grp < PeerFrag<C>::G; ++grp) {
+                    const int n = C::MF == 32 ? wn * C::WTN + j * 32 + grp * 8 + (lane / 32) * 4
+                                              : wn * C::WTN + j * 16 + (lane / 16) * 4;
+                    const uint32_t off =
+                        (m < rows && n < cols) ? (((uint32_t)(srow0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
+                    pf.v[s][i][j][grp] =
+                        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, kAuxNt));
+                }
+        }
+    }
+}
+
+// os = (((0 + p_0) + ... ) + p_6) + RNE_bf16(st), element by element (FP32).
+template <class C>
+__device__ __forceinline__ void epi_sum(const PeerFrag<C>& pf, const TileState<C>& st, TileState<C>& os)
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int grp = 0; grp < PeerFrag<C>::G; ++grp)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < kPeers; ++s) {
+                        const uint32_t w = e < 2 ? pf.v[s][i][j][grp].x : pf.v[s][i][j][grp].y;
+                        acc += bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+                    }
+                    const int k = grp * 4 + e;
+                    const float local = bf16_bits_to_f32(pack_bf16x2(st.acc[i][j][k], 0.0f) & 0xFFFFu);
+                    os.acc[i][j][k] = acc + local;
+                }
+}
+
+// The epilogue's sum stores: the rounded sums into `out` and, in an all-reduce
+// run, into the gather buffers (each through the tile store's LDS staging).
+template <class C>
+__device__ __forceinline__ void epi_store(const Args& a, const TileState<C>& os, char* area, int srow0, int rows,
+                                          int n0, int cols)
+{
+    store_tile<C>(a, os, area, __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags), srow0, rows,
+                  n0, cols);
+    if (a.gather_on) {
+#pragma unroll 1
+        for (int g = 0; g < kPeers; ++g)
+            store_tile<C>(a, os, area,
+                          __builtin_amdgcn_make_buffer_rsrc(pick7(a.gather, g), 0, a.slice_bytes, kRsrcFlags),
+                          srow0, rows, n0, cols);
+    }
+}
+
 // ---------------------------------------------------------------- tile loop
 
 // Per-tile state shared by the K loop and the role loop.
@@ -1423,10 +1516,11 @@ __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int gr
 // the next tile's waits have covered the tile's stores: publishing costs no
 // extra wait.  Loader and engine waves run the same loop (the same barriers);
 // engine waves also run the reduce engine.
-template <class C, bool FUSED, bool LOADER, bool STREAM>
+template <class C, bool FUSED, bool LOADER, bool STREAM, bool EPI = false>
 __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos, uint32_t who, uint32_t epoch,
                                               bool interleave)
 {
+    static_assert(!EPI || (FUSED && C::WAVES == 4 && C::EW == 0), "the epilogue sum: four-wave fused tiles");
     const int Ctot = a.num_compute;
     const int wave = uni((int)(threadIdx.x >> 6));
     Engine eng;
@@ -1451,10 +1545,15 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     hk.epoch = epoch;
     TileState<C> st;
     TileJob<C> job;
+    PeerFrag<C> pf;
     int q = pos;
     TileCoord t;
     if (q < a.g.tiles) {
         t = decode_slot(a.g, q);
+        // (the peer values load ahead of the first stage, which waits for them)
+        if constexpr (EPI)
+            if (t.d == a.g.rank)
+                epi_load_peers<C>(a, pf, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
         tile_prologue<C, LOADER>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN,
                                  tile_cols(a.g, t));
     }
@@ -1476,6 +1575,18 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.dst[t.d], 0, a.slice_bytes, kRsrcFlags);
         store_tile<C>(a, st, lds + (C::NS - 1) * C::STAGE_BYTES, rd, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN,
                       tile_cols(a.g, t));
+        if constexpr (EPI) {
+            if (t.d == a.g.rank) {
+                TileState<C> os;
+                epi_sum<C>(pf, st, os);
+                epi_store<C>(a, os, lds + (C::NS - 1) * C::STAGE_BYTES, t.tml * C::BM, tile_rows(a.g, t),
+                             t.tn * C::BN, tile_cols(a.g, t));
+            }
+            // a later own tile's peer values load behind these stores (its
+            // stage waits then cover them)
+            if (qn < a.g.tiles && tn.d == a.g.rank)
+                epi_load_peers<C>(a, pf, tn.tml * C::BM, tile_rows(a.g, tn), tn.tn * C::BN, tile_cols(a.g, tn));
+        }
         hk.stores = true;
         if constexpr (!LOADER) {
             eng.vm += C::STORES;
@@ -1493,7 +1604,9 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         stage_barrier();
         if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
-    if constexpr (STREAM) {
+    if constexpr (EPI) {
+        // every own tile was summed by its producer
+    } else if constexpr (STREAM) {
         // the items the stream has not finished
         __shared__ int s_progress[C::WAVES / kStreamOps];
         stream_drain<C::WAVES>(rs, a, wave, s_progress);
@@ -1514,7 +1627,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
 // Compute role of the l-th compute workgroup of group grp: its position in a
 // round is either the group's block offset + l (contiguous split) or
 // l * 8 + grp (strided, used when all C_x are equal).
-template <class C, bool FUSED, bool STREAM>
+template <class C, bool FUSED, bool STREAM, bool EPI = false>
 __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, int l, uint32_t epoch, int base)
 {
     const int pos = uni(a.strided ? (l * kGroups + grp) : (base + l));
@@ -1523,7 +1636,7 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
     const bool interleave = FUSED && a.num_reducers == 0;
     const int wave = uni((int)(threadIdx.x >> 6));
     if (C::EW == 0 || wave < C::LW)
-        compute_waves<C, FUSED, true, STREAM>(a, lds, pos, who, epoch, interleave);
+        compute_waves<C, FUSED, true, STREAM, EPI>(a, lds, pos, who, epoch, interleave);
     else if constexpr (C::EW > 0)
         compute_waves<C, FUSED, false, false>(a, lds, pos, who, epoch, interleave);
 }
@@ -1607,7 +1720,7 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
 // launch stored the same value, so all workgroups of a launch agree on its
 // epoch without communicating (the words change only at kernel ends).  A
 // GEMM-only launch has no flags and touches none of this.
-template <class C, bool FUSED, bool STREAM = false>
+template <class C, bool FUSED, bool STREAM = false, bool EPI = false>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1629,7 +1742,7 @@ __device__ __forceinline__ void fused_body(const Args& a)
     const uint32_t epoch = (uint32_t)uni((int)s_epoch) + 1u;  // value this run's flags carry
     const GroupSplit split = group_split((int)gridDim.x, uni(a.num_reducers), grp);
     if (ticket < (uint32_t)split.compute)
-        compute_role<C, FUSED, STREAM>(a, lds, grp, (int)ticket, epoch, split.base);
+        compute_role<C, FUSED, STREAM, EPI>(a, lds, grp, (int)ticket, epoch, split.base);
     else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers) {
         if (a.coresident) {
             // reducer r of R owns items r*W + wave, + R*W, ...: its peer chunks
@@ -1666,10 +1779,10 @@ __device__ __forceinline__ void fused_body(const Args& a)
 }
 
 // Tiles that fit two workgroups per CU keep two waves per SIMD resident.
-template <class C, bool FUSED>
+template <class C, bool FUSED, bool EPI = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(Args a)
 {
-    fused_body<C, FUSED>(a);
+    fused_body<C, FUSED, false, EPI>(a);
 }
 
 // Eight-wave workgroups (one per CU): two waves per SIMD, so one wave's

@@ -42,7 +42,8 @@ REDUCE_AUTO = 0
 REDUCE_TAIL = 1
 REDUCE_STREAM = 2
 REDUCE_CORESIDENT = 3
-REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2, "coresident": 3}
+REDUCE_EPILOGUE = 4
+REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2, "coresident": 3, "epilogue": 4}
 
 DEBUG_TRACE = 1
 

@@ -75,7 +75,11 @@ def cfg(**kw):
     (dict(drop_flag=100000), gr.ERR_INVALID_ARG),
     (dict(num_reducers=-2), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode=4), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.OK),
+    (dict(reduce_mode="epilogue"), gr.ERR_UNSUPPORTED_SHAPE),            # 256x256 tile
+    (dict(reduce_mode="epilogue", tile="128x128"), gr.ERR_UNSUPPORTED_SHAPE),
+    (dict(reduce_mode="epilogue", M=512, K_local=1024, num_reducers=8), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="coresident"), gr.OK),
     (dict(reduce_mode="coresident", num_reducers=8), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="coresident", engine_interval=1), gr.ERR_INVALID_ARG),
@@ -142,6 +146,7 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
     (dict(reduce_mode="stream"), gr.REDUCE_STREAM),  # 256x256 tile
     (dict(reduce_mode="tail"), gr.REDUCE_TAIL),
     (dict(reduce_mode="coresident"), gr.REDUCE_CORESIDENT),
+    (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.REDUCE_EPILOGUE),
     (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
     (dict(engine_interval=2), gr.REDUCE_TAIL),
     (dict(tile="128x128"), gr.REDUCE_TAIL),           # no stream for this tile
