@@ -53,7 +53,8 @@ def parse():
     p.add_argument("--no-check", dest="check", action="store_false")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tile", default="auto")
-    p.add_argument("--reducers", type=int, default=-1)
+    p.add_argument("--reducers", type=int, default=-1,
+                   help="dedicated reducer workgroups: -1 the plan's default, -2 adaptive")
     p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "stream", "coresident", "epilogue"],
                    help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--engine-interval", type=int, default=0,
@@ -109,6 +110,13 @@ class Case:
         self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
                             num_reducers=args.reducers, engine_interval=args.engine_interval,
                             reduce_mode=args.reduce_mode)
+        # the adaptive split (reducers -2) times its candidates on uncaptured
+        # runs: give it those before anything is captured into a graph
+        if args.reducers == -2:
+            for _ in range(16):
+                self.run(gr.MODE_FUSED)
+                torch.cuda.synchronize()
+            log(f"[{name}] adaptive split settled: {gr.gemm_rs_query(self.op.h).reducer_wgs} reducer workgroups")
         # where the fused launch streams the sum through the K loop, the same
         # launch with the sum after the last tile is timed beside it
         self.op_tail = None

@@ -123,7 +123,12 @@ typedef struct gemm_rs_config {
     int32_t rank;         /* this rank, 0 <= rank < tp                        */
     int32_t tile;         /* GEMM_RS_TILE_*                                   */
     int32_t group_m;      /* tile rows per raster group; 0 = automatic        */
-    int32_t num_reducers; /* reducer workgroups in FUSED mode; -1 = automatic */
+    int32_t num_reducers; /* reducer workgroups in FUSED mode; -1 = automatic
+                             (none); -2 = adaptive: the first uncaptured FUSED
+                             runs are timed with 0, 8, 16, 32 and 64 dedicated
+                             reducers (two runs each), and once all have
+                             completed the fastest count is kept (results
+                             are identical for every count)                  */
     int32_t engine_interval; /* FUSED without reducer workgroups: K steps between
                              reduce-engine slots inside the compute loop;
                              0 = the engine waves sum the slice after their
@@ -159,6 +164,9 @@ typedef struct gemm_rs_info {
                                  (read from the device; waits for the stream) */
     int32_t reduce_mode;      /* resolved GEMM_RS_REDUCE_* of a FUSED run with
                                  no dedicated reducers and no engine slots    */
+    int32_t split_state;      /* 0: fixed reducer count; 1: adaptive, still
+                                 timing candidates; 2: adaptive, settled on
+                                 reducer_wgs                                  */
 } gemm_rs_info;
 
 typedef struct gemm_rs_handle gemm_rs_handle;

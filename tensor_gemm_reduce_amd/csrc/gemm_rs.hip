@@ -183,6 +183,11 @@ Geometry geometry_of(const gemm_rs_config& c)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Adaptive split: candidate dedicated-reducer counts and runs timed per candidate.
+constexpr int kSplitCands = 5;
+constexpr int kSplitReps = 2;
+constexpr int kSplitChoices[kSplitCands] = {0, 8, 16, 32, 64};
+
 }  // namespace
 
 struct gemm_rs_handle {
@@ -198,6 +203,14 @@ struct gemm_rs_handle {
     // all-gather + GEMM runs
     uint32_t* agflags;     // tp * tile rows per slice copy counters
     uint32_t* agfinished;  // per workgroup of ag_grid
+    // adaptive split (num_reducers == -2): the first fused runs cycle through
+    // candidate reducer counts, timed with events; the fastest is kept
+    struct {
+        bool on, settled;
+        int ncand, reps, launched;
+        int cand[kSplitCands];
+        hipEvent_t ev[kSplitCands * kSplitReps][2];
+    } split;
     int ag_grid;
     int ag_strided;
     int ag_units;
@@ -261,7 +274,11 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->rank < 0 || c->rank >= c->tp) return GEMM_RS_ERR_INVALID_ARG;
     if (c->tile < 0 || c->tile >= GEMM_RS_TILE_COUNT) return GEMM_RS_ERR_INVALID_ARG;
     if (c->group_m < 0) return GEMM_RS_ERR_INVALID_ARG;
-    if (c->num_reducers < -1) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->num_reducers < -2) return GEMM_RS_ERR_INVALID_ARG;
+    // the adaptive split chooses among dedicated-reducer counts
+    if (c->num_reducers == -2 && (c->engine_interval > 0 || (c->reduce_mode != GEMM_RS_REDUCE_AUTO &&
+                                                              c->reduce_mode != GEMM_RS_REDUCE_TAIL)))
+        return GEMM_RS_ERR_INVALID_ARG;
     if (c->engine_interval < 0 || c->engine_interval > 4096) return GEMM_RS_ERR_INVALID_ARG;
     if (c->debug_flags & ~GEMM_RS_DEBUG_TRACE) return GEMM_RS_ERR_INVALID_ARG;
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
@@ -350,8 +367,61 @@ const char* gemm_rs_strerror(int code)
     }
 }
 
+// Sets the dedicated-reducer count of fused launches (and the XCD split that
+// goes with it).
+static void set_split(gemm_rs_handle* h, int red)
+{
+    if (red >= h->grid) red = h->grid - 1;
+    h->reducer_wgs = red;
+    h->compute_wgs = h->grid - red;
+    h->strided = (h->reducer_wgs % kGroups == 0 && h->g.tiles > 0 &&
+                  xcd_footprint(h->g, h->grid, h->reducer_wgs, true) <
+                      xcd_footprint(h->g, h->grid, h->reducer_wgs, false))
+                     ? 1 : 0;
+}
+
+// Adaptive split: once every timed run has completed, keep the candidate with
+// the shortest run (the fastest of its repetitions).  Until then fused runs
+// use no dedicated reducers.
+static void split_try_settle(gemm_rs_handle* h)
+{
+    const int n = h->split.ncand * h->split.reps;
+    for (int i = 0; i < n; ++i) {
+        const hipError_t q = hipEventQuery(h->split.ev[i][1]);
+        if (q != hipSuccess) {
+            (void)hipGetLastError();  // a pending event is not an error
+            set_split(h, 0);
+            return;
+        }
+    }
+    int best = 0;
+    float best_ms = -1.0f;
+    for (int c = 0; c < h->split.ncand; ++c) {
+        float cand_ms = -1.0f;
+        for (int r = 0; r < h->split.reps; ++r) {
+            const int i = r * h->split.ncand + c;
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, h->split.ev[i][0], h->split.ev[i][1]) == hipSuccess &&
+                (cand_ms < 0.0f || ms < cand_ms))
+                cand_ms = ms;
+        }
+        if (cand_ms >= 0.0f && (best_ms < 0.0f || cand_ms < best_ms)) {
+            best_ms = cand_ms;
+            best = h->split.cand[c];
+        }
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < 2; ++j) (void)hipEventDestroy(h->split.ev[i][j]);
+    h->split.settled = true;
+    set_split(h, best);
+}
+
 static void free_state(gemm_rs_handle* h)
 {
+    if (h->split.on && !h->split.settled)
+        for (int i = 0; i < h->split.ncand * h->split.reps; ++i)
+            for (int j = 0; j < 2; ++j)
+                if (h->split.ev[i][j]) (void)hipEventDestroy(h->split.ev[i][j]);
     if (h->flags) (void)hipFree(h->flags);
     if (h->state) (void)hipFree(h->state);
     if (h->trace) (void)hipFree(h->trace);
@@ -430,13 +500,29 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
         h->wgs_per_cu += 1;
     }
     if (red >= h->grid) red = h->grid - 1;
-    h->reducer_wgs = red;
-    h->compute_wgs = h->grid - red;
     h->reduce_grid = h->num_cus * 8;
-    h->strided = (h->reducer_wgs % kGroups == 0 && h->g.tiles > 0 &&
-                  xcd_footprint(h->g, h->grid, h->reducer_wgs, true) <
-                      xcd_footprint(h->g, h->grid, h->reducer_wgs, false))
-                     ? 1 : 0;
+    set_split(h, red);
+    h->split.on = c->num_reducers == -2;
+    h->split.settled = !h->split.on;
+    h->split.ncand = 0;
+    h->split.reps = kSplitReps;
+    h->split.launched = 0;
+    if (h->split.on) {
+        for (int i = 0; i < kSplitCands; ++i)
+            if (kSplitChoices[i] < h->grid) h->split.cand[h->split.ncand++] = kSplitChoices[i];
+        for (int i = 0; i < h->split.ncand * h->split.reps; ++i)
+            for (int j = 0; j < 2; ++j) {
+                hipError_t ee = hipEventCreate(&h->split.ev[i][j]);
+                if (ee != hipSuccess) {
+                    // (the handle was value-initialised: events not created are null)
+                    for (int k = 0; k < h->split.ncand * h->split.reps; ++k)
+                        for (int l = 0; l < 2; ++l)
+                            if (h->split.ev[k][l]) (void)hipEventDestroy(h->split.ev[k][l]);
+                    delete h;
+                    return hip_fail(ee, "hipEventCreate");
+                }
+            }
+    }
 
     // all-gather + GEMM launches: the compute grid of the same tile (no reducers)
     for (const void* k : {h->td.ag_kernel, h->td.ag_gemm_kernel}) {
@@ -528,6 +614,24 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
 {
+    // adaptive split: time the candidates on the first uncaptured fused runs
+    int timed = -1;
+    if (fused && h->split.on && !h->split.settled) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(s, &cs));
+        if (cs == hipStreamCaptureStatusNone) {
+            const int n = h->split.ncand * h->split.reps;
+            if (h->split.launched < n) {
+                timed = h->split.launched++;
+                set_split(h, h->split.cand[timed % h->split.ncand]);
+            } else {
+                split_try_settle(h);
+            }
+        } else {
+            set_split(h, 0);
+        }
+        a.strided = h->strided;
+    }
     a.fused = fused ? 1 : 0;
     a.num_compute = fused ? h->compute_wgs : h->grid;
     a.num_reducers = fused ? h->reducer_wgs : 0;
@@ -548,8 +652,10 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // (a GEMM-only launch runs on the compute workgroups' grid: the
     // co-resident reducers' extra workgroup per CU is not part of the GEMM)
     if (!fused) a.num_compute = h->gemm_grid;
+    if (timed >= 0) HIP_TRY(hipEventRecord(h->split.ev[timed][0], s));
     HIP_TRY(hipLaunchKernel(k, dim3(fused ? h->grid : h->gemm_grid), dim3(h->td.threads), params,
                             fused ? h->fused_lds : h->td.lds_bytes, s));
+    if (timed >= 0) HIP_TRY(hipEventRecord(h->split.ev[timed][1], s));
     return GEMM_RS_OK;
 }
 
@@ -737,6 +843,7 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->reduce_grid = h->reduce_grid;
     info->xcd_split = h->strided;
     info->reduce_mode = h->reduce_mode;
+    info->split_state = !h->split.on ? 0 : (h->split.settled ? 2 : 1);
     // every workgroup's finish mark holds the epoch of the last fused launch
     HIP_TRY(hipStreamSynchronize(h->last_stream));
     HIP_TRY(hipMemcpy(&info->epoch, h->finished, sizeof info->epoch, hipMemcpyDeviceToHost));

@@ -66,7 +66,8 @@ class gemm_rs_info(ctypes.Structure):
         "bm", "bn", "bk", "group_m", "tiles", "tiles_per_slice", "tile_rows_per_slice",
         "tile_cols", "grid", "compute_wgs", "reducer_wgs", "num_cus", "wgs_per_cu",
         "lds_bytes", "reduce_grid", "xcd_split")] + [("epoch", ctypes.c_uint32),
-                                                     ("reduce_mode", ctypes.c_int32)]
+                                                     ("reduce_mode", ctypes.c_int32),
+                                                     ("split_state", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

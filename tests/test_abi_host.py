@@ -73,7 +73,10 @@ def cfg(**kw):
     (dict(flag_stride=2), gr.ERR_INVALID_ARG),
     (dict(debug_flags=4), gr.ERR_INVALID_ARG),
     (dict(drop_flag=100000), gr.ERR_INVALID_ARG),
-    (dict(num_reducers=-2), gr.ERR_INVALID_ARG),
+    (dict(num_reducers=-3), gr.ERR_INVALID_ARG),
+    (dict(num_reducers=-2), gr.OK),
+    (dict(num_reducers=-2, engine_interval=2), gr.ERR_INVALID_ARG),
+    (dict(num_reducers=-2, reduce_mode="stream"), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.OK),

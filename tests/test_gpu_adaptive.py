@@ -1,0 +1,75 @@
+"""GPU tests of the adaptive split (num_reducers = -2): the first uncaptured
+fused runs are timed with 0, 8, 16, 32 and 64 dedicated reducer workgroups,
+and the fastest count is kept.  Every count gives the same result, so every
+run must equal the oracle bit for bit (integer inputs) while the split moves.
+"""
+import numpy as np
+import torch
+
+import oracle
+import synthetic
+from tensor_gemm_reduce_amd import gemm_rs as gr
+from gpu_util import SENTINEL, Buffers, dev, host
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+CANDIDATES = {0, 8, 16, 32, 64}
+
+
+def test_adaptive_split_settles_and_every_run_is_exact():
+    cfg = synthetic.Config("adaptive", 19, 8 * 512, 2048, 256)  # 256x256 tiles, 2 rounds
+    rank = 3
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    want = dev(oracle.gemm_rs(x, w, peers, 8, rank)[2])
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, num_reducers=-2)
+    assert op.info.split_state == 1
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    fill = np.array(SENTINEL, np.uint16).view(np.int16).item()
+    seen = set()
+    for it in range(16):
+        b.out.fill_(fill)
+        op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local)
+        torch.cuda.synchronize()
+        assert op.status() == gr.OK
+        assert torch.equal(b.out, want), it
+        seen.add(gr.gemm_rs_query(op.h).reducer_wgs)
+    info = gr.gemm_rs_query(op.h)
+    assert info.split_state == 2
+    assert info.reducer_wgs in CANDIDATES
+    assert info.compute_wgs + info.reducer_wgs == info.grid
+    assert len(seen) >= 2  # the candidates were actually run
+    # and the settled split keeps giving the oracle's slice, also from a graph
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.out.fill_(fill)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert op.status() == gr.OK
+        assert torch.equal(b.out, want)
+
+
+def test_adaptive_split_under_capture_uses_no_reducers():
+    cfg = synthetic.CONFIGS["tiny"]
+    rank = 1
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    want = oracle.gemm_rs(x, w, peers, 8, rank)[2]
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, num_reducers=-2)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert op.status() == gr.OK
+    assert np.array_equal(host(b.out), want)
+    assert gr.gemm_rs_query(op.h).split_state == 1  # nothing was timed under capture
