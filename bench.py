@@ -57,6 +57,8 @@ def parse():
                    help="dedicated reducer workgroups: -1 the plan's default, -2 adaptive")
     p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "stream", "coresident", "epilogue"],
                    help="where the fused launch sums the slice without dedicated reducers")
+    p.add_argument("--tile-stores", default="device", choices=["device", "nt"],
+                   help="cache policy of the routed tile stores (nt: non-temporal hint)")
     p.add_argument("--engine-interval", type=int, default=0,
                    help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
     p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
@@ -109,7 +111,7 @@ class Case:
         self.out = z()
         self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
                             num_reducers=args.reducers, engine_interval=args.engine_interval,
-                            reduce_mode=args.reduce_mode)
+                            reduce_mode=args.reduce_mode, tile_stores=args.tile_stores)
         # the adaptive split (reducers -2) times its candidates on uncaptured
         # runs: give it those before anything is captured into a graph
         if args.reducers == -2:
@@ -123,7 +125,7 @@ class Case:
         if self.op.info.reduce_mode in (gr.REDUCE_STREAM, gr.REDUCE_CORESIDENT, gr.REDUCE_EPILOGUE):
             self.op_tail = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
                                      num_reducers=args.reducers, engine_interval=args.engine_interval,
-                                     reduce_mode="tail")
+                                     reduce_mode="tail", tile_stores=args.tile_stores)
         self.gr = gr
 
     def run(self, mode):
@@ -409,6 +411,7 @@ SPLIT_KNOBS = (
     [dict(num_reducers=r) for r in (0, 2, 4, 8, 16, 32, 64)]
     + [dict(num_reducers=r, flag_stride=32) for r in (0, 8, 64)]
     + [dict(num_reducers=0, engine_interval=n) for n in (1, 4)]
+    + [dict(num_reducers=r, tile_stores=1) for r in (0, 8, 64)]
 )
 
 
@@ -447,6 +450,7 @@ def split_sweep(args):
         st = op.status()
         tf = statistics.median(t[f"k{i}"])
         rows.append({**kw, "flag_stride": kw.get("flag_stride", 1), "engine_interval": kw.get("engine_interval", 0),
+                     "tile_stores": kw.get("tile_stores", 0),
                      "compute_wgs": op.info.compute_wgs, "reducer_wgs": op.info.reducer_wgs,
                      "T_fused_us": tf, "fused_tflops": cfg.flops / tf * 1e-6,
                      "overlap": 1.0 - (tf - tg) / tr, "out_matches_default": same[i],
@@ -692,6 +696,7 @@ def main():
         "T_reduce_us": m["T_reduce_us"]["median_us"],
         "reduce_gbs": m["reduce_gbs"],
         "reduce_mode": m["reduce_mode"],
+        "tile_stores": args.tile_stores,
         "T_fused_tail_us": (m.get("T_fused_tail_us") or {}).get("median_us"),
         "overlap_tail": m.get("overlap_tail"),
         "parity": check,

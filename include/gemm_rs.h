@@ -111,6 +111,11 @@ extern "C" {
                                    and the tile's peer values, loaded ahead of the
                                    tile's first stage (16x64 and 64x128 tiles)   */
 
+/* ---- cache policy of the routed tile stores ------------------------------ */
+#define GEMM_RS_STORES_DEVICE 0      /* device scope, written through L2        */
+#define GEMM_RS_STORES_NONTEMPORAL 1 /* device scope with the non-temporal hint:
+                                        the tiles are not kept in L2 for reuse  */
+
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
                                  the compute workgroup and a release timestamp */
@@ -143,6 +148,9 @@ typedef struct gemm_rs_config {
                              num_reducers <= 0 and engine_interval == 0;
                              STREAM needs the 256x256 tile, EPILOGUE the
                              16x64 or 64x128 tile                            */
+    int32_t tile_stores;  /* GEMM_RS_STORES_*: cache policy of the tile stores
+                             into the destination slices (every mode and entry
+                             point that routes tiles)                        */
 } gemm_rs_config;
 
 typedef struct gemm_rs_info {

@@ -284,6 +284,8 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
     if (c->watchdog_us < 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (c->tile_stores != GEMM_RS_STORES_DEVICE && c->tile_stores != GEMM_RS_STORES_NONTEMPORAL)
+        return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_EPILOGUE)
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL &&
@@ -610,6 +612,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
     a.engine_every = h->cfg.engine_interval;
     a.coresident = h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT ? 1 : 0;
+    a.nt_stores = h->cfg.tile_stores == GEMM_RS_STORES_NONTEMPORAL ? 1 : 0;
 }
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)

@@ -71,6 +71,11 @@ constexpr int kStoreDevice = 16;
 // run is never used.
 constexpr int kAuxNt = 2;
 constexpr int kAuxSc1 = 16;
+// Routed tile stores with the non-temporal hint on top of device scope: the
+// tile is not read back through this XCD's L2 (the sum reads the local slice
+// at device scope, the send buffers leave the GPU), so it need not displace
+// the GEMM's operands there.
+constexpr int kStoreDeviceNt = kStoreDevice | kAuxNt;
 
 // Reduce engine: 16-byte loads per operation (one per lane each), LDS bytes an
 // operation lands in, operations in flight per engine wave.
@@ -114,6 +119,7 @@ struct Args {
     int32_t engine_every;    // K steps between reduce-engine slots (0: reduce after the last tile)
     int32_t coresident;      // 1: the reducer workgroups sit beside the compute workgroups of
                              // their CUs and sum a static share of items (peers first)
+    int32_t nt_stores;       // 1: routed tiles are stored with the non-temporal hint
     // all-gather + GEMM runs (the column-parallel layer): M x K gathered
     // activations times this rank's N x K weight shard
     const uint16_t* xsrc[8];  // row slice [S][K] of source rank d; xsrc[rank] is this rank's own
@@ -403,7 +409,8 @@ __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsr
 // then the wave reads 8 rows x 8 chunks per instruction and stores them.
 template <class C>
 __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st, char* area,
-                                           __amdgpu_buffer_rsrc_t rd, int row0, int rows, int n0, int cols)
+                                           __amdgpu_buffer_rsrc_t rd, int row0, int rows, int n0, int cols,
+                                           bool nt = false)
 {
     const int lane = threadIdx.x & 63;
     const int wave = uni((int)(threadIdx.x >> 6));
@@ -440,7 +447,10 @@ __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st
                     const int m = wm * C::WTM + i * 32 + row;
                     const uint32_t off =
                         (m < rows && n < cols) ? (((uint32_t)(row0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, kStoreDevice);
+                    if (nt)
+                        __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, kStoreDeviceNt);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, kStoreDevice);
                 }
                 __asm__ __volatile__("" ::: "memory");
             }
@@ -459,7 +469,10 @@ __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st
                                      pack_bf16x2(st.acc[i][j][grp * 4 + 2], st.acc[i][j][grp * 4 + 3])};
                     const uint32_t off =
                         (m < rows && n < cols) ? (((uint32_t)(row0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, kStoreDevice);
+                    if (nt)
+                        __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, kStoreDeviceNt);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, kStoreDevice);
                 }
             }
         }
@@ -1574,7 +1587,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         // epilogue staging areas
         const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.dst[t.d], 0, a.slice_bytes, kRsrcFlags);
         store_tile<C>(a, st, lds + (C::NS - 1) * C::STAGE_BYTES, rd, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN,
-                      tile_cols(a.g, t));
+                      tile_cols(a.g, t), uni(a.nt_stores) != 0);
         if constexpr (EPI) {
             if (t.d == a.g.rank) {
                 TileState<C> os;

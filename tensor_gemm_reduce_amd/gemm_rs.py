@@ -45,6 +45,10 @@ REDUCE_CORESIDENT = 3
 REDUCE_EPILOGUE = 4
 REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2, "coresident": 3, "epilogue": 4}
 
+STORES_DEVICE = 0
+STORES_NONTEMPORAL = 1
+TILE_STORES = {"device": 0, "nt": 1}
+
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
@@ -58,7 +62,8 @@ class gemm_rs_config(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("num_reducers", ctypes.c_int32),
                 ("engine_interval", ctypes.c_int32), ("debug_flags", ctypes.c_int32),
                 ("drop_flag", ctypes.c_int32), ("flag_stride", ctypes.c_int32),
-                ("watchdog_us", ctypes.c_int64), ("reduce_mode", ctypes.c_int32)]
+                ("watchdog_us", ctypes.c_int64), ("reduce_mode", ctypes.c_int32),
+                ("tile_stores", ctypes.c_int32)]
 
 
 class gemm_rs_info(ctypes.Structure):
@@ -132,13 +137,15 @@ def _check(code: int, what: str) -> int:
 
 def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_reducers=-1,
                 engine_interval=0, debug_flags=0, drop_flag=-1, flag_stride=1,
-                watchdog_us=0, reduce_mode=REDUCE_AUTO) -> gemm_rs_config:
+                watchdog_us=0, reduce_mode=REDUCE_AUTO, tile_stores=STORES_DEVICE) -> gemm_rs_config:
     if isinstance(tile, str):
         tile = TILES[tile]
     if isinstance(reduce_mode, str):
         reduce_mode = REDUCE_MODES[reduce_mode]
+    if isinstance(tile_stores, str):
+        tile_stores = TILE_STORES[tile_stores]
     return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers, engine_interval,
-                          debug_flags, drop_flag, flag_stride, watchdog_us, reduce_mode)
+                          debug_flags, drop_flag, flag_stride, watchdog_us, reduce_mode, tile_stores)
 
 
 # ---- C names ------------------------------------------------------------------

@@ -77,6 +77,10 @@ def cfg(**kw):
     (dict(num_reducers=-2), gr.OK),
     (dict(num_reducers=-2, engine_interval=2), gr.ERR_INVALID_ARG),
     (dict(num_reducers=-2, reduce_mode="stream"), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="nt"), gr.OK),
+    (dict(tile_stores="nt", num_reducers=8), gr.OK),
+    (dict(tile_stores=2), gr.ERR_INVALID_ARG),
+    (dict(tile_stores=-1), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.OK),

@@ -25,6 +25,8 @@ REDUCERS = list(REDUCE)
 # the sum streamed through the K loop (256x256 tile only; the automatic choice
 # sums after the last tile)
 REDUCE["stream"] = dict(num_reducers=0, reduce_mode="stream")
+# the automatic placement with the routed tiles stored non-temporally
+REDUCE["nt"] = dict(tile_stores="nt")
 
 
 def _op(cfg, M=None, **kw):
@@ -163,7 +165,7 @@ def test_error_within_1p1x_of_unfused_path(name, mode):
 
 # ------------------------------------------------------------------ full shapes, sampled rows
 
-@pytest.mark.parametrize("red", ["bench", "stream", "engine_loop3", "reducers8"])
+@pytest.mark.parametrize("red", ["bench", "stream", "engine_loop3", "reducers8", "nt"])
 @pytest.mark.parametrize("name", ["o_proj", "down_proj", "mixtral_down", "large_prefill"])
 @pytest.mark.parametrize("mode", ["normal", "integer"])
 def test_benchmark_shapes_sampled_rows(name, mode, red):
@@ -224,6 +226,9 @@ def test_modes_agree_bit_exactly():
     dict(num_reducers=0, tile="128x128", group_m=3), dict(num_reducers=0, tile="256x256"),
     dict(num_reducers=8, flag_stride=32, tile="128x256"),
     dict(num_reducers=0, engine_interval=1, flag_stride=32), dict(num_reducers=0, engine_interval=5, tile="16x64"),
+    dict(tile_stores="nt"), dict(tile_stores="nt", num_reducers=8), dict(tile_stores="nt", tile="64x128"),
+    dict(tile_stores="nt", tile="16x64", reduce_mode="epilogue"),
+    dict(tile_stores="nt", tile="256x256", reduce_mode="stream"),
 ])
 def test_knobs_keep_results(kw):
     cfg = synthetic.CONFIGS["mixtral_down"]

@@ -102,7 +102,8 @@ def test_alternating_inputs_never_read_stale_tiles():
     shared_send, shared_local, shared_out = bufs[0].send, bufs[0].local, bufs[0].out
     for kw in (dict(num_reducers=0), dict(num_reducers=0, tile="128x128"), dict(num_reducers=8),
                dict(num_reducers=1), dict(num_reducers=0, engine_interval=1),
-               dict(num_reducers=0, engine_interval=2, tile="128x128")):
+               dict(num_reducers=0, engine_interval=2, tile="128x128"), dict(tile_stores="nt"),
+               dict(num_reducers=8, tile_stores="nt")):
         op = gr.GemmRS(base.M, base.N, base.K_local, rank=rank, **kw)
         bad = 0
         for it in range(40):
