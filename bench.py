@@ -59,6 +59,9 @@ def parse():
                    help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--tile-stores", default="device", choices=["device", "nt"],
                    help="cache policy of the routed tile stores (nt: non-temporal hint)")
+    p.add_argument("--cold", action="store_true",
+                   help="also time the fused, GEMM-only and reduce launches with cold caches (a 512 MiB "
+                        "buffer written before each launch)")
     p.add_argument("--engine-interval", type=int, default=0,
                    help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
     p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
@@ -91,6 +94,7 @@ class Case:
     """Device inputs/outputs and a handle for one benchmark shape."""
 
     def __init__(self, name, args, rank=0):
+        self.args = args
         import numpy as np
         import torch
 
@@ -229,6 +233,35 @@ def time_interleaved(fns, warmup_s=0.3, rounds=20, per_graph=10):
     return {k: [s.elapsed_time(e) * 1e3 / per_graph for s, e in v] for k, v in ev.items()}
 
 
+def time_cold(fns, rounds=20, flush_bytes=512 << 20):
+    """Per-launch times (us) with cold caches: before every launch a
+    flush_bytes buffer (twice the 256 MiB last-level cache) is written on the
+    same stream, outside the events that bracket the launch.  Launches are
+    eager (one launch per event pair), in rotating order."""
+    import torch
+
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    names = list(fns)
+    stream = torch.cuda.current_stream()
+    for k in names:  # first launches (and the adaptive split's timing) untimed
+        flush.fill_(0)
+        fns[k]()
+    torch.cuda.synchronize()
+    ev = {k: [] for k in names}
+    for r in range(rounds):
+        order = names[r % len(names):] + names[:r % len(names)]
+        for k in order:
+            flush.fill_(r & 0xFF)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fns[k]()
+            e.record(stream)
+            ev[k].append((s, e))
+    torch.cuda.synchronize()
+    del flush
+    return {k: [s.elapsed_time(e) * 1e3 for s, e in v] for k, v in ev.items()}
+
+
 def summary(us):
     q = statistics.quantiles(us, n=10) if len(us) >= 2 else [us[0]] * 9
     return {"median_us": statistics.median(us), "mean_us": statistics.fmean(us), "p10_us": q[0],
@@ -257,6 +290,13 @@ def measure_case(c: Case, warmup, iters):
     if c.op_tail is not None:
         tail = summary(t["fused_tail"])
         extra = {"T_fused_tail_us": tail, "overlap_tail": 1.0 - (tail["median_us"] - tg) / tr}
+    if c.args.cold:
+        tc = time_cold({k: fns[k] for k in ("fused", "gemm", "reduce")}, rounds=max(5, -(-iters // 10)))
+        cf, cg, cr = (statistics.median(tc[k]) for k in ("fused", "gemm", "reduce"))
+        if c.op.status() != gr.OK:
+            raise RuntimeError(f"{c.name}: device status after the cold runs")
+        extra["cold"] = {"T_fused_us": cf, "T_gemm_us": cg, "T_reduce_us": cr,
+                         "fused_tflops": cfg.flops / cf * 1e-6, "overlap": 1.0 - (cf - cg) / cr}
     return {
         "shape": {"M": cfg.M, "N": cfg.N, "K_local": cfg.K_local, "tp": cfg.tp},
         "launch": c.op.info.as_dict(),
@@ -697,6 +737,7 @@ def main():
         "reduce_gbs": m["reduce_gbs"],
         "reduce_mode": m["reduce_mode"],
         "tile_stores": args.tile_stores,
+        "cold": m.get("cold"),
         "T_fused_tail_us": (m.get("T_fused_tail_us") or {}).get("median_us"),
         "overlap_tail": m.get("overlap_tail"),
         "parity": check,
@@ -711,6 +752,7 @@ def main():
                        "reduce_mode": v.get("reduce_mode"),
                        "T_fused_tail_us": (v.get("T_fused_tail_us") or {}).get("median_us"),
                        "overlap_tail": v.get("overlap_tail"),
+                       "cold": v.get("cold"),
                        "parity_ok": (v.get("parity") or {}).get("ok")} if "error" not in v else v)
                   for k, v in sweep.items()},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
