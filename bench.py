@@ -452,6 +452,7 @@ SPLIT_KNOBS = (
     + [dict(num_reducers=r, flag_stride=32) for r in (0, 8, 64)]
     + [dict(num_reducers=0, engine_interval=n) for n in (1, 4)]
     + [dict(num_reducers=r, tile_stores=1) for r in (0, 8, 64)]
+    + [dict(num_reducers=r, flag_protocol=1) for r in (0, 8, 64)]
 )
 
 
@@ -491,6 +492,7 @@ def split_sweep(args):
         tf = statistics.median(t[f"k{i}"])
         rows.append({**kw, "flag_stride": kw.get("flag_stride", 1), "engine_interval": kw.get("engine_interval", 0),
                      "tile_stores": kw.get("tile_stores", 0),
+                     "flag_protocol": kw.get("flag_protocol", 0),
                      "compute_wgs": op.info.compute_wgs, "reducer_wgs": op.info.reducer_wgs,
                      "T_fused_us": tf, "fused_tflops": cfg.flops / tf * 1e-6,
                      "overlap": 1.0 - (tf - tg) / tr, "out_matches_default": same[i],

@@ -116,6 +116,18 @@ extern "C" {
 #define GEMM_RS_STORES_NONTEMPORAL 1 /* device scope with the non-temporal hint:
                                         the tiles are not kept in L2 for reuse  */
 
+/* ---- how a released tile is signalled ------------------------------------ */
+#define GEMM_RS_FLAGS_TILE 0        /* one ready flag per tile, set to the run's
+                                       epoch                                    */
+#define GEMM_RS_FLAGS_ROW_COUNTER 1 /* one counter per tile row (destination
+                                       slice, tile row), atomically incremented
+                                       per released tile and never reset; a tile
+                                       is summed once its row's counter reaches
+                                       epoch x tile columns.  Not with in-loop
+                                       engine slots or the reduce stream.  After
+                                       a watchdog timeout the counters are one
+                                       short for good: create a new handle.     */
+
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
                                  the compute workgroup and a release timestamp */
@@ -151,6 +163,7 @@ typedef struct gemm_rs_config {
     int32_t tile_stores;  /* GEMM_RS_STORES_*: cache policy of the tile stores
                              into the destination slices (every mode and entry
                              point that routes tiles)                        */
+    int32_t flag_protocol; /* GEMM_RS_FLAGS_*                                 */
 } gemm_rs_config;
 
 typedef struct gemm_rs_info {

@@ -286,6 +286,13 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->watchdog_us < 0) return GEMM_RS_ERR_INVALID_ARG;
     if (c->tile_stores != GEMM_RS_STORES_DEVICE && c->tile_stores != GEMM_RS_STORES_NONTEMPORAL)
         return GEMM_RS_ERR_INVALID_ARG;
+    if (c->flag_protocol != GEMM_RS_FLAGS_TILE && c->flag_protocol != GEMM_RS_FLAGS_ROW_COUNTER)
+        return GEMM_RS_ERR_INVALID_ARG;
+    // row counters are read by the sum after the last tile and by dedicated or
+    // co-resident reducers; the in-loop engine and the stream poll tile flags
+    if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER &&
+        (c->engine_interval > 0 || c->reduce_mode == GEMM_RS_REDUCE_STREAM))
+        return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_EPILOGUE)
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL &&
@@ -613,6 +620,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.engine_every = h->cfg.engine_interval;
     a.coresident = h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT ? 1 : 0;
     a.nt_stores = h->cfg.tile_stores == GEMM_RS_STORES_NONTEMPORAL ? 1 : 0;
+    a.row_counter = h->cfg.flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER ? 1 : 0;
 }
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)

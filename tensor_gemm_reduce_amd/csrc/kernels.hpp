@@ -120,6 +120,8 @@ struct Args {
     int32_t coresident;      // 1: the reducer workgroups sit beside the compute workgroups of
                              // their CUs and sum a static share of items (peers first)
     int32_t nt_stores;       // 1: routed tiles are stored with the non-temporal hint
+    int32_t row_counter;     // 1: a counter per tile row (destination slice, tile row) counts the
+                             // tiles released in that row, summed over runs; 0: a flag per tile
     // all-gather + GEMM runs (the column-parallel layer): M x K gathered
     // activations times this rank's N x K weight shard
     const uint16_t* xsrc[8];  // row slice [S][K] of source rank d; xsrc[rank] is this rank's own
@@ -491,9 +493,31 @@ __device__ __forceinline__ void publish(const Args& a, int q, int flag, uint32_t
         tr[2] = (uint32_t)now;
         tr[3] = (uint32_t)(now >> 32);
     }
-    if (flag != a.drop_flag)
-        __hip_atomic_store(a.flags + (int64_t)flag * a.flag_stride, epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    if (flag != a.drop_flag) {
+        if (a.row_counter)
+            __hip_atomic_fetch_add(a.flags + (int64_t)(flag / a.g.tnc) * a.flag_stride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(a.flags + (int64_t)flag * a.flag_stride, epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The word that says whether tile `flag` of this run is released: its own
+// flag, or under the row-counter protocol its tile row's counter.
+__device__ __forceinline__ const uint32_t* ready_word(const Args& a, int flag)
+{
+    const int idx = a.row_counter ? flag / a.g.tnc : flag;
+    return a.flags + (int64_t)idx * a.flag_stride;
+}
+
+// Whether a ready word read in run `epoch` releases the tile: the flag holds
+// the epoch, or the row counter has reached epoch * (tiles per row) -- every
+// run adds one per tile, so the counter passes that value exactly when the
+// whole row of this run is stored (compared modulo 2^32).
+__device__ __forceinline__ bool released(const Args& a, uint32_t v, uint32_t epoch)
+{
+    return a.row_counter ? (int32_t)(v - epoch * (uint32_t)a.g.tnc) >= 0 : v == epoch;
 }
 
 // ---------------------------------------------------------------- slice sum
@@ -856,11 +880,11 @@ template <int SLEEP = 2>
 __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, bool& gave_up)
 {
     const int flag = a.g.rank * a.g.ts + t;
-    const uint32_t* f = a.flags + (int64_t)flag * a.flag_stride;
-    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
+    const uint32_t* f = ready_word(a, flag);
+    if (released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
     if (gave_up) return false;
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    while (!released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
         __builtin_amdgcn_s_sleep(SLEEP);
         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
             gave_up = true;
@@ -1668,10 +1692,10 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
             int abort_now = 0;
             if (u < a.g.ts) {
                 const TileCoord t = decode_slot(a.g, u);
-                const uint32_t* f = a.flags + (int64_t)t.flag * a.flag_stride;
-                if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+                const uint32_t* f = ready_word(a, t.flag);
+                if (!released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
                     const uint64_t t0 = wall_clock64();
-                    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+                    while (!released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
                         __builtin_amdgcn_s_sleep(2);
                         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
                             abort_now = 1;

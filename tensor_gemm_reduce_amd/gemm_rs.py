@@ -49,6 +49,10 @@ STORES_DEVICE = 0
 STORES_NONTEMPORAL = 1
 TILE_STORES = {"device": 0, "nt": 1}
 
+FLAGS_TILE = 0
+FLAGS_ROW_COUNTER = 1
+FLAG_PROTOCOLS = {"tile": 0, "row_counter": 1}
+
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
@@ -63,7 +67,7 @@ class gemm_rs_config(ctypes.Structure):
                 ("engine_interval", ctypes.c_int32), ("debug_flags", ctypes.c_int32),
                 ("drop_flag", ctypes.c_int32), ("flag_stride", ctypes.c_int32),
                 ("watchdog_us", ctypes.c_int64), ("reduce_mode", ctypes.c_int32),
-                ("tile_stores", ctypes.c_int32)]
+                ("tile_stores", ctypes.c_int32), ("flag_protocol", ctypes.c_int32)]
 
 
 class gemm_rs_info(ctypes.Structure):
@@ -137,15 +141,19 @@ def _check(code: int, what: str) -> int:
 
 def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_reducers=-1,
                 engine_interval=0, debug_flags=0, drop_flag=-1, flag_stride=1,
-                watchdog_us=0, reduce_mode=REDUCE_AUTO, tile_stores=STORES_DEVICE) -> gemm_rs_config:
+                watchdog_us=0, reduce_mode=REDUCE_AUTO, tile_stores=STORES_DEVICE,
+                flag_protocol=FLAGS_TILE) -> gemm_rs_config:
     if isinstance(tile, str):
         tile = TILES[tile]
     if isinstance(reduce_mode, str):
         reduce_mode = REDUCE_MODES[reduce_mode]
     if isinstance(tile_stores, str):
         tile_stores = TILE_STORES[tile_stores]
+    if isinstance(flag_protocol, str):
+        flag_protocol = FLAG_PROTOCOLS[flag_protocol]
     return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers, engine_interval,
-                          debug_flags, drop_flag, flag_stride, watchdog_us, reduce_mode, tile_stores)
+                          debug_flags, drop_flag, flag_stride, watchdog_us, reduce_mode, tile_stores,
+                          flag_protocol)
 
 
 # ---- C names ------------------------------------------------------------------

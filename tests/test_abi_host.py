@@ -81,6 +81,12 @@ def cfg(**kw):
     (dict(tile_stores="nt", num_reducers=8), gr.OK),
     (dict(tile_stores=2), gr.ERR_INVALID_ARG),
     (dict(tile_stores=-1), gr.ERR_INVALID_ARG),
+    (dict(flag_protocol="row_counter"), gr.OK),
+    (dict(flag_protocol="row_counter", num_reducers=8), gr.OK),
+    (dict(flag_protocol="row_counter", num_reducers=-2), gr.OK),
+    (dict(flag_protocol="row_counter", engine_interval=1), gr.ERR_INVALID_ARG),
+    (dict(flag_protocol="row_counter", reduce_mode="stream"), gr.ERR_INVALID_ARG),
+    (dict(flag_protocol=2), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.OK),

@@ -27,6 +27,8 @@ REDUCERS = list(REDUCE)
 REDUCE["stream"] = dict(num_reducers=0, reduce_mode="stream")
 # the automatic placement with the routed tiles stored non-temporally
 REDUCE["nt"] = dict(tile_stores="nt")
+# the automatic placement with a released-tile counter per tile row
+REDUCE["rowc"] = dict(flag_protocol="row_counter")
 
 
 def _op(cfg, M=None, **kw):
@@ -165,7 +167,7 @@ def test_error_within_1p1x_of_unfused_path(name, mode):
 
 # ------------------------------------------------------------------ full shapes, sampled rows
 
-@pytest.mark.parametrize("red", ["bench", "stream", "engine_loop3", "reducers8", "nt"])
+@pytest.mark.parametrize("red", ["bench", "stream", "engine_loop3", "reducers8", "nt", "rowc"])
 @pytest.mark.parametrize("name", ["o_proj", "down_proj", "mixtral_down", "large_prefill"])
 @pytest.mark.parametrize("mode", ["normal", "integer"])
 def test_benchmark_shapes_sampled_rows(name, mode, red):
@@ -229,6 +231,8 @@ def test_modes_agree_bit_exactly():
     dict(tile_stores="nt"), dict(tile_stores="nt", num_reducers=8), dict(tile_stores="nt", tile="64x128"),
     dict(tile_stores="nt", tile="16x64", reduce_mode="epilogue"),
     dict(tile_stores="nt", tile="256x256", reduce_mode="stream"),
+    dict(flag_protocol="row_counter"), dict(flag_protocol="row_counter", num_reducers=8),
+    dict(flag_protocol="row_counter", tile="16x64", flag_stride=32),
 ])
 def test_knobs_keep_results(kw):
     cfg = synthetic.CONFIGS["mixtral_down"]

@@ -103,7 +103,8 @@ def test_alternating_inputs_never_read_stale_tiles():
     for kw in (dict(num_reducers=0), dict(num_reducers=0, tile="128x128"), dict(num_reducers=8),
                dict(num_reducers=1), dict(num_reducers=0, engine_interval=1),
                dict(num_reducers=0, engine_interval=2, tile="128x128"), dict(tile_stores="nt"),
-               dict(num_reducers=8, tile_stores="nt")):
+               dict(num_reducers=8, tile_stores="nt"), dict(flag_protocol="row_counter"),
+               dict(num_reducers=8, flag_protocol="row_counter")):
         op = gr.GemmRS(base.M, base.N, base.K_local, rank=rank, **kw)
         bad = 0
         for it in range(40):
@@ -151,3 +152,52 @@ def test_graph_replays_match_eager(red):
             run(op, b)  # an eager run between replays
             assert torch.equal(b.out, want)
     assert gr.gemm_rs_query(op.h).epoch == 1 + 6 + 3
+
+
+ROWC = synthetic.Config("rowc", 21, 8 * 64, 1024, 128)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(num_reducers=8), dict(flag_stride=32)], ids=["tail", "reducers8", "padded"])
+def test_row_counters_count_every_tile_of_every_run(kw):
+    """Under the row-counter protocol each (destination slice, tile row) word
+    holds runs x tile columns after every run, and the words past the last
+    tile row stay zero."""
+    cfg = ROWC  # four tile rows per slice
+    rank = 3
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    want = oracle.gemm_rs(x, w, peers, 8, rank)[2]
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile="16x64", flag_protocol="row_counter", **kw)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    info = op.info
+    rows = 8 * info.tile_rows_per_slice
+    for epoch in (1, 2, 3):
+        b.refill()
+        run(op, b)
+        assert np.array_equal(host(b.out), want)
+        _, words = op.debug_read()
+        assert np.all(words[:rows] == epoch * info.tile_cols), (epoch, words[:rows])
+        assert np.all(words[rows:] == 0)
+
+
+@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=8)], ids=["tail", "reducers8"])
+def test_row_counter_watchdog_skips_the_dropped_row(red):
+    """A tile whose release is dropped leaves its row's counter one short: the
+    watchdog reports it and the sum skips that whole tile row of the slice;
+    every other row is summed."""
+    cfg = ROWC  # four tile rows per slice
+    rank = 2
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    plan = gr.gemm_rs_plan(gr.make_config(cfg.M, cfg.N, cfg.K_local, rank=rank, tile="16x64"))
+    assert plan.tile_rows_per_slice == 4
+    sched = oracle.schedule(cfg.M, cfg.N, 8, rank, plan.bm, plan.bn, plan.group_m)
+    dropped = int(sched["flag"][0])  # first tile of the own slice: tile row 0
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile="16x64", drop_flag=dropped, watchdog_us=2000,
+                   flag_protocol="row_counter", **red)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    run(op, b, check_status=False)
+    assert op.status() == gr.ERR_TIMEOUT
+    send_o, local_o, out_o = oracle.gemm_rs(x, w, peers, tp=8, rank=rank)
+    assert np.array_equal(host(b.local), local_o)
+    got = host(b.out)
+    assert np.all(got[:plan.bm] == SENTINEL)
+    assert np.array_equal(got[plan.bm:], out_o[plan.bm:])
