@@ -114,7 +114,12 @@ extern "C" {
 /* ---- cache policy of the routed tile stores ------------------------------ */
 #define GEMM_RS_STORES_DEVICE 0      /* device scope, written through L2        */
 #define GEMM_RS_STORES_NONTEMPORAL 1 /* device scope with the non-temporal hint:
-                                        the tiles are not kept in L2 for reuse  */
+                                        the tiles are not kept in L2 for reuse.
+                                        A separate kernel variant: with the sum
+                                        after the last tile, dedicated or
+                                        co-resident reducers and GEMM_ONLY; not
+                                        with engine slots, the stream, the
+                                        epilogue sum or row counters            */
 
 /* ---- how a released tile is signalled ------------------------------------ */
 #define GEMM_RS_FLAGS_TILE 0        /* one ready flag per tile, set to the run's
@@ -123,8 +128,9 @@ extern "C" {
                                        slice, tile row), atomically incremented
                                        per released tile and never reset; a tile
                                        is summed once its row's counter reaches
-                                       epoch x tile columns.  Not with in-loop
-                                       engine slots or the reduce stream.  After
+                                       epoch x tile columns.  A separate kernel
+                                       variant: not with in-loop engine slots,
+                                       the reduce stream or the epilogue sum.  After
                                        a watchdog timeout the counters are one
                                        short for good: create a new handle.     */
 

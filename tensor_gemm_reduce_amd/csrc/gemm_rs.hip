@@ -59,6 +59,9 @@ struct TileDesc {
     int stream_lds_bytes;      // its LDS: stages + the streaming waves' slots
     const void* kernel;        // fused: dedicated reducer workgroups
     const void* gemm_kernel;   // the same GEMM without flags or reduction
+    const void* kernel_nt;     // `kernel` storing routed tiles non-temporally
+    const void* gemm_kernel_nt;  // `gemm_kernel` storing routed tiles non-temporally
+    const void* kernel_rows;   // `kernel` reading row counters
     const void* ag_kernel;     // all-gather + GEMM: copy phase, then the GEMM waiting for rows
     const void* ag_gemm_kernel;  // the same GEMM over an already gathered buffer
     const void* epi_kernel;    // fused: own tiles summed in their producer's epilogue (or null)
@@ -67,15 +70,15 @@ struct TileDesc {
 // Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
 // tiles that cannot fit two workgroups per CU get the occupancy-1 kernel (one
 // wave per SIMD, the whole register file).
-template <class C, bool FUSED, bool TWO_PER_CU>
+template <class C, bool FUSED, bool TWO_PER_CU, int VAR = 0>
 const void* kernel_for()
 {
     if constexpr (C::WAVES == 8)
-        return reinterpret_cast<const void*>(&fused_kernel_8w<C, FUSED>);
+        return reinterpret_cast<const void*>(&fused_kernel_8w<C, FUSED, false, VAR>);
     else if constexpr (TWO_PER_CU)
-        return reinterpret_cast<const void*>(&fused_kernel<C, FUSED>);
+        return reinterpret_cast<const void*>(&fused_kernel<C, FUSED, false, VAR>);
     else
-        return reinterpret_cast<const void*>(&fused_kernel_1w<C, FUSED>);
+        return reinterpret_cast<const void*>(&fused_kernel_1w<C, FUSED, VAR>);
 }
 
 template <class C, bool FUSED, bool TWO_PER_CU>
@@ -117,6 +120,8 @@ TileDesc desc()
     return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, elds, C::LDS_BYTES,
                     kernel_for<CE, true, two>(), sk, stream ? slds : 0,
                     kernel_for<C, true, two>(), kernel_for<C, false, two>(),
+                    kernel_for<C, true, two, kVarNt>(), kernel_for<C, false, two, kVarNt>(),
+                    kernel_for<C, true, two, kVarRows>(),
                     ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), epi_kernel_for<C>()};
 }
 
@@ -129,7 +134,8 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, 0, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+    default: return TileDesc{0,       0,       0,       0,       0,       0,       0,       nullptr, nullptr,
+                             0,       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
     }
 }
 
@@ -292,6 +298,14 @@ int gemm_rs_validate(const gemm_rs_config* c)
     // co-resident reducers; the in-loop engine and the stream poll tile flags
     if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER &&
         (c->engine_interval > 0 || c->reduce_mode == GEMM_RS_REDUCE_STREAM))
+        return GEMM_RS_ERR_INVALID_ARG;
+    // both are kernel variants of the tail sum / reducer-workgroup kernel
+    // (and, for the stores, of the GEMM-only kernel); one at a time
+    if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL &&
+        (c->engine_interval > 0 || c->reduce_mode == GEMM_RS_REDUCE_STREAM ||
+         c->reduce_mode == GEMM_RS_REDUCE_EPILOGUE || c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER))
+        return GEMM_RS_ERR_INVALID_ARG;
+    if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER && c->reduce_mode == GEMM_RS_REDUCE_EPILOGUE)
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_EPILOGUE)
         return GEMM_RS_ERR_INVALID_ARG;
@@ -459,6 +473,13 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     h->g = geometry_of(*c);
     h->tile_id = resolve_tile(*c);
     h->td = tile_desc(h->tile_id);
+    // the kernel variant of the requested store policy or flag protocol
+    if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL) {
+        h->td.kernel = h->td.kernel_nt;
+        h->td.gemm_kernel = h->td.gemm_kernel_nt;
+    } else if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER) {
+        h->td.kernel = h->td.kernel_rows;
+    }
     h->device = dev;
     h->num_cus = prop.multiProcessorCount;
     h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
@@ -619,8 +640,6 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
     a.engine_every = h->cfg.engine_interval;
     a.coresident = h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT ? 1 : 0;
-    a.nt_stores = h->cfg.tile_stores == GEMM_RS_STORES_NONTEMPORAL ? 1 : 0;
-    a.row_counter = h->cfg.flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER ? 1 : 0;
 }
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)

@@ -77,6 +77,12 @@ constexpr int kAuxSc1 = 16;
 // the GEMM's operands there.
 constexpr int kStoreDeviceNt = kStoreDevice | kAuxNt;
 
+// Kernel variants (a template parameter of the fused and GEMM kernels, so that
+// the default kernel carries no code of the others): bit 0 stores routed tiles
+// with kStoreDeviceNt, bit 1 reads row counters instead of tile flags.
+constexpr int kVarNt = 1;
+constexpr int kVarRows = 2;
+
 // Reduce engine: 16-byte loads per operation (one per lane each), LDS bytes an
 // operation lands in, operations in flight per engine wave.
 constexpr int kEngLoads = 2;
@@ -119,9 +125,6 @@ struct Args {
     int32_t engine_every;    // K steps between reduce-engine slots (0: reduce after the last tile)
     int32_t coresident;      // 1: the reducer workgroups sit beside the compute workgroups of
                              // their CUs and sum a static share of items (peers first)
-    int32_t nt_stores;       // 1: routed tiles are stored with the non-temporal hint
-    int32_t row_counter;     // 1: a counter per tile row (destination slice, tile row) counts the
-                             // tiles released in that row, summed over runs; 0: a flag per tile
     // all-gather + GEMM runs (the column-parallel layer): M x K gathered
     // activations times this rank's N x K weight shard
     const uint16_t* xsrc[8];  // row slice [S][K] of source rank d; xsrc[rank] is this rank's own
@@ -409,10 +412,10 @@ __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsr
 // 16-byte chunks) into the wave's LDS area, chunk k of row r at k ^ ((r>>1)&7)
 // so that both the 32-row writes and the 8-row reads spread over all banks;
 // then the wave reads 8 rows x 8 chunks per instruction and stores them.
-template <class C>
+// AUX: the stores' cache-policy bits.
+template <class C, int AUX = kStoreDevice>
 __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st, char* area,
-                                           __amdgpu_buffer_rsrc_t rd, int row0, int rows, int n0, int cols,
-                                           bool nt = false)
+                                           __amdgpu_buffer_rsrc_t rd, int row0, int rows, int n0, int cols)
 {
     const int lane = threadIdx.x & 63;
     const int wave = uni((int)(threadIdx.x >> 6));
@@ -449,10 +452,7 @@ __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st
                     const int m = wm * C::WTM + i * 32 + row;
                     const uint32_t off =
                         (m < rows && n < cols) ? (((uint32_t)(row0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
-                    if (nt)
-                        __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, kStoreDeviceNt);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, kStoreDevice);
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rd, off, 0, AUX);
                 }
                 __asm__ __volatile__("" ::: "memory");
             }
@@ -471,10 +471,7 @@ __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st
                                      pack_bf16x2(st.acc[i][j][grp * 4 + 2], st.acc[i][j][grp * 4 + 3])};
                     const uint32_t off =
                         (m < rows && n < cols) ? (((uint32_t)(row0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
-                    if (nt)
-                        __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, kStoreDeviceNt);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, kStoreDevice);
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rd, off, 0, AUX);
                 }
             }
         }
@@ -482,7 +479,9 @@ __device__ __forceinline__ void store_tile(const Args& a, const TileState<C>& st
 }
 
 // Publish a finished tile by storing its ready flag (device scope).  Called by
-// one thread once every wave's stores of the tile have completed.
+// one thread once every wave's stores of the tile have completed.  ROWS: the
+// row-counter protocol (the tile's row counter is incremented instead).
+template <bool ROWS = false>
 __device__ __forceinline__ void publish(const Args& a, int q, int flag, uint32_t who, uint32_t epoch)
 {
     if (a.trace_on) {
@@ -494,7 +493,7 @@ __device__ __forceinline__ void publish(const Args& a, int q, int flag, uint32_t
         tr[3] = (uint32_t)(now >> 32);
     }
     if (flag != a.drop_flag) {
-        if (a.row_counter)
+        if constexpr (ROWS)
             __hip_atomic_fetch_add(a.flags + (int64_t)(flag / a.g.tnc) * a.flag_stride, 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         else
@@ -505,9 +504,10 @@ __device__ __forceinline__ void publish(const Args& a, int q, int flag, uint32_t
 
 // The word that says whether tile `flag` of this run is released: its own
 // flag, or under the row-counter protocol its tile row's counter.
+template <bool ROWS>
 __device__ __forceinline__ const uint32_t* ready_word(const Args& a, int flag)
 {
-    const int idx = a.row_counter ? flag / a.g.tnc : flag;
+    const int idx = ROWS ? flag / a.g.tnc : flag;
     return a.flags + (int64_t)idx * a.flag_stride;
 }
 
@@ -515,9 +515,13 @@ __device__ __forceinline__ const uint32_t* ready_word(const Args& a, int flag)
 // the epoch, or the row counter has reached epoch * (tiles per row) -- every
 // run adds one per tile, so the counter passes that value exactly when the
 // whole row of this run is stored (compared modulo 2^32).
+template <bool ROWS>
 __device__ __forceinline__ bool released(const Args& a, uint32_t v, uint32_t epoch)
 {
-    return a.row_counter ? (int32_t)(v - epoch * (uint32_t)a.g.tnc) >= 0 : v == epoch;
+    if constexpr (ROWS)
+        return (int32_t)(v - epoch * (uint32_t)a.g.tnc) >= 0;
+    else
+        return v == epoch;
 }
 
 // ---------------------------------------------------------------- slice sum
@@ -875,16 +879,16 @@ __device__ __forceinline__ void engine_step(Engine& e, const Args& a, bool start
 // Waits (device-scope polls, short sleeps) until own tile t is flagged.  The
 // first wait that exceeds the watchdog limit reports the tile and sets
 // gave_up; after that no wait blocks, so a drain never waits longer than one
-// watchdog period in total.
-template <int SLEEP = 2>
+// watchdog period in total.  ROWS: the row-counter protocol.
+template <int SLEEP = 2, bool ROWS = false>
 __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, bool& gave_up)
 {
     const int flag = a.g.rank * a.g.ts + t;
-    const uint32_t* f = ready_word(a, flag);
-    if (released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
+    const uint32_t* f = ready_word<ROWS>(a, flag);
+    if (released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) return true;
     if (gave_up) return false;
     const uint64_t t0 = wall_clock64();
-    while (!released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
+    while (!released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
         __builtin_amdgcn_s_sleep(SLEEP);
         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
             gave_up = true;
@@ -901,8 +905,9 @@ __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, 
 // checked (they need none), then its local chunks, in the sum order.  A tile
 // whose flag does not arrive within the watchdog limit is reported and its
 // items are skipped.
-// SLEEP: s_sleep argument between flag polls (64 clocks each).
-template <int BATCH, int SLEEP = 2>
+// SLEEP: s_sleep argument between flag polls (64 clocks each); ROWS: the
+// row-counter protocol.
+template <int BATCH, int SLEEP = 2, bool ROWS = false>
 __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int first, int stride, uint32_t epoch)
 {
     constexpr int kDrainBatch = BATCH;
@@ -925,7 +930,7 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
 #pragma unroll
         for (int b = 0; b < kDrainBatch; ++b) {
             const int item = base + b * stride;
-            const bool ok = item < m.nitems && wait_tile<SLEEP>(a, epoch, item >> m.ipt_log2, gave_up);
+            const bool ok = item < m.nitems && wait_tile<SLEEP, ROWS>(a, epoch, item >> m.ipt_log2, gave_up);
             boff[b] = ok ? boff[b] : kOob;
             v[b][kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, boff[b], 0, kAuxSc1));
         }
@@ -1352,7 +1357,7 @@ __device__ __forceinline__ void wait_own_stores(const Engine& eng)
 // tile's epilogue stores were issued after this tile's prologue and before the
 // first refill, so they have completed once the refill issued at step 0 has:
 // at step NS-1 (or after the loop) its flag is published.
-template <class C, bool LOADER>
+template <class C, bool LOADER, bool ROWS = false>
 __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
                                            StepHooks& hk, Engine& eng)
 {
@@ -1376,7 +1381,7 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
         if (kt == C::NS - 1) {
             hk.stores = false;
             if (hk.pend_flag >= 0) {
-                if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
+                if (threadIdx.x == 0) publish<ROWS>(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
                 hk.pend_flag = -1;
             }
         }
@@ -1400,7 +1405,7 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
     stage_barrier();
     hk.stores = false;
     if (hk.pend_flag >= 0) {
-        if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
+        if (threadIdx.x == 0) publish<ROWS>(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
         hk.pend_flag = -1;
     }
 }
@@ -1409,11 +1414,12 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
 
 // Publishes the previous tile's flag once a barrier has certified its stores.
+template <bool ROWS = false>
 __device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
 {
     hk.stores = false;
     if (hk.pend_flag >= 0) {
-        if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
+        if (threadIdx.x == 0) publish<ROWS>(a, hk.pend_q, hk.pend_flag, hk.who, hk.epoch);
         hk.pend_flag = -1;
     }
 }
@@ -1436,7 +1442,7 @@ __device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
 // refill (and its sched barriers keep those instructions younger than every
 // load of the refill), so a step's wait allows as many more outstanding
 // instructions as the previous step's stream issued.
-template <class C, bool STREAM>
+template <class C, bool STREAM, bool ROWS = false>
 __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
                                               StepHooks& hk, Stream& rs)
 {
@@ -1491,7 +1497,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
             }
             wait_lgkm0();
             stage_barrier();
-            if (kt + 1 == C::NS - 1) publish_pending(a, hk);
+            if (kt + 1 == C::NS - 1) publish_pending<ROWS>(a, hk);
             // raised issue priority from the barrier to the end of the step,
             // while the wave issues the refill (measured: ~1% faster than
             // without, and than raising it over the MFMA-only part)
@@ -1525,7 +1531,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
     wait_vmcnt<0>();
     stage_barrier();
     if constexpr (STREAM) stream_settle(rs);
-    publish_pending(a, hk);
+    publish_pending<ROWS>(a, hk);
 }
 
 // Every group holds G/8 workgroups; group x has R_x = R/8 + (x < R%8) reducers
@@ -1553,7 +1559,7 @@ __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int gr
 // the next tile's waits have covered the tile's stores: publishing costs no
 // extra wait.  Loader and engine waves run the same loop (the same barriers);
 // engine waves also run the reduce engine.
-template <class C, bool FUSED, bool LOADER, bool STREAM, bool EPI = false>
+template <class C, bool FUSED, bool LOADER, bool STREAM, bool EPI = false, int VAR = 0>
 __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos, uint32_t who, uint32_t epoch,
                                               bool interleave)
 {
@@ -1596,9 +1602,9 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     }
     while (q < a.g.tiles) {
         if constexpr (C::XP)
-            tile_kloop_xp<C, STREAM>(a, lds, st, job, hk, rs);
+            tile_kloop_xp<C, STREAM, (VAR & kVarRows) != 0>(a, lds, st, job, hk, rs);
         else
-            tile_kloop<C, LOADER>(a, lds, st, job, hk, eng);
+            tile_kloop<C, LOADER, (VAR & kVarRows) != 0>(a, lds, st, job, hk, eng);
         // issue the next tile's first stages before this tile's stores
         const int qn = q + Ctot;
         TileCoord tn = t;
@@ -1610,8 +1616,9 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         // the stage buffer the next tile's prologue left free holds the
         // epilogue staging areas
         const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.dst[t.d], 0, a.slice_bytes, kRsrcFlags);
-        store_tile<C>(a, st, lds + (C::NS - 1) * C::STAGE_BYTES, rd, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN,
-                      tile_cols(a.g, t), uni(a.nt_stores) != 0);
+        store_tile<C, (VAR & kVarNt) ? kStoreDeviceNt : kStoreDevice>(
+            a, st, lds + (C::NS - 1) * C::STAGE_BYTES, rd, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN,
+            tile_cols(a.g, t));
         if constexpr (EPI) {
             if (t.d == a.g.rank) {
                 TileState<C> os;
@@ -1639,7 +1646,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     if (hk.pend_flag >= 0) {
         wait_own_stores<LOADER>(eng);
         stage_barrier();
-        if (threadIdx.x == 0) publish(a, hk.pend_q, hk.pend_flag, who, epoch);
+        if (threadIdx.x == 0) publish<(VAR & kVarRows) != 0>(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
     if constexpr (EPI) {
         // every own tile was summed by its producer
@@ -1655,8 +1662,9 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
             // every wave sums a share of the slice after its last tile
             const int wave = uni((int)(threadIdx.x >> 6));
             // (sixteen items in flight per CU)
-            drain_items<16 / C::WAVES / (C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64 ? 2 : 1)>(
-                a, item_map(a), pos * C::WAVES + wave, a.num_compute * C::WAVES, epoch);
+            drain_items<16 / C::WAVES / (C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64 ? 2 : 1), 2,
+                        (VAR & kVarRows) != 0>(a, item_map(a), pos * C::WAVES + wave, a.num_compute * C::WAVES,
+                                               epoch);
         }
     }
 }
@@ -1664,7 +1672,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
 // Compute role of the l-th compute workgroup of group grp: its position in a
 // round is either the group's block offset + l (contiguous split) or
 // l * 8 + grp (strided, used when all C_x are equal).
-template <class C, bool FUSED, bool STREAM, bool EPI = false>
+template <class C, bool FUSED, bool STREAM, bool EPI = false, int VAR = 0>
 __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, int l, uint32_t epoch, int base)
 {
     const int pos = uni(a.strided ? (l * kGroups + grp) : (base + l));
@@ -1673,15 +1681,16 @@ __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, 
     const bool interleave = FUSED && a.num_reducers == 0;
     const int wave = uni((int)(threadIdx.x >> 6));
     if (C::EW == 0 || wave < C::LW)
-        compute_waves<C, FUSED, true, STREAM, EPI>(a, lds, pos, who, epoch, interleave);
+        compute_waves<C, FUSED, true, STREAM, EPI, VAR>(a, lds, pos, who, epoch, interleave);
     else if constexpr (C::EW > 0)
-        compute_waves<C, FUSED, false, false>(a, lds, pos, who, epoch, interleave);
+        compute_waves<C, FUSED, false, false, false, VAR>(a, lds, pos, who, epoch, interleave);
 }
 
 // Dedicated reducer role (used when reducers are requested): claim own-slice
 // tiles in schedule order, wait for each tile's flag (thread 0 polls with
 // device-scope loads and short sleeps, bounded by the watchdog), then sum the
 // tile, reading the local slice at device scope.
+template <bool ROWS>
 __device__ void reducer_role(const Args& a, uint32_t epoch)
 {
     __shared__ int s_unit;
@@ -1692,10 +1701,10 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
             int abort_now = 0;
             if (u < a.g.ts) {
                 const TileCoord t = decode_slot(a.g, u);
-                const uint32_t* f = ready_word(a, t.flag);
-                if (!released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
+                const uint32_t* f = ready_word<ROWS>(a, t.flag);
+                if (!released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
                     const uint64_t t0 = wall_clock64();
-                    while (!released(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
+                    while (!released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
                         __builtin_amdgcn_s_sleep(2);
                         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
                             abort_now = 1;
@@ -1757,7 +1766,7 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
 // launch stored the same value, so all workgroups of a launch agree on its
 // epoch without communicating (the words change only at kernel ends).  A
 // GEMM-only launch has no flags and touches none of this.
-template <class C, bool FUSED, bool STREAM = false, bool EPI = false>
+template <class C, bool FUSED, bool STREAM = false, bool EPI = false, int VAR = 0>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1779,7 +1788,7 @@ __device__ __forceinline__ void fused_body(const Args& a)
     const uint32_t epoch = (uint32_t)uni((int)s_epoch) + 1u;  // value this run's flags carry
     const GroupSplit split = group_split((int)gridDim.x, uni(a.num_reducers), grp);
     if (ticket < (uint32_t)split.compute)
-        compute_role<C, FUSED, STREAM, EPI>(a, lds, grp, (int)ticket, epoch, split.base);
+        compute_role<C, FUSED, STREAM, EPI, VAR>(a, lds, grp, (int)ticket, epoch, split.base);
     else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers) {
         if (a.coresident) {
             // reducer r of R owns items r*W + wave, + R*W, ...: its peer chunks
@@ -1787,9 +1796,10 @@ __device__ __forceinline__ void fused_body(const Args& a)
             // checked; once a tile is flagged only its local chunks remain
             const int r = split.rbase + (int)(ticket - (uint32_t)split.compute);
             const int wave = uni((int)(threadIdx.x >> 6));
-            drain_items<2, 1>(a, item_map(a), r * C::WAVES + wave, uni(a.num_reducers) * C::WAVES, epoch);
+            drain_items<2, 1, (VAR & kVarRows) != 0>(a, item_map(a), r * C::WAVES + wave,
+                                                     uni(a.num_reducers) * C::WAVES, epoch);
         } else {
-            reducer_role(a, epoch);
+            reducer_role<(VAR & kVarRows) != 0>(a, epoch);
         }
     }
 
@@ -1816,26 +1826,26 @@ __device__ __forceinline__ void fused_body(const Args& a)
 }
 
 // Tiles that fit two workgroups per CU keep two waves per SIMD resident.
-template <class C, bool FUSED, bool EPI = false>
+template <class C, bool FUSED, bool EPI = false, int VAR = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(Args a)
 {
-    fused_body<C, FUSED, false, EPI>(a);
+    fused_body<C, FUSED, false, EPI, VAR>(a);
 }
 
 // Eight-wave workgroups (one per CU): two waves per SIMD, so one wave's
 // MFMAs run while its sibling waits on LDS, a barrier or the reduce engine.
-template <class C, bool FUSED, bool STREAM = false>
+template <class C, bool FUSED, bool STREAM = false, int VAR = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel_8w(Args a)
 {
-    fused_body<C, FUSED, STREAM>(a);
+    fused_body<C, FUSED, STREAM, false, VAR>(a);
 }
 
 // Large tiles run one workgroup (one wave per SIMD) per CU: let the compiler
 // use the whole register file for latency hiding.
-template <class C, bool FUSED>
+template <class C, bool FUSED, int VAR = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_kernel_1w(Args a)
 {
-    fused_body<C, FUSED>(a);
+    fused_body<C, FUSED, false, false, VAR>(a);
 }
 
 // Standalone slice sum: every workgroup reduces, no flags, grid-stride over the

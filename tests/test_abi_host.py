@@ -87,6 +87,12 @@ def cfg(**kw):
     (dict(flag_protocol="row_counter", engine_interval=1), gr.ERR_INVALID_ARG),
     (dict(flag_protocol="row_counter", reduce_mode="stream"), gr.ERR_INVALID_ARG),
     (dict(flag_protocol=2), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="nt", flag_protocol="row_counter"), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="nt", engine_interval=2), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="nt", reduce_mode="stream"), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="nt", tile="64x128", reduce_mode="epilogue"), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="nt", reduce_mode="coresident"), gr.OK),
+    (dict(flag_protocol="row_counter", tile="64x128", reduce_mode="epilogue"), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.OK),

@@ -56,6 +56,12 @@ def test_coresident_o_proj_integer_bit_exact():
     _check_integer(synthetic.CONFIGS["o_proj"], 6)
 
 
+@pytest.mark.parametrize("tile", ["16x64", "64x128"])
+def test_coresident_row_counters_integer_bit_exact(tile):
+    # the reducers wait for whole tile rows instead of single tiles
+    _check_integer(RAGGED, 2, tile=tile, flag_protocol="row_counter")
+
+
 def test_coresident_equals_tail_on_normal_inputs():
     cfg = synthetic.CONFIGS["o_proj"]
     x, w, peers = synthetic.make_inputs(cfg, "normal")

@@ -229,8 +229,7 @@ def test_modes_agree_bit_exactly():
     dict(num_reducers=8, flag_stride=32, tile="128x256"),
     dict(num_reducers=0, engine_interval=1, flag_stride=32), dict(num_reducers=0, engine_interval=5, tile="16x64"),
     dict(tile_stores="nt"), dict(tile_stores="nt", num_reducers=8), dict(tile_stores="nt", tile="64x128"),
-    dict(tile_stores="nt", tile="16x64", reduce_mode="epilogue"),
-    dict(tile_stores="nt", tile="256x256", reduce_mode="stream"),
+    dict(tile_stores="nt", tile="256x256"), dict(tile_stores="nt", tile="16x64", num_reducers=8),
     dict(flag_protocol="row_counter"), dict(flag_protocol="row_counter", num_reducers=8),
     dict(flag_protocol="row_counter", tile="16x64", flag_stride=32),
 ])
