@@ -256,6 +256,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// A pointer every lane holds the same value of, made visibly uniform: buffer
+// resources built from it then stay in scalar registers (a resource the
+// compiler takes for divergent wraps every buffer access in a readfirstlane
+// loop).
+__device__ __forceinline__ const void* uni_ptr(const void* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------- GEMM tile
 
@@ -1335,7 +1346,7 @@ __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<
     job.xbytes = xp ? xbytes : a.x_bytes;
     if constexpr (LOADER) {
         if (job.nk == 0) return;
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)job.xp, 0, job.xbytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
         make_plan<C>(a, job.lp, row0, rows, n0, cols);
 #pragma unroll
@@ -1370,7 +1381,7 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
 
     const int K = a.g.K;
     const int nk = job.nk;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)job.xp, 0, job.xbytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
     for (int kt = 0; kt < nk; ++kt) {
         if constexpr (LOADER)
@@ -1462,7 +1473,7 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
     constexpr int kMf = C::FM * C::FN;   // MFMAs per substep
     constexpr int kDs = C::FM + C::FN;   // fragment reads per substep
     if (nk > 0) {
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)job.xp, 0, job.xbytes, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
         bf16x8 xf[2][C::FM], wf[2][C::FN];
         // stage 0 came from the prologue, before the previous tile's stores
