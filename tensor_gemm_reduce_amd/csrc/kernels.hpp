@@ -1672,8 +1672,11 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         } else {
             // every wave sums a share of the slice after its last tile
             const int wave = uni((int)(threadIdx.x >> 6));
-            // (sixteen items in flight per CU)
-            drain_items<16 / C::WAVES / (C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64 ? 2 : 1), 2,
+            // (sixteen items in flight per CU for the eight-wave and one-per-CU
+            // tiles; one per wave for four-wave tiles at two per CU, whose
+            // shapes leave about one item per wave: a second, empty slot of a
+            // batch still issues its eight loads and lengthens the wait)
+            drain_items<(C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64) ? 1 : 16 / C::WAVES, 2,
                         (VAR & kVarRows) != 0>(a, item_map(a), pos * C::WAVES + wave, a.num_compute * C::WAVES,
                                                epoch);
         }
