@@ -73,3 +73,22 @@ def test_adaptive_split_under_capture_uses_no_reducers():
     assert op.status() == gr.OK
     assert np.array_equal(host(b.out), want)
     assert gr.gemm_rs_query(op.h).split_state == 1  # nothing was timed under capture
+
+
+@pytest.mark.parametrize("kw", [dict(tile_stores="nt"), dict(flag_protocol="row_counter")], ids=["nt", "rows"])
+def test_adaptive_split_with_kernel_variants(kw):
+    # the timed candidates run the variant kernel with and without reducers
+    cfg = synthetic.Config("adaptive_var", 23, 8 * 512, 2048, 256)
+    rank = 6
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    want = dev(oracle.gemm_rs(x, w, peers, 8, rank)[2])
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, num_reducers=-2, **kw)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    fill = np.array(SENTINEL, np.uint16).view(np.int16).item()
+    for it in range(12):
+        b.out.fill_(fill)
+        op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local)
+        torch.cuda.synchronize()
+        assert op.status() == gr.OK
+        assert torch.equal(b.out, want), it
+    assert gr.gemm_rs_query(op.h).split_state == 2
