@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused BF16 GEMM + reduce-scatter (one TP=8 rank's share).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload o_proj]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large_prefill]
 
 A step is one fused run of the whole hot path (GEMM tiles, routed BF16
 epilogue with ready flags, reducers summing this rank's slice with the 7 peer
@@ -9,8 +9,10 @@ partials) over inputs already resident in HBM.  Prints ONE JSON line:
 fused TFLOP/s (value), its fraction of the MI355X dense BF16 MFMA peak, the
 overlap efficiency 1 - (T_fused - T_gemm) / T_reduce against the same GEMM and
 the standalone reduce kernel run alone, a roofline object for the fused kernel,
-and the CPU oracle timed on the host cores as a baseline.  With --sweep (the
-default) the other benchmark shapes are timed too and reported under "sweep".
+and the CPU oracle timed on the host cores as a baseline.  The headline
+workload is the large prefill shape (M = 32768), the largest of the metric's
+range M = 512..32768; with --sweep (the default) the other benchmark shapes
+are timed too and reported under "sweep", each with its own roofline fraction.
 """
 from __future__ import annotations
 
@@ -28,8 +30,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA (AMD published figure)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (AMD published figure)
 METRIC = "fused GEMM+RS TFLOP/s (% bf16 MFMA peak) + overlap efficiency, M=512..32768"
-DEFAULT_WORKLOAD = "o_proj"
-SWEEP = ("down_proj", "mixtral_down", "large_prefill")
+DEFAULT_WORKLOAD = "large_prefill"
+SWEEP = ("o_proj", "down_proj", "mixtral_down", "large_prefill")
 
 
 def source_digest() -> str:
@@ -55,15 +57,13 @@ def parse():
     p.add_argument("--tile", default="auto")
     p.add_argument("--reducers", type=int, default=-1,
                    help="dedicated reducer workgroups: -1 the plan's default, -2 adaptive")
-    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "stream", "coresident", "epilogue"],
+    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "coresident"],
                    help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--tile-stores", default="device", choices=["device", "nt"],
                    help="cache policy of the routed tile stores (nt: non-temporal hint)")
     p.add_argument("--cold", action="store_true",
                    help="also time the fused, GEMM-only and reduce launches with cold caches (a 512 MiB "
                         "buffer written before each launch)")
-    p.add_argument("--engine-interval", type=int, default=0,
-                   help="K steps between in-loop reduce-engine slots (0: reduce after the last tile)")
     p.add_argument("--sweep-out", default=None, help="also write per-config lines here")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run only a plain copy of known size and a few fused launches of --workload "
@@ -114,8 +114,8 @@ class Case:
         self.local = z()
         self.out = z()
         self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
-                            num_reducers=args.reducers, engine_interval=args.engine_interval,
-                            reduce_mode=args.reduce_mode, tile_stores=args.tile_stores)
+                            num_reducers=args.reducers, reduce_mode=args.reduce_mode,
+                            tile_stores=args.tile_stores)
         # the adaptive split (reducers -2) times its candidates on uncaptured
         # runs: give it those before anything is captured into a graph
         if args.reducers == -2:
@@ -123,13 +123,13 @@ class Case:
                 self.run(gr.MODE_FUSED)
                 torch.cuda.synchronize()
             log(f"[{name}] adaptive split settled: {gr.gemm_rs_query(self.op.h).reducer_wgs} reducer workgroups")
-        # where the fused launch streams the sum through the K loop, the same
-        # launch with the sum after the last tile is timed beside it
+        # where the fused launch sums the slice elsewhere than after the last
+        # tile, the same launch with the sum after the last tile is timed beside it
         self.op_tail = None
-        if self.op.info.reduce_mode in (gr.REDUCE_STREAM, gr.REDUCE_CORESIDENT, gr.REDUCE_EPILOGUE):
+        if self.op.info.reduce_mode != gr.REDUCE_TAIL:
             self.op_tail = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
-                                     num_reducers=args.reducers, engine_interval=args.engine_interval,
-                                     reduce_mode="tail", tile_stores=args.tile_stores)
+                                     num_reducers=args.reducers, reduce_mode="tail",
+                                     tile_stores=args.tile_stores)
         self.gr = gr
 
     def run(self, mode):
@@ -304,19 +304,25 @@ def measure_case(c: Case, warmup, iters):
         "T_torch_linear_us": mm,
         "fused_tflops": cfg.flops / tf * 1e-6,
         "fused_pct_peak": 100.0 * cfg.flops / tf * 1e-6 / PEAK_BF16_TFLOPS,
+        # the fused kernel's average launch duration (events around graph
+        # replays of back-to-back launches) against the dense BF16 peak
+        "roofline_frac": cfg.flops / tf * 1e-6 / PEAK_BF16_TFLOPS,
         "gemm_only_tflops": cfg.flops / tg * 1e-6,
         "reduce_gbs": cfg.reduce_bytes / tr * 1e-3,
         "reduce_pct_hbm": 100.0 * cfg.reduce_bytes / tr * 1e-3 / PEAK_HBM_GBS,
         "overlap": 1.0 - (tf - tg) / tr,
         "speedup_vs_sequential": seq["median_us"] / tf,
-        "reduce_mode": {0: "auto", 1: "tail", 2: "stream", 3: "coresident", 4: "epilogue"}[c.op.info.reduce_mode],
+        "reduce_mode": {0: "auto", 1: "tail", 2: "coresident"}[c.op.info.reduce_mode],
         **extra,
     }
 
 
 def check_case(c: Case, rows_per=3):
-    """Untimed parity check on sampled rows against the oracle, and the local
-    slice's error against the unfused path's (no worse than 1.1x)."""
+    """Untimed parity check on sampled rows against the oracle: `out` equals
+    the oracle's slice sum of the GPU's local partial, and both the local
+    slice and `out` are within 1e-2 of the FP64 reference and no worse than
+    1.1x the unfused path's error (the vendor GEMM with BF16 output, then the
+    slice sum)."""
     import numpy as np
 
     import oracle
@@ -332,16 +338,21 @@ def check_case(c: Case, rows_per=3):
     host = lambda t: t.cpu().numpy().view(np.uint16)
     local = host(c.local)[rows]
     out = host(c.out)[rows]
-    want_out = oracle.slice_sum(local, [p[rows] for p in peers], tp=8)
+    prows = [p[rows] for p in peers]
+    want_out = oracle.slice_sum(local, prows, tp=8)
     ref = oracle.ref_f64(x, w, None, tp=8, rank=c.rank, rows=rows)
-    err = lambda bits: float(np.max(np.abs(oracle.bf16_to_f32(bits) - ref)) / np.max(np.abs(ref)))
-    err_local = err(local)
-    # the unfused path's local slice: the vendor GEMM with BF16 output
+    ref_out = oracle.ref_f64(x, w, peers, tp=8, rank=c.rank, rows=rows)
+    err = lambda bits, r: float(np.max(np.abs(oracle.bf16_to_f32(bits) - r)) / np.max(np.abs(r)))
+    err_local, err_out = err(local, ref), err(out, ref_out)
+    # the unfused path: the vendor GEMM with BF16 output, then the slice sum
     y = c.matmul()[c.rank * cfg.S + torch.from_numpy(rows).cuda()]
-    err_unfused = err(y.view(torch.int16).cpu().numpy().view(np.uint16))
-    ok = bool(np.array_equal(out, want_out)) and err_local <= 1e-2 and err_local <= 1.1 * err_unfused
+    y_local = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    unf_local, unf_out = err(y_local, ref), err(oracle.slice_sum(y_local, prows, tp=8), ref_out)
+    ok = (bool(np.array_equal(out, want_out)) and err_local <= 1e-2 and err_out <= 1e-2
+          and err_local <= 1.1 * unf_local and err_out <= 1.1 * unf_out)
     return {"ok": ok, "rows": int(rows.size), "local_max_rel_err": err_local,
-            "unfused_local_max_rel_err": err_unfused}
+            "unfused_local_max_rel_err": unf_local, "out_max_rel_err": err_out,
+            "unfused_out_max_rel_err": unf_out}
 
 
 def cpu_baseline(c: Case, seconds):
@@ -365,12 +376,10 @@ def cpu_baseline(c: Case, seconds):
         rows = (np.arange(chunk) + start) % S
         t0 = time.perf_counter()
         # whole path for these slice rows: all 8 destination row blocks of the
-        # GEMM (routing), the BF16 rounding and the slice sum
-        locals_ = None
-        for d in range(8):
-            part = oracle.f32_to_bf16(oracle.gemm_f32acc(x, w, rows=d * S + rows))
-            if d == c.rank:
-                locals_ = part
+        # GEMM (routing) in one call (W is transposed once per call), the BF16
+        # rounding and the slice sum
+        part = oracle.f32_to_bf16(oracle.gemm_f32acc(x, w, rows=np.concatenate([d * S + rows for d in range(8)])))
+        locals_ = part[c.rank * chunk:(c.rank + 1) * chunk]
         oracle.slice_sum(locals_, [p[rows] for p in peers], tp=8)
         t_total += time.perf_counter() - t0
         rows_done += chunk
@@ -379,7 +388,8 @@ def cpu_baseline(c: Case, seconds):
     flops = 2.0 * rows_done * 8 * cfg.N * cfg.K_local
     return {"value": flops / t_total * 1e-12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows_done} slice rows x 8 destination blocks of {c.name} (GEMM, BF16 rounding, "
-                      f"routing, slice sum) in {t_total:.1f} s",
+                      f"routing, slice sum; one oracle GEMM call per {chunk} slice rows, which converts and "
+                      f"transposes W once) in {t_total:.1f} s",
             "seconds": t_total}
 
 
@@ -450,7 +460,6 @@ def traffic_from(args):
 SPLIT_KNOBS = (
     [dict(num_reducers=r) for r in (0, 2, 4, 8, 16, 32, 64)]
     + [dict(num_reducers=r, flag_stride=32) for r in (0, 8, 64)]
-    + [dict(num_reducers=0, engine_interval=n) for n in (1, 4)]
     + [dict(num_reducers=r, tile_stores=1) for r in (0, 8, 64)]
     + [dict(num_reducers=r, flag_protocol=1) for r in (0, 8, 64)]
 )
@@ -490,7 +499,7 @@ def split_sweep(args):
     for i, (kw, op) in enumerate(ops):
         st = op.status()
         tf = statistics.median(t[f"k{i}"])
-        rows.append({**kw, "flag_stride": kw.get("flag_stride", 1), "engine_interval": kw.get("engine_interval", 0),
+        rows.append({**kw, "flag_stride": kw.get("flag_stride", 1),
                      "tile_stores": kw.get("tile_stores", 0),
                      "flag_protocol": kw.get("flag_protocol", 0),
                      "compute_wgs": op.info.compute_wgs, "reducer_wgs": op.info.reducer_wgs,
@@ -516,7 +525,7 @@ def allreduce_sweep(args):
     import torch
 
     rows = {}
-    for name in (DEFAULT_WORKLOAD,) + SWEEP:
+    for name in SWEEP:
         c = Case(name, args)
         cfg = c.cfg
         gr = c.gr
@@ -702,7 +711,7 @@ def main():
         "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": achieved / PEAK_BF16_TFLOPS,
         "traffic": (traffic["fetch_bytes"] + traffic["write_bytes"]) if traffic else None,
-        "kernel": "fused_kernel", "algorithmic_flops_per_launch": cfg.flops,
+        "kernel": f"fused_kernel ({c.op.info.bm}x{c.op.info.bn} tile)", "algorithmic_flops_per_launch": cfg.flops,
         "avg_launch_us": mean_us,
     }
     cpu = cpu_baseline(c, args.cpu_seconds) if args.cpu else None
@@ -710,6 +719,9 @@ def main():
     sweep = {}
     if args.sweep:
         for name in SWEEP:
+            if name == args.workload:
+                sweep[name] = dict(m, parity=check)
+                continue
             try:
                 sc = Case(name, args)
                 sweep[name] = measure_case(sc, args.warmup, args.steps)
@@ -746,6 +758,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": {k: ({"fused_tflops": v.get("fused_tflops"), "fused_pct_peak": v.get("fused_pct_peak"),
+                       "roofline_frac": v.get("roofline_frac"),
                        "overlap": v.get("overlap"), "T_fused_us": v.get("T_fused_us", {}).get("median_us"),
                        "T_gemm_us": v.get("T_gemm_us", {}).get("median_us"),
                        "T_reduce_us": v.get("T_reduce_us", {}).get("median_us"),

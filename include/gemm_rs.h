@@ -21,8 +21,8 @@
  *   reducers            wait for the flags of this rank's own slice and sum each
  *                       tile with the tp-1 peer partials into `out`: by default
  *                       the compute workgroups themselves after their last
- *                       tile, optionally between MFMAs (engine_interval) or in
- *                       dedicated workgroups (num_reducers).
+ *                       tile, optionally in dedicated workgroups (num_reducers)
+ *                       or in co-resident ones (reduce_mode).
  *
  * On one GPU the tp-1 peer partials are buffers already resident in HBM that
  * stand in for the other ranks' remote writes, and the tp-1 send buffers stand
@@ -54,7 +54,10 @@
  * are advanced by the kernel itself, so runs may be captured into a HIP graph
  * and replayed; each replay is a new run.  A fused run needs its whole grid
  * resident at once (the grid is sized to the device: CUs x workgroups per CU),
- * as a persistent kernel whose workgroups wait for each other's flags.
+ * as a persistent kernel whose workgroups wait for each other's flags.  This
+ * is not checked at launch: a kernel that holds CUs on another stream can
+ * delay part of the grid, and a reducer that then waits longer than the
+ * watchdog reports GEMM_RS_ERR_TIMEOUT with `out` incomplete.
  */
 #ifndef GEMM_RS_H
 #define GEMM_RS_H
@@ -92,34 +95,24 @@ extern "C" {
 #define GEMM_RS_TILE_256x256 6
 #define GEMM_RS_TILE_COUNT 7
 
-/* ---- where the slice sum runs without dedicated reducers or engine slots -- */
-#define GEMM_RS_REDUCE_AUTO 0   /* TAIL (measured faster on every benchmark shape)  */
+/* ---- where the slice sum runs without dedicated reducers ------------------ */
+#define GEMM_RS_REDUCE_AUTO 0   /* TAIL                                             */
 #define GEMM_RS_REDUCE_TAIL 1   /* each compute workgroup sums its share of the
                                    slice after its last tile                      */
-#define GEMM_RS_REDUCE_STREAM 2 /* every wave streams its share through the K loop:
-                                   one load or store of the sum per K step, issued
-                                   behind the stage refill (256x256 tile only)    */
-#define GEMM_RS_REDUCE_CORESIDENT 3 /* one reducer workgroup per CU beside the
+#define GEMM_RS_REDUCE_CORESIDENT 2 /* one reducer workgroup per CU beside the
                                    compute workgroups (tiles whose kernel fits one
                                    more workgroup per CU, else gemm_rs_create gives
                                    GEMM_RS_ERR_UNSUPPORTED_SHAPE); each reducer wave
                                    sums the peers of its items while the GEMM runs,
                                    then adds the local chunk once the tile's flag
                                    is set                                          */
-#define GEMM_RS_REDUCE_EPILOGUE 4 /* the workgroup that computes an own-slice tile
-                                   sums it in its epilogue from its accumulators
-                                   and the tile's peer values, loaded ahead of the
-                                   tile's first stage (16x64 and 64x128 tiles)   */
 
 /* ---- cache policy of the routed tile stores ------------------------------ */
 #define GEMM_RS_STORES_DEVICE 0      /* device scope, written through L2        */
 #define GEMM_RS_STORES_NONTEMPORAL 1 /* device scope with the non-temporal hint:
                                         the tiles are not kept in L2 for reuse.
-                                        A separate kernel variant: with the sum
-                                        after the last tile, dedicated or
-                                        co-resident reducers and GEMM_ONLY; not
-                                        with engine slots, the stream, the
-                                        epilogue sum or row counters            */
+                                        A separate kernel variant (also of
+                                        GEMM_ONLY); not with row counters      */
 
 /* ---- how a released tile is signalled ------------------------------------ */
 #define GEMM_RS_FLAGS_TILE 0        /* one ready flag per tile, set to the run's
@@ -129,10 +122,9 @@ extern "C" {
                                        per released tile and never reset; a tile
                                        is summed once its row's counter reaches
                                        epoch x tile columns.  A separate kernel
-                                       variant: not with in-loop engine slots,
-                                       the reduce stream or the epilogue sum.  After
-                                       a watchdog timeout the counters are one
-                                       short for good: create a new handle.     */
+                                       variant.  After a watchdog timeout the
+                                       counters are one short for good: create a
+                                       new handle.                              */
 
 /* ---- debug flags -------------------------------------------------------- */
 #define GEMM_RS_DEBUG_TRACE 1 /* record, per schedule slot, the tile's flag index,
@@ -152,10 +144,6 @@ typedef struct gemm_rs_config {
                              reducers (two runs each), and once all have
                              completed the fastest count is kept (results
                              are identical for every count)                  */
-    int32_t engine_interval; /* FUSED without reducer workgroups: K steps between
-                             reduce-engine slots inside the compute loop;
-                             0 = the engine waves sum the slice after their
-                             last tile (0 .. 4096)                          */
     int32_t debug_flags;  /* GEMM_RS_DEBUG_* bits                             */
     int32_t drop_flag;    /* debug: index of a ready flag the producer never
                              releases, to exercise the watchdog; -1 = none    */
@@ -163,9 +151,7 @@ typedef struct gemm_rs_config {
     int64_t watchdog_us;  /* reducer wait limit per tile in microseconds;
                              0 = default (2 000 000)                          */
     int32_t reduce_mode;  /* GEMM_RS_REDUCE_*; all but AUTO and TAIL need
-                             num_reducers <= 0 and engine_interval == 0;
-                             STREAM needs the 256x256 tile, EPILOGUE the
-                             16x64 or 64x128 tile                            */
+                             num_reducers <= 0                               */
     int32_t tile_stores;  /* GEMM_RS_STORES_*: cache policy of the tile stores
                              into the destination slices (every mode and entry
                              point that routes tiles)                        */
@@ -190,7 +176,7 @@ typedef struct gemm_rs_info {
     uint32_t epoch;           /* value the last FUSED run stored in its flags
                                  (read from the device; waits for the stream) */
     int32_t reduce_mode;      /* resolved GEMM_RS_REDUCE_* of a FUSED run with
-                                 no dedicated reducers and no engine slots    */
+                                 no dedicated reducers                        */
     int32_t split_state;      /* 0: fixed reducer count; 1: adaptive, still
                                  timing candidates; 2: adaptive, settled on
                                  reducer_wgs                                  */
@@ -218,12 +204,24 @@ int gemm_rs_plan_slots(const gemm_rs_config *cfg, int32_t *slot_d, int32_t *slot
  * device is gfx950, and allocates the handle-owned device state (ready flags
  * and per-workgroup finish marks zeroed, arrival tickets, status word, trace
  * log, and a [S][N] BF16 scratch used as the local slice when gemm_rs_run gets
- * local_slice == NULL).
- * On success *out receives the handle; on failure *out is set to NULL. */
+ * local_slice == NULL).  The handle is the persistent kernel's setup: mKernel
+ * ("mKernel: Fast Multi-GPU, Multi-Node Fused Kernels", section 3) splits one
+ * persistent kernel's blocks into compute and communication roles that
+ * coordinate through per-tile readiness flags in GPU memory; the flags, the
+ * role tickets and the grid size (CUs x workgroups per CU, all resident at
+ * once) are fixed here.
+ * On success *out receives the handle; on failure *out is set to NULL.
+ * Errors: INVALID_ARG / UNSUPPORTED_SHAPE (as gemm_rs_validate), NO_DEVICE,
+ * NO_MEMORY, HIP. */
 int gemm_rs_create(const gemm_rs_config *cfg, gemm_rs_handle **out);
 
 /* Enqueues one run on `stream` (a hipStream_t; NULL = the null stream) and
- * returns without waiting.
+ * returns without waiting.  A FUSED run is the operation of the problem page
+ * ("A fused GEMM + reduce-scatter kernel hiding 90% of communication on 8 H100
+ * GPUs", "What is asked"): the local GEMM and the reduce-scatter of its
+ * partial in one kernel, partial tiles handed on as they are finished; the
+ * other modes are the unfused baselines the same page's "How it gets
+ * verified" compares against (the GEMM alone, then the reduction).
  *   mode         GEMM_RS_MODE_*.
  *   x, w         device inputs (see Layouts); unused by REDUCE_ONLY.
  *   send         host array of tp-1 device pointers; send[i] receives the
@@ -290,13 +288,24 @@ int gemm_rs_run_allgather(gemm_rs_handle *h, int32_t mode, const void *const *x_
 /* Waits for the handle's last run and returns its device status:
  * GEMM_RS_OK, or GEMM_RS_ERR_TIMEOUT if a reducer gave up waiting for a ready
  * flag (the kernel still exits; `out` is then incomplete).  Reading the status
- * clears it. */
+ * clears it.  The waits it reports are the readiness-flag waits of mKernel's
+ * communication roles ("mKernel: Fast Multi-GPU, Multi-Node Fused Kernels",
+ * section 4: tiles signal completion through flags that consumers poll), here
+ * bounded by a watchdog.  A wait also times out when the grid is not wholly
+ * resident, for instance while other kernels hold CUs on another stream: the
+ * persistent launch assumes every workgroup runs at once.
+ * Errors: INVALID_ARG (h NULL), HIP. */
 int gemm_rs_status(gemm_rs_handle *h);
 
 /* Fills *info with the resolved launch parameters of a handle. */
 int gemm_rs_query(gemm_rs_handle *h, gemm_rs_info *info);
 
 /* Copies debug state of the last run to host memory (waits for it first):
+ * the per-tile release times and flag values that make the overlap and the
+ * flag order visible (the progress counters mKernel's controller reads,
+ * "mKernel: Fast Multi-GPU, Multi-Node Fused Kernels", section 3.2; the flag
+ * order fixed by FLUX's tile coordinate swizzling, TL;DR of "FLUX: Fast
+ * Software-based Communication Overlap On GPUs Through Kernel Fusion").
  *   slot_log   if non-NULL, 4 words per schedule slot: the tile's flag index,
  *              the compute workgroup's ticket, and the 64-bit release time
  *              (100 MHz counter; low word then high word).  Written only when
@@ -306,8 +315,10 @@ int gemm_rs_query(gemm_rs_handle *h, gemm_rs_info *info);
 int gemm_rs_debug_read(gemm_rs_handle *h, uint32_t *slot_log, size_t slot_words,
                        uint32_t *flags, size_t flag_words);
 
-/* Waits for outstanding work and frees the handle's device state.  NULL is a
- * no-op. */
+/* Waits for outstanding work and frees the handle's device state (what
+ * gemm_rs_create set up for the persistent kernel of mKernel, "mKernel: Fast
+ * Multi-GPU, Multi-Node Fused Kernels", section 3).  NULL is a no-op; nothing
+ * is returned, and a HIP error while waiting is ignored. */
 void gemm_rs_destroy(gemm_rs_handle *h);
 
 /* Message for an error code (static storage; for GEMM_RS_ERR_HIP the last HIP

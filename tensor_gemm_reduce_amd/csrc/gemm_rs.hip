@@ -32,39 +32,26 @@ int hip_fail(hipError_t e, const char* what)
     } while (0)
 
 // Tile table: id -> tile shape, stage depth and the kernel instantiations.
-// Each shape has two load splits: every wave loads stages (GEMM only, and the
-// fused kernel with dedicated reducer workgroups), or the first half of the
-// waves load and the second half run the reduce engine (the fused kernel
-// without dedicated reducers).
-//                      BM   BN   BK  NS  waves  MFMA  loader waves
-#define GEMM_RS_TILE(name, ...)                          \
-    typedef TileCfg<__VA_ARGS__> name;                   \
-    typedef TileCfg<__VA_ARGS__, (name::WAVES / 2)> name##E;
-GEMM_RS_TILE(Tile16x64, 16, 64, 128, 2, 1, 4, 16)
-GEMM_RS_TILE(Tile64x128, 64, 128, 64, 2, 2, 2, 32)
-GEMM_RS_TILE(Tile128x128, 128, 128, 32, 3, 2, 2, 32)
-GEMM_RS_TILE(Tile128x256, 128, 256, 32, 4, 2, 2, 32)
-GEMM_RS_TILE(Tile256x128, 256, 128, 32, 4, 2, 2, 32)
-GEMM_RS_TILE(Tile256x256, 256, 256, 64, 2, 2, 4, 32)
-#undef GEMM_RS_TILE
+//                      BM   BN   BK  NS  waves  MFMA
+typedef TileCfg<16, 64, 128, 2, 1, 4, 16> Tile16x64;
+typedef TileCfg<64, 128, 64, 2, 2, 2, 32> Tile64x128;
+typedef TileCfg<128, 128, 32, 3, 2, 2, 32> Tile128x128;
+typedef TileCfg<128, 256, 32, 4, 2, 2, 32> Tile128x256;
+typedef TileCfg<256, 128, 32, 4, 2, 2, 32> Tile256x128;
+typedef TileCfg<256, 256, 64, 2, 2, 4, 32> Tile256x256;
 
 struct TileDesc {
     int bm, bn, bk;
     int threads;               // workgroup size
     int wgs_per_cu;            // workgroups per CU the kernels are built for
-    int engine_lds_bytes;      // fused kernel with in-loop engine slots: stages + engine areas
-    int lds_bytes;             // every other launch: stages
-    const void* engine_kernel; // fused: compute waves run the reduce engine
-    const void* stream_kernel; // fused: the waves stream the sum through the K loop (or null)
-    int stream_lds_bytes;      // its LDS: stages + the streaming waves' slots
-    const void* kernel;        // fused: dedicated reducer workgroups
+    int lds_bytes;             // stages
+    const void* kernel;        // fused (every reducer placement)
     const void* gemm_kernel;   // the same GEMM without flags or reduction
     const void* kernel_nt;     // `kernel` storing routed tiles non-temporally
     const void* gemm_kernel_nt;  // `gemm_kernel` storing routed tiles non-temporally
     const void* kernel_rows;   // `kernel` reading row counters
     const void* ag_kernel;     // all-gather + GEMM: copy phase, then the GEMM waiting for rows
     const void* ag_gemm_kernel;  // the same GEMM over an already gathered buffer
-    const void* epi_kernel;    // fused: own tiles summed in their producer's epilogue (or null)
 };
 
 // Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
@@ -74,9 +61,9 @@ template <class C, bool FUSED, bool TWO_PER_CU, int VAR = 0>
 const void* kernel_for()
 {
     if constexpr (C::WAVES == 8)
-        return reinterpret_cast<const void*>(&fused_kernel_8w<C, FUSED, false, VAR>);
+        return reinterpret_cast<const void*>(&fused_kernel_8w<C, FUSED, VAR>);
     else if constexpr (TWO_PER_CU)
-        return reinterpret_cast<const void*>(&fused_kernel<C, FUSED, false, VAR>);
+        return reinterpret_cast<const void*>(&fused_kernel<C, FUSED, VAR>);
     else
         return reinterpret_cast<const void*>(&fused_kernel_1w<C, FUSED, VAR>);
 }
@@ -92,50 +79,29 @@ const void* ag_kernel_for()
         return reinterpret_cast<const void*>(&ag_kernel_1w<C, FUSED>);
 }
 
-// The epilogue sum keeps a tile's peer values in registers: four-wave tiles
-// with at most 32 accumulators per lane (16x64, 64x128).
 template <class C>
-const void* epi_kernel_for()
-{
-    if constexpr (C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64 && C::FM * C::FN * AccT<C::MF>::N <= 32)
-        return reinterpret_cast<const void*>(&fused_kernel<C, true, true>);
-    else
-        return nullptr;
-}
-
-template <class C, class CE>
 TileDesc desc()
 {
-    static_assert(C::LDS_BYTES == CE::LDS_BYTES && CE::EW > 0, "load splits of one shape");
-    constexpr int elds = CE::LDS_BYTES + CE::ENG_LDS;
-    static_assert(elds <= 160 * 1024 - 64, "LDS of one workgroup");
-    // occupancy is set by the stages; in-loop engine slots may cost it
+    static_assert(C::LDS_BYTES <= 160 * 1024 - 64, "LDS of one workgroup");
+    // occupancy is set by the stages
     constexpr bool two = C::LDS_BYTES <= 80 * 1024 - 64;
-    // the reduce stream runs in the two-stage pipelined K loop of eight-wave tiles
-    constexpr bool stream = C::XP && C::NS == 2 && C::WAVES == 8;
-    constexpr int slds = C::LDS_BYTES + C::WAVES / kStreamOps * kStreamLds;
-    static_assert(!stream || slds <= 160 * 1024 - 64, "LDS of one workgroup");
-    const void* sk = nullptr;
-    if constexpr (stream) sk = reinterpret_cast<const void*>(&fused_kernel_8w<C, true, true>);
-    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, elds, C::LDS_BYTES,
-                    kernel_for<CE, true, two>(), sk, stream ? slds : 0,
+    return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, C::LDS_BYTES,
                     kernel_for<C, true, two>(), kernel_for<C, false, two>(),
                     kernel_for<C, true, two, kVarNt>(), kernel_for<C, false, two, kVarNt>(),
                     kernel_for<C, true, two, kVarRows>(),
-                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), epi_kernel_for<C>()};
+                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>()};
 }
 
 TileDesc tile_desc(int id)
 {
     switch (id) {
-    case GEMM_RS_TILE_16x64: return desc<Tile16x64, Tile16x64E>();
-    case GEMM_RS_TILE_64x128: return desc<Tile64x128, Tile64x128E>();
-    case GEMM_RS_TILE_128x128: return desc<Tile128x128, Tile128x128E>();
-    case GEMM_RS_TILE_128x256: return desc<Tile128x256, Tile128x256E>();
-    case GEMM_RS_TILE_256x128: return desc<Tile256x128, Tile256x128E>();
-    case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256E>();
-    default: return TileDesc{0,       0,       0,       0,       0,       0,       0,       nullptr, nullptr,
-                             0,       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    case GEMM_RS_TILE_16x64: return desc<Tile16x64>();
+    case GEMM_RS_TILE_64x128: return desc<Tile64x128>();
+    case GEMM_RS_TILE_128x128: return desc<Tile128x128>();
+    case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
+    case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
+    case GEMM_RS_TILE_256x256: return desc<Tile256x256>();
+    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
     }
 }
 
@@ -159,19 +125,10 @@ int auto_tile(const gemm_rs_config& c)
 
 int resolve_tile(const gemm_rs_config& c) { return c.tile == GEMM_RS_TILE_AUTO ? auto_tile(c) : c.tile; }
 
-// Tiles whose fused kernel can stream the slice sum through the K loop.
-bool stream_tile(int id) { return id == GEMM_RS_TILE_256x256; }
-
-// Tiles whose fused kernel can sum own tiles in the epilogue.
-bool epilogue_tile(int id) { return id == GEMM_RS_TILE_16x64 || id == GEMM_RS_TILE_64x128; }
-
-// Where the slice sum of a fused run without dedicated reducers or engine
-// slots runs.
+// Where the slice sum of a fused run without dedicated reducers runs.
 int resolve_reduce_mode(const gemm_rs_config& c)
 {
-    if (c.num_reducers > 0 || c.engine_interval > 0) return GEMM_RS_REDUCE_TAIL;
-    // automatic: the sum after the last tile, measured faster than the stream
-    // on every benchmark shape
+    if (c.num_reducers > 0) return GEMM_RS_REDUCE_TAIL;
     if (c.reduce_mode == GEMM_RS_REDUCE_AUTO) return GEMM_RS_REDUCE_TAIL;
     return c.reduce_mode;
 }
@@ -221,7 +178,7 @@ struct gemm_rs_handle {
     int ag_strided;
     int ag_units;
     uint32_t ag_unit_bytes;
-    int reduce_mode;       // resolved GEMM_RS_REDUCE_* (TAIL when reducers or engine slots run the sum)
+    int reduce_mode;       // resolved GEMM_RS_REDUCE_* (TAIL when dedicated reducers run the sum)
     int grid;
     int compute_wgs;
     int reducer_wgs;
@@ -282,10 +239,8 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->group_m < 0) return GEMM_RS_ERR_INVALID_ARG;
     if (c->num_reducers < -2) return GEMM_RS_ERR_INVALID_ARG;
     // the adaptive split chooses among dedicated-reducer counts
-    if (c->num_reducers == -2 && (c->engine_interval > 0 || (c->reduce_mode != GEMM_RS_REDUCE_AUTO &&
-                                                              c->reduce_mode != GEMM_RS_REDUCE_TAIL)))
+    if (c->num_reducers == -2 && c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL)
         return GEMM_RS_ERR_INVALID_ARG;
-    if (c->engine_interval < 0 || c->engine_interval > 4096) return GEMM_RS_ERR_INVALID_ARG;
     if (c->debug_flags & ~GEMM_RS_DEBUG_TRACE) return GEMM_RS_ERR_INVALID_ARG;
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_stride != 0 && c->flag_stride != 1 && c->flag_stride != 32) return GEMM_RS_ERR_INVALID_ARG;
@@ -294,23 +249,13 @@ int gemm_rs_validate(const gemm_rs_config* c)
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->flag_protocol != GEMM_RS_FLAGS_TILE && c->flag_protocol != GEMM_RS_FLAGS_ROW_COUNTER)
         return GEMM_RS_ERR_INVALID_ARG;
-    // row counters are read by the sum after the last tile and by dedicated or
-    // co-resident reducers; the in-loop engine and the stream poll tile flags
-    if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER &&
-        (c->engine_interval > 0 || c->reduce_mode == GEMM_RS_REDUCE_STREAM))
+    // both are kernel variants of the fused kernel (and, for the stores, of
+    // the GEMM-only kernel); one at a time
+    if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL && c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER)
         return GEMM_RS_ERR_INVALID_ARG;
-    // both are kernel variants of the tail sum / reducer-workgroup kernel
-    // (and, for the stores, of the GEMM-only kernel); one at a time
-    if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL &&
-        (c->engine_interval > 0 || c->reduce_mode == GEMM_RS_REDUCE_STREAM ||
-         c->reduce_mode == GEMM_RS_REDUCE_EPILOGUE || c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER))
+    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_CORESIDENT)
         return GEMM_RS_ERR_INVALID_ARG;
-    if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER && c->reduce_mode == GEMM_RS_REDUCE_EPILOGUE)
-        return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_EPILOGUE)
-        return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL &&
-        (c->num_reducers > 0 || c->engine_interval > 0))
+    if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL && c->num_reducers > 0)
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->tp != 8) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->M % c->tp != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
@@ -322,7 +267,7 @@ int gemm_rs_validate(const gemm_rs_config* c)
         S * (int64_t)c->N > ((int64_t)1 << 40))
         return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     // slice buffers are written through buffer resources with 31-bit byte
-    // offsets (and the reduce engine uses 32-bit element offsets)
+    // offsets
     if ((int64_t)(c->M / c->tp) * c->N * 2 >= ((int64_t)1 << 31)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     // X_r and W_r are read through buffer resources with 31-bit byte offsets
     if ((int64_t)c->M * c->K_local * 2 >= ((int64_t)1 << 31) ||
@@ -333,9 +278,6 @@ int gemm_rs_validate(const gemm_rs_config* c)
     const int64_t tiles = (int64_t)c->tp * ((S + bm - 1) / bm) * (((int64_t)c->N + bn - 1) / bn);
     if (tiles > (1 << 30)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->drop_flag >= 0 && c->drop_flag >= tiles) return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM && !stream_tile(resolve_tile(*c))) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
-    if (c->reduce_mode == GEMM_RS_REDUCE_EPILOGUE && !epilogue_tile(resolve_tile(*c)))
-        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return GEMM_RS_OK;
 }
 
@@ -484,34 +426,16 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     h->num_cus = prop.multiProcessorCount;
     h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
 
-    // automatic: no dedicated reducers, the engine waves of the compute
-    // workgroups run the reduction
+    // automatic: no dedicated reducers, the compute workgroups sum the slice
     const int red_req = c->num_reducers < 0 ? 0 : c->num_reducers;
-    hipError_t e = hipFuncSetAttribute(h->td.engine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       h->td.engine_lds_bytes);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
+    hipError_t e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
     if (e == hipSuccess)
         e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
-    if (e == hipSuccess && h->td.stream_kernel)
-        e = hipFuncSetAttribute(h->td.stream_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                h->td.stream_lds_bytes);
-    if (e == hipSuccess && h->td.epi_kernel)
-        e = hipFuncSetAttribute(h->td.epi_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
     h->reduce_mode = resolve_reduce_mode(*c);
     int occ = 0;
     const void* fk = h->td.kernel;
     h->fused_lds = h->td.lds_bytes;
-    if (red_req == 0 && c->engine_interval > 0) {
-        fk = h->td.engine_kernel;
-        h->fused_lds = h->td.engine_lds_bytes;
-    } else if (h->reduce_mode == GEMM_RS_REDUCE_STREAM) {
-        fk = h->td.stream_kernel;
-        h->fused_lds = h->td.stream_lds_bytes;
-    } else if (h->reduce_mode == GEMM_RS_REDUCE_EPILOGUE) {
-        fk = h->td.epi_kernel;
-    }
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, h->td.threads, h->fused_lds);
     if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
     // the persistent grid holds the workgroups per CU the kernel was built for
@@ -638,7 +562,6 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.flag_stride = h->flag_stride;
     a.drop_flag = h->cfg.drop_flag;
     a.trace_on = (h->cfg.debug_flags & GEMM_RS_DEBUG_TRACE) ? 1 : 0;
-    a.engine_every = h->cfg.engine_interval;
     a.coresident = h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT ? 1 : 0;
 }
 
@@ -668,17 +591,7 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // GEMM_ONLY has no reducers, so its groups always split evenly
     if (!fused) a.strided = h->strided;
     void* params[] = {&a};
-    // in-loop engine slots need the kernel whose waves are split into stage
-    // loaders and engine waves; otherwise every wave loads stages
-    // (the reduce stream: every wave loads stages and streams its share of the sum)
-    const bool engine = fused && h->reducer_wgs == 0 && h->cfg.engine_interval > 0;
-    const bool stream = fused && h->reducer_wgs == 0 && h->reduce_mode == GEMM_RS_REDUCE_STREAM;
-    const bool epi = fused && h->reducer_wgs == 0 && h->reduce_mode == GEMM_RS_REDUCE_EPILOGUE;
-    const void* k = engine ? h->td.engine_kernel
-                  : stream ? h->td.stream_kernel
-                  : epi    ? h->td.epi_kernel
-                  : fused  ? h->td.kernel
-                           : h->td.gemm_kernel;
+    const void* k = fused ? h->td.kernel : h->td.gemm_kernel;
     // (a GEMM-only launch runs on the compute workgroups' grid: the
     // co-resident reducers' extra workgroup per CU is not part of the GEMM)
     if (!fused) a.num_compute = h->gemm_grid;
@@ -784,6 +697,12 @@ int gemm_rs_run_allgather(gemm_rs_handle* h, int32_t mode, const void* const* x_
     const bool needs_gemm = mode != GEMM_RS_MODE_REDUCE_ONLY;
     if (!x_slices || !x_gathered) return GEMM_RS_ERR_INVALID_ARG;
     if (!aligned16(x_gathered)) return GEMM_RS_ERR_MISALIGNED;
+    if (mode == GEMM_RS_MODE_FUSED) {
+        // the fused launch's no-stale-line argument needs every 128-byte line of
+        // x_gathered inside one copy block: the buffer and each slice aligned
+        if ((reinterpret_cast<uintptr_t>(x_gathered) & 127u) != 0) return GEMM_RS_ERR_MISALIGNED;
+        if (((int64_t)h->g.S * h->g.K * 2) % 128 != 0) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+    }
     for (int d = 0; d < h->g.tp; ++d) {
         // GEMM_ONLY reads only this rank's own slice (the rest from x_gathered)
         if (!needs_copy && d != h->g.rank) continue;

@@ -13,21 +13,18 @@
 //             scope and publishes the tile's ready flag;
 //   reducer   sums this rank's slice with the tp-1 peer partials, tile by tile
 //             as the ready flags arrive.
-// The reduction runs either in dedicated reducer workgroups or, by default,
-// inside the compute workgroups: there the first half of the waves ("loader"
-// waves) issue every stage load of the GEMM and the second half ("engine"
-// waves) run the reduce engine between their MFMAs.  Vector-memory operations
-// of one wave retire in issue order, so an HBM load issued by a wave that also
-// waits for stage loads would hold every later stage of that wave behind one
-// HBM round trip; engine waves wait for stage loads only through the barrier.
+// By default the compute workgroups themselves sum the slice after their last
+// tile; dedicated reducer workgroups (arrival tickets) and co-resident reducer
+// workgroups (one more per CU, role by index) are the other placements.
 //
 // Workgroup g belongs to group g % 8, which is the XCD it runs on (workgroups
-// are dispatched to the 8 XCDs round-robin).  Each group hands out its own
-// arrival tickets: the first C_x arrivals of group x compute, the next R_x
-// reduce.  A reducer therefore exists only after every compute workgroup of its
-// group is resident, and compute workgroups never wait, so reducers cannot
-// starve their producers.  Compute slots are split so that the workgroups of
-// one XCD work on tiles that share rows of X or columns of W in that XCD's L2.
+// are dispatched to the 8 XCDs round-robin).  With dedicated reducers each
+// group hands out its own arrival tickets: the first C_x arrivals of group x
+// compute, the next R_x reduce.  A reducer therefore exists only after every
+// compute workgroup of its group is resident, and compute workgroups never
+// wait, so reducers cannot starve their producers.  Compute slots are split so
+// that the workgroups of one XCD work on tiles that share rows of X or columns
+// of W in that XCD's L2.
 //
 // The run epoch, the tickets and the reducer work counter live in device
 // memory (see fused_body), so a launch needs no host-side state and can be
@@ -65,10 +62,10 @@ constexpr int kRsrcFlags = 0x00020000;
 // XCD sees it once the store has completed -- no L2 write-back is needed to
 // publish a tile).
 constexpr int kStoreDevice = 16;
-// Cache-policy bits of the engine's loads and stores: peer partials are read
-// once and sums written once (non-temporal); the local slice and the flags are
-// read at device scope (sc1), so a copy left in this XCD's L2 by an earlier
-// run is never used.
+// Cache-policy bits of the slice sum's loads and stores: peer partials are
+// read once and sums written once (non-temporal); the local slice and the
+// flags are read at device scope (sc1), so a copy left in this XCD's L2 by an
+// earlier run is never used.
 constexpr int kAuxNt = 2;
 constexpr int kAuxSc1 = 16;
 // Routed tile stores with the non-temporal hint on top of device scope: the
@@ -83,20 +80,17 @@ constexpr int kStoreDeviceNt = kStoreDevice | kAuxNt;
 constexpr int kVarNt = 1;
 constexpr int kVarRows = 2;
 
-// Reduce engine: 16-byte loads per operation (one per lane each), LDS bytes an
-// operation lands in, operations in flight per engine wave.
-constexpr int kEngLoads = 2;
-constexpr int kEngAreaBytes = kEngLoads * 1024;
-constexpr int kEngAreas = 2;
 
-// Handle-owned device state, zeroed at creation.
+// Handle-owned device state, zeroed at creation.  The arrival tickets and the
+// reducer claim counter exist twice: run e uses set e & 1 and clears set
+// (e + 1) & 1 for the next run, which no workgroup of run e touches (runs of
+// one handle do not overlap), so no counter is ever reset while a run may
+// still use it.
 struct DeviceState {
-    uint32_t pad1;
-    uint32_t role[kGroups];   // per-group arrival tickets (dedicated reducers only)
-    uint32_t unit;            // next reducer unit to claim
-    uint32_t pad0;
-    int32_t status[2];        // [0] error code, [1] flag index that timed out
-    uint32_t pad[3];
+    uint32_t role[2][kGroups];  // per-group arrival tickets (dedicated reducers only)
+    uint32_t unit[2];           // next reducer unit to claim
+    int32_t status[2];          // [0] error code, [1] flag index that timed out
+    uint32_t pad[12];
 };
 
 struct Args {
@@ -122,7 +116,6 @@ struct Args {
     int32_t fused;           // 1: release flags, reducers run, epoch advances
     int32_t drop_flag;
     int32_t trace_on;
-    int32_t engine_every;    // K steps between reduce-engine slots (0: reduce after the last tile)
     int32_t coresident;      // 1: the reducer workgroups sit beside the compute workgroups of
                              // their CUs and sum a static share of items (peers first)
     // all-gather + GEMM runs (the column-parallel layer): M x K gathered
@@ -141,8 +134,7 @@ struct Args {
 // BM x BN output tile, BK deep stages, NS stages in LDS, WAVES_M x WAVES_N
 // waves (4: one wave per SIMD, 8: two), MF x MF MFMA output blocks (32:
 // v_mfma_f32_32x32x16_bf16, 16: v_mfma_f32_16x16x32_bf16).  The first LW waves
-// issue the stage loads (LW = 0: all of them); the other EW waves run the
-// reduce engine.
+// issue the stage loads (LW = 0: all of them); the other EW waves issue none.
 template <int BM_, int BN_, int BK_, int NS_, int WAVES_M_, int WAVES_N_, int MF_, int LW_ = 0>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
@@ -182,7 +174,6 @@ struct TileCfg {
     static constexpr int STORES = STAGED_EPI ? FM * (WTN / 64) * 4 : FM * FN * (MF == 32 ? 4 : 1);
     static_assert(!STAGED_EPI || WAVES * EPI_AREA <= STAGE_BYTES, "epilogue staging fits one stage buffer");
     static_assert((NS - 2) * LPS + STORES <= 63, "vmcnt range");
-    static constexpr int ENG_LDS = EW * kEngAreas * kEngAreaBytes;
     // One workgroup per CU (four waves whose stages fit only once, or eight
     // waves) with every wave loading: the K loop is pipelined across steps.
     static constexpr bool XP = EW == 0 && LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
@@ -579,17 +570,6 @@ __device__ __forceinline__ int store_sum(const Args& a, const u32x4& v, uint32_t
     return 1 + kPeers;
 }
 
-template <int AUX>
-__device__ __forceinline__ void lds_load16(const uint16_t* g, const char* slot)
-{
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)slot, 16, 0, AUX);
-}
-
-__device__ __forceinline__ void lds_load_flag(const uint32_t* g, const char* slot)
-{
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)slot, 4, 0, kAuxSc1);
-}
-
 // out = RNE( (((0 + peer_0) + ... + peer_6) + local ) for 8 elements at `off`
 // (standalone reduce kernel; plain loads are coherent after the kernel
 // boundary).
@@ -636,43 +616,15 @@ __device__ __forceinline__ void sum_block(const Args& a, int row0, int rows, int
     }
 }
 
-// ---------------------------------------------------------------- reduce engine
+// ---------------------------------------------------------------- slice-sum items
 //
 // The slice sum is cut into items: item i covers 64 16-byte chunks (512
 // elements) of own-slice tile t = i / IPT, one chunk per lane, where own tiles
 // are numbered row-major (t = tile row * tile columns + tile column, so own
 // tile t carries ready flag rank * tiles_per_slice + t); an item spans
 // 64 / (BN/8) consecutive rows of the tile, so a lane's offset inside an item
-// is a constant and the item's base offset is wave-uniform.  Engine wave gw (of
-// W) owns items gw, gw + W, gw + 2W, ... -- tile order.
-//
-// Between MFMAs an engine wave sums the items whose tile is flagged, in four
-// steps of two loads each, in the sum order:
-//   step 0: peers 0, 1      acc = (0 + p0) + p1
-//   step 1: peers 2, 3      acc = (acc + p2) + p3
-//   step 2: peers 4, 5      acc = (acc + p4) + p5
-//   step 3: peer 6, local   acc = (acc + p6) + local, rounded and stored to out
-// and otherwise polls: POLL reads 64 consecutive ready flags (own tiles
-// anchor .. anchor+63, one per lane).  Operations are issued and consumed in
-// order, two in flight: each engine slot consumes the older operation and
-// issues a new one.  The loads land in the wave's two LDS areas (LDS-direct
-// global loads), so no register is live while they fly; the consumer waits
-// with s_waitcnt until at most the vector-memory instructions issued after the
-// operation are outstanding (the wave counts every one it issues: engine
-// loads, out stores, epilogue stores).  Every lane issues every load and store
-// (lanes without a valid chunk read the slice's first chunk and store out of
-// bounds), so the count is exact.  Items still open after the wave's last
-// tile are summed by engine_drain.
+// is a constant and the item's base offset is wave-uniform.
 
-enum EngineOp { kOpNone = 0, kOpStep = 1, kOpPoll = 2 };
-
-struct EngOp {
-    int op, step, area, anchor;
-    uint32_t soff;    // STEP 3: this lane's byte offset in out (kOob: no valid chunk)
-    uint32_t vm_end;  // the wave's vector-memory count right after the operation's issue
-};
-
-// Where an item lies: item i is chunk row (i % IPT) * RPI .. of own tile
 // i / IPT, tile t = tile row * tile columns + tile column.
 struct ItemMap {
     int nitems;         // items of the slice
@@ -717,179 +669,6 @@ __device__ __forceinline__ uint32_t item_boff(const ItemMap& m, const Args& a, i
     const uint32_t base = (uint32_t)(tml * a.g.bm + row) * (uint32_t)a.g.N + (uint32_t)(tn * a.g.bn);
     return valid ? (base + (uint32_t)m.lane_off) * 2u : kOob;
 }
-
-struct Engine {
-    char* areas;    // kEngAreas LDS areas of kEngAreaBytes
-    ItemMap m;
-    int next;       // next owned item not yet started
-    int stride;     // engine waves W
-    int nitems, ipt, ipt_log2;  // copies of m's (items per tile: a power of two)
-    // issue side
-    int i_item;     // item being issued, -1 if none
-    int i_step;     // its next step
-    uint32_t i_off; // this lane's element offset in the slice (0 if no valid chunk)
-    uint32_t i_soff;
-    int anchor;     // tile of bit 0 of `ready`
-    uint64_t ready; // ready tiles anchor .. anchor+63
-    int area;       // area of the next operation
-    // consume side
-    f32x8 acc;
-    // in flight, oldest first
-    EngOp o0, o1;
-    uint32_t vm;         // vector-memory instructions issued by this wave
-    uint32_t vm_stores;  // vm right after this wave's last epilogue stores
-    uint32_t epoch;
-};
-
-// Element offset of this lane's chunk of an item in the slice (0 if the chunk
-// lies outside the possibly ragged tile) and its byte offset for a store
-// (kOob then).
-__device__ __forceinline__ void item_offsets(const Engine& e, const Args& a, int item, uint32_t& off,
-                                             uint32_t& soff)
-{
-    soff = item_boff(e.m, a, item);
-    off = soff == kOob ? 0u : soff >> 1;
-}
-
-__device__ __forceinline__ void engine_init(Engine& e, const Args& a, char* areas, int gw, int waves,
-                                            uint32_t epoch)
-{
-    e.areas = areas;
-    e.m = item_map(a);
-    e.ipt_log2 = e.m.ipt_log2;
-    e.ipt = 1 << e.ipt_log2;
-    e.nitems = e.m.nitems;
-    e.next = uni(gw);
-    e.stride = waves;
-    e.i_item = -1;
-    e.i_step = 0;
-    e.i_off = 0;
-    e.i_soff = kOob;
-    e.anchor = 0;
-    e.ready = 0;
-    e.area = 0;
-    e.o0 = EngOp{kOpNone, 0, 0, 0, kOob, 0u};
-    e.o1 = e.o0;
-    e.vm = 0;
-    e.vm_stores = 0;
-    e.epoch = epoch;
-}
-
-__device__ __forceinline__ bool tile_ready(const Engine& e, int tile)
-{
-    const int b = tile - e.anchor;
-    return b >= 0 && b < 64 && ((e.ready >> b) & 1ull);
-}
-
-// Move the ready window so that it starts at the oldest tile still needed.
-__device__ __forceinline__ void engine_reanchor(Engine& e)
-{
-    int want = e.i_item >= 0 ? e.i_item : e.next;
-    if (want > e.nitems) want = e.nitems;
-    want >>= e.ipt_log2;
-    const int sh = want - e.anchor;
-    if (sh > 0) {
-        e.ready = sh >= 64 ? 0ull : (e.ready >> sh);
-        e.anchor = want;
-    }
-}
-
-__device__ __forceinline__ char* area_ptr(const Engine& e, int area) { return e.areas + area * kEngAreaBytes; }
-
-__device__ __forceinline__ u32x4 engine_chunk(const Engine& e, int area, int k)
-{
-    return *reinterpret_cast<const u32x4*>(area_ptr(e, area) + k * 1024 + (threadIdx.x & 63) * 16);
-}
-
-// Consume an operation whose loads have completed.
-__device__ __forceinline__ void engine_consume(Engine& e, const Args& a, const EngOp& o)
-{
-    if (o.op == kOpStep) {
-        f32x8 acc = o.step == 0 ? f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f} : e.acc;
-        acc = add8(acc, engine_chunk(e, o.area, 0));
-        acc = add8(acc, engine_chunk(e, o.area, 1));
-        if (o.step < 3) {
-            e.acc = acc;
-        } else {
-            e.vm += store_sum(a, pack8(acc), o.soff);
-        }
-    } else if (o.op == kOpPoll) {
-        const int lane = threadIdx.x & 63;
-        const uint32_t f = *reinterpret_cast<const uint32_t*>(area_ptr(e, o.area) + lane * 4);
-        const bool mine = o.anchor + lane < a.g.ts;
-        const uint64_t bits = __builtin_amdgcn_ballot_w64(mine && f == e.epoch);
-        // the window has only moved forward since the poll was issued
-        const int sh = e.anchor - o.anchor;
-        if (sh < 64) e.ready |= bits >> sh;
-    }
-}
-
-// Choose and issue the next operation; with `start` false no new item is
-// begun and no flag is polled.
-__device__ __forceinline__ EngOp engine_issue(Engine& e, const Args& a, bool start)
-{
-    EngOp o{kOpNone, 0, e.area, e.anchor, kOob, 0u};
-    if (start && e.i_item < 0 && e.next < e.nitems && tile_ready(e, e.next >> e.ipt_log2)) {
-        e.i_item = e.next;
-        e.i_step = 0;
-        e.next += e.stride;
-        item_offsets(e, a, e.i_item, e.i_off, e.i_soff);
-    }
-    char* ar = area_ptr(e, o.area);
-    if (e.i_item >= 0) {
-        o.op = kOpStep;
-        o.step = e.i_step;
-        o.soff = e.i_soff;
-        const uint32_t off = e.i_off;
-        switch (e.i_step) {
-        case 0:
-            lds_load16<kAuxNt>(a.peers[0] + off, ar);
-            lds_load16<kAuxNt>(a.peers[1] + off, ar + 1024);
-            break;
-        case 1:
-            lds_load16<kAuxNt>(a.peers[2] + off, ar);
-            lds_load16<kAuxNt>(a.peers[3] + off, ar + 1024);
-            break;
-        case 2:
-            lds_load16<kAuxNt>(a.peers[4] + off, ar);
-            lds_load16<kAuxNt>(a.peers[5] + off, ar + 1024);
-            break;
-        default:
-            lds_load16<kAuxNt>(a.peers[6] + off, ar);
-            lds_load16<kAuxSc1>(a.dst[a.g.rank] + off, ar + 1024);
-            break;
-        }
-        e.vm += 2;
-        if (++e.i_step == 4) e.i_item = -1;
-    } else if (start && e.next < e.nitems) {
-        o.op = kOpPoll;
-        const int lane = threadIdx.x & 63;
-        const int t = e.anchor + lane < a.g.ts ? e.anchor + lane : 0;
-        lds_load_flag(a.flags + (int64_t)(a.g.rank * a.g.ts + t) * a.flag_stride, ar);
-        e.vm += 1;
-    }
-    o.vm_end = e.vm;
-    if (o.op != kOpNone) e.area ^= 1;
-    engine_reanchor(e);
-    // keep the issue order of these loads against later memory operations
-    __builtin_amdgcn_sched_barrier(0);
-    return o;
-}
-
-// One engine slot: consume the older operation in flight, issue a new one.
-__device__ __forceinline__ void engine_step(Engine& e, const Args& a, bool start)
-{
-    if (e.o0.op != kOpNone) {
-        wait_vmcnt_upto(e.vm - e.o0.vm_end);
-        engine_consume(e, a, e.o0);
-    }
-    e.o0 = e.o1;
-    e.o1 = engine_issue(e, a, start);
-}
-
-// Waits (device-scope polls, short sleeps) until own tile t is flagged.  The
-// first wait that exceeds the watchdog limit reports the tile and sets
-// gave_up; after that no wait blocks, so a drain never waits longer than one
 // watchdog period in total.  ROWS: the row-counter protocol.
 template <int SLEEP = 2, bool ROWS = false>
 __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, bool& gave_up)
@@ -955,359 +734,22 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
     }
 }
 
-// After the last tile of an engine wave that ran in-loop slots: settle the
-// operations in flight and the item being summed (its tile is flagged), then
-// drain the wave's remaining items.
-__device__ __forceinline__ void engine_drain(Engine& e, const Args& a)
-{
-    while (e.o0.op != kOpNone || e.o1.op != kOpNone || e.i_item >= 0) engine_step(e, a, false);
-    wait_vmcnt<0>();
-    drain_items<2>(a, e.m, e.next, e.stride, e.epoch);
-}
-
-// ---------------------------------------------------------------- reduce stream
-//
-// The slice sum streamed through the cross-step pipelined K loop (eight-wave
-// workgroups, two stages).  With kStreamOps = 1 every wave streams; with 2
-// one wave per SIMD (waves 0..3) does, at twice the rate, so that the sibling
-// wave on its SIMD keeps the matrix core fed while the streaming wave runs the
-// sum's bookkeeping (measured: no better).  Streaming wave gw of TW owns a
-// contiguous range of items, [gw * n / TW, (gw + 1) * n / TW) of n, and per K
-// step issues at most kStreamOps vector-memory instructions of the sum, right
-// after its stage refill.  With two stages the next step's wait then lets
-// those instructions stay outstanding (and only those), so an operation issued
-// at step k has completed by the wait of step k + 2, where it is consumed: the
-// sum adds nothing to the stage waits.  Loads land in the wave's LDS slots
-// (LDS-direct loads), so nothing but the running FP32 sum is held in registers
-// while they fly.
-//
-// Per item, in the sum order: poll the tile's ready flag (unless the wave has
-// already seen that tile flagged), load peers 0..6 (they need no flag), load
-// the local chunk once the flag has been seen, then store the rounded sum into
-// `out` and, in an all-reduce run, into the 7 gather buffers, one store per
-// step.  A poll that finds the tile not yet flagged is repeated only after
-// kStreamBackoff steps; a step with nothing to issue and nothing in flight
-// runs no stream code at all.  Items a streaming wave has not finished when
-// the workgroup's last tile is done are summed by drain_items, split between
-// that wave and the waves that do not stream on its SIMD.
-
-constexpr int kStreamOps = 1;                      // per streaming wave and K step
-constexpr int kStreamQueue = 2 * kStreamOps;       // operations in flight (two steps)
-constexpr int kStreamSlots = kStreamQueue + 1;     // 1 KiB LDS slots per streaming wave
-constexpr int kStreamLds = kStreamSlots * 1024;
-constexpr int kStreamBackoff = 8;                  // K steps between polls of one tile
-
-enum StreamOp { kSoNone = 0, kSoPeer = 1, kSoPoll = 2, kSoLocal = 3 };
-
-struct Stream {
-    char* slots;          // this wave's kStreamSlots LDS slots
-    const uint16_t* local;
-    ItemMap m;
-    int item, end;        // next item to finish, end of the wave's range
-    int phase;            // 0..6: load peer `phase`; 7: load local; 8: local in flight; 9..: stores
-    int nst;              // stores per item (1, or 8 in an all-reduce run)
-    int ready_tile;       // the last tile seen flagged (-1: none)
-    int poll_tile;        // tile of the poll in flight (-1: none)
-    int poll_wait;        // steps before the next poll may be issued
-    int slot;             // slot of the next operation
-    int q[kStreamQueue];  // operations in flight, oldest first (kSoNone: none)
-    int nissued;          // vector-memory instructions the last step issued
-    uint32_t soff;        // this lane's byte offset of the item's chunk (kOob: none)
-    uint32_t epoch;
-    int gw0, tw;          // the workgroup's first streaming wave, streaming waves in all
-    f32x8 acc;
-};
-
-// arr[i] for a wave-uniform i in 0..6, as a chain of selects: a switch would
-// merge the pointers through control flow, which the compiler may keep in
-// vector registers (and then wrap every buffer access of the loop in a
-// per-lane loop over its resource).
-template <class T>
-__device__ __forceinline__ T pick7(T const (&arr)[kPeers], int i)
-{
-    T r = arr[0];
-#pragma unroll
-    for (int k = 1; k < kPeers; ++k) r = i == k ? arr[k] : r;
-    return r;
-}
-
-__device__ __forceinline__ void stream_item_start(Stream& s, const Args& a)
-{
-    s.phase = 0;
-    s.soff = s.item < s.end ? item_boff(s.m, a, s.item) : kOob;
-}
-
-// Streaming wave gw of tw (gw0: the workgroup's first); a wave that does not
-// stream passes active = false and gets an empty range.
-__device__ __forceinline__ void stream_init(Stream& s, const Args& a, char* slots, int gw0, int gw, int tw,
-                                            bool active, uint32_t epoch)
-{
-    s.slots = slots;
-    s.local = a.dst[a.g.rank];
-    s.m = item_map(a);
-    s.gw0 = gw0;
-    s.tw = tw;
-    const int64_t n = s.m.nitems;
-    s.item = active ? uni((int)(n * gw / tw)) : 0;
-    s.end = active ? uni((int)(n * (gw + 1) / tw)) : 0;
-    s.nst = a.gather_on ? 1 + kPeers : 1;
-    s.ready_tile = -1;
-    s.poll_tile = -1;
-    s.poll_wait = 0;
-    s.slot = 0;
-#pragma unroll
-    for (int i = 0; i < kStreamQueue; ++i) s.q[i] = kSoNone;
-    s.nissued = 0;
-    // (the epoch comes from an LDS read: make it provably uniform, so that
-    // the whole stream state stays in scalar registers)
-    s.epoch = (uint32_t)uni((int)epoch);
-    s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    stream_item_start(s, a);
-}
-
-// Operation code: kind | slot << 4 | peer << 8.
-__device__ __forceinline__ void stream_consume(Stream& s, int code)
-{
-    const int kind = code & 15;
-    if (kind == kSoNone) return;
-    const char* slot = s.slots + ((code >> 4) & 7) * 1024;
-    if (kind == kSoPoll) {
-        const uint32_t f = (uint32_t)uni((int)*reinterpret_cast<const uint32_t*>(slot));
-        if (f == s.epoch)
-            s.ready_tile = s.poll_tile;
-        else
-            s.poll_wait = kStreamBackoff;
-        s.poll_tile = -1;
-        return;
-    }
-    const u32x4 v = *reinterpret_cast<const u32x4*>(slot + (threadIdx.x & 63) * 16);
-    if (kind == kSoPeer && (code >> 8) == 0) s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    s.acc = add8(s.acc, v);
-    if (kind == kSoLocal) s.phase = 9;
-}
-
-// Issues the next operation, if any; returns its code (kSoNone when nothing
-// was issued).
-__device__ __forceinline__ int stream_issue(Stream& s, const Args& a)
-{
-    char* slot = s.slots + s.slot * 1024;
-    const uint32_t off = s.soff == kOob ? 0u : s.soff >> 1;  // element offset of a valid chunk
-    int code = kSoNone;
-    bool issued = false;
-    if (s.item < s.end) {
-        const int tile = s.item >> s.m.ipt_log2;
-        const bool ready = tile == s.ready_tile;
-        if (!ready && s.poll_tile < 0 && s.poll_wait == 0 && (s.phase == 0 || s.phase == 7)) {
-            lds_load_flag(a.flags + (int64_t)(a.g.rank * a.g.ts + tile) * a.flag_stride, slot);
-            s.poll_tile = tile;
-            code = kSoPoll;
-            issued = true;
-        } else if (s.phase < 7) {
-            lds_load16<kAuxNt>(pick7(a.peers, s.phase) + off, slot);
-            code = kSoPeer | (s.phase << 8);
-            ++s.phase;
-            issued = true;
-        } else if (s.phase == 7 && ready) {
-            lds_load16<kAuxSc1>(s.local + off, slot);
-            code = kSoLocal;
-            s.phase = 8;
-            issued = true;
-        } else if (s.phase >= 9) {
-            const u32x4 v = pack8(s.acc);
-            uint16_t* dst = s.phase == 9 ? a.out : pick7(a.gather, s.phase - 10);
-            __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(dst, 0, a.slice_bytes, kRsrcFlags),
-                                                   s.soff, 0, kAuxNt);
-            issued = true;
-            if (++s.phase == 9 + s.nst) {
-                ++s.item;
-                stream_item_start(s, a);
-            }
-        }
-    }
-    if (!issued) return kSoNone;
-    ++s.nissued;
-    code |= s.slot << 4;
-    s.slot = s.slot == kStreamSlots - 1 ? 0 : s.slot + 1;
-    return code;
-}
-
-// One K step of the stream, after the step's refill: kStreamOps times,
-// consume the operation issued two steps ago and issue the next.  Nothing
-// runs once the wave's items are done and nothing is in flight.
-__device__ __forceinline__ void stream_step(Stream& s, const Args& a)
-{
-    __builtin_amdgcn_sched_barrier(0);
-    bool busy = s.item < s.end;
-#pragma unroll
-    for (int i = 0; i < kStreamQueue; ++i) busy = busy || s.q[i] != kSoNone;
-    s.nissued = 0;
-    if (busy) {
-        if (s.poll_wait > 0) --s.poll_wait;
-#pragma unroll
-        for (int k = 0; k < kStreamOps; ++k) {
-            stream_consume(s, s.q[0]);
-#pragma unroll
-            for (int i = 0; i + 1 < kStreamQueue; ++i) s.q[i] = s.q[i + 1];
-            s.q[kStreamQueue - 1] = stream_issue(s, a);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// Wait for the stage refill issued by the previous step, letting the stream
-// instructions issued after it stay in flight.
-template <int B>
-__device__ __forceinline__ void stream_wait(const Stream& s)
-{
-    static_assert(kStreamOps <= 2, "wait counts below");
-    if (s.nissued == 0)
-        wait_vmcnt<B>();
-    else if (s.nissued == 1)
-        wait_vmcnt<B + 1>();
-    else
-        wait_vmcnt<B + 2>();
-}
-
-// After a wait for every vector-memory instruction: consume what is in flight.
-__device__ __forceinline__ void stream_settle(Stream& s)
-{
-#pragma unroll
-    for (int i = 0; i < kStreamQueue; ++i) {
-        stream_consume(s, s.q[i]);
-        s.q[i] = kSoNone;
-    }
-    s.nissued = 0;
-}
-
-// After the last tile, in every wave of the workgroup: the items the streaming
-// waves have not finished (an item in progress restarts) are split between
-// each streaming wave w and the waves w + SW, w + 2 SW, ... on its SIMD.
-// `progress` is an LDS array of SW entries; called by all waves, it holds one
-// workgroup barrier.
-template <int WAVES>
-__device__ __forceinline__ void stream_drain(const Stream& s, const Args& a, int wave, int* progress)
-{
-    constexpr int SW = WAVES / kStreamOps;
-    if (wave < SW && (threadIdx.x & 63) == 0) progress[wave] = s.item;
-    __syncthreads();
-    const int w = wave % SW, part = wave / SW;
-    const int64_t n = s.m.nitems;
-    const int gw = s.gw0 + w;
-    const int end = (int)(n * (gw + 1) / s.tw);
-    const int cur = uni(progress[w]);
-    ItemMap m = s.m;
-    m.nitems = cur + (end - cur) * (part + 1) / kStreamOps;
-    drain_items<2>(a, m, cur + (end - cur) * part / kStreamOps, 1, s.epoch);
-}
-
-
-// ---------------------------------------------------------------- sum in the epilogue
-//
-// reduce_mode EPILOGUE (four-wave tiles small enough to keep a tile's peer
-// chunks in registers): the workgroup that computes an own-slice tile sums it
-// in its epilogue, from its accumulators, the way FLUX fuses the
-// reduce-scatter into the GEMM epilogue (TL;DR of "FLUX: Fast Software-based
-// Communication Overlap On GPUs Through Kernel Fusion").  Each lane loads the
-// 7 peers' values of exactly the output elements its accumulators hold (the
-// same element map as the unstaged tile store) before the tile's first stage
-// loads, so they arrive with the first stage; the epilogue forms
-// (((0 + p_0) + ...) + p_6) + RNE_bf16(acc) in FP32, the oracle's order, and
-// stores it rounded to `out` (and the gather buffers in an all-reduce run).
-// No flag is polled: the producer sums its own tile.
-
-template <class C>
-struct PeerFrag {
-    static constexpr int G = C::MF == 32 ? 4 : 1;  // groups of four columns per MFMA block
-    u32x2 v[kPeers][C::FM][C::FN][G];
-};
-
-// Loads the peer values of tile (srow0.., n0..) that this lane's accumulators
-// hold; elements outside the (ragged) tile read as zero.
-template <class C>
-__device__ __forceinline__ void epi_load_peers(const Args& a, PeerFrag<C>& pf, int srow0, int rows, int n0, int cols)
-{
-    const int lane = threadIdx.x & 63;
-    const int wave = uni((int)(threadIdx.x >> 6));
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const uint32_t N = (uint32_t)a.g.N;
-#pragma unroll
-    for (int s = 0; s < kPeers; ++s) {
-        const __amdgpu_buffer_rsrc_t rp =
-            __builtin_amdgcn_make_buffer_rsrc((void*)a.peers[s], 0, a.slice_bytes, kRsrcFlags);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            const int m = wm * C::WTM + i * C::MF + (lane % C::MF);
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                for (int grp = 0; grp < PeerFrag<C>::G; ++grp) {
-                    const int n = C::MF == 32 ? wn * C::WTN + j * 32 + grp * 8 + (lane / 32) * 4
-                                              : wn * C::WTN + j * 16 + (lane / 16) * 4;
-                    const uint32_t off =
-                        (m < rows && n < cols) ? (((uint32_t)(srow0 + m) * N + (uint32_t)(n0 + n)) * 2u) : kOob;
-                    pf.v[s][i][j][grp] =
-                        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, kAuxNt));
-                }
-        }
-    }
-}
-
-// os = (((0 + p_0) + ... ) + p_6) + RNE_bf16(st), element by element (FP32).
-template <class C>
-__device__ __forceinline__ void epi_sum(const PeerFrag<C>& pf, const TileState<C>& st, TileState<C>& os)
-{
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-            for (int grp = 0; grp < PeerFrag<C>::G; ++grp)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int s = 0; s < kPeers; ++s) {
-                        const uint32_t w = e < 2 ? pf.v[s][i][j][grp].x : pf.v[s][i][j][grp].y;
-                        acc += bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
-                    }
-                    const int k = grp * 4 + e;
-                    const float local = bf16_bits_to_f32(pack_bf16x2(st.acc[i][j][k], 0.0f) & 0xFFFFu);
-                    os.acc[i][j][k] = acc + local;
-                }
-}
-
-// The epilogue's sum stores: the rounded sums into `out` and, in an all-reduce
-// run, into the gather buffers (each through the tile store's LDS staging).
-template <class C>
-__device__ __forceinline__ void epi_store(const Args& a, const TileState<C>& os, char* area, int srow0, int rows,
-                                          int n0, int cols)
-{
-    store_tile<C>(a, os, area, __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.slice_bytes, kRsrcFlags), srow0, rows,
-                  n0, cols);
-    if (a.gather_on) {
-#pragma unroll 1
-        for (int g = 0; g < kPeers; ++g)
-            store_tile<C>(a, os, area,
-                          __builtin_amdgcn_make_buffer_rsrc(pick7(a.gather, g), 0, a.slice_bytes, kRsrcFlags),
-                          srow0, rows, n0, cols);
-    }
-}
 
 // ---------------------------------------------------------------- tile loop
 
-// Per-tile state shared by the K loop and the role loop.
+// State carried from one tile to the next: whether the previous tile's
+// epilogue stores may still be in flight, and its flag, which is stored once a
+// wait has covered those stores.
 struct StepHooks {
-    bool interleave; // engine waves run the reduce engine between MFMAs
-    int eng_countdown;  // K steps to the next engine slot
     bool stores;     // the previous tile's epilogue stores are still in flight
     int pend_q;      // slot of the previous tile, whose flag is still to be stored
     int pend_flag;
     uint32_t who, epoch;
 };
 
-// Stage wait of a loader wave: B = (NS-2)*LPS younger direct loads may stay in
-// flight, plus the previous tile's C::STORES epilogue stores while they are
-// younger than the stage waited for (steps before NS-1).
+// Stage wait: B = (NS-2)*LPS younger direct loads may stay in flight, plus the
+// previous tile's C::STORES epilogue stores while they are younger than the
+// stage waited for (steps before NS-1).
 template <class C>
 __device__ __forceinline__ void wait_stage(bool stores)
 {
@@ -1321,12 +763,10 @@ __device__ __forceinline__ void wait_stage(bool stores)
 // The K loop of one tile is split in two so that the next tile's first stages
 // can be issued before the current tile's epilogue stores (see compute_waves).
 // Stage kt lives in buffer kt % NS and NS-1 stages are always in flight
-// (stages past the end load zeros), so every step of a loader wave waits for
-// the same count; the barrier then certifies that every loader's loads of stage
-// kt have landed and that every wave has finished reading stage kt-1, whose
-// buffer the step refills.  Engine waves issue no stage loads: their waits
-// cover only their own epilogue stores (before a flag is published) and their
-// engine operations (inside engine_step).
+// (stages past the end load zeros), so every step waits for the same count;
+// the barrier then certifies that every wave's loads of stage kt have landed
+// and that every wave has finished reading stage kt-1, whose buffer the step
+// refills.
 template <class C>
 struct TileJob {
     LoadPlan<C> lp;
@@ -1336,7 +776,7 @@ struct TileJob {
 };
 
 // X rows come from `xp` (xbytes long, row0 counted in it); by default from a.x.
-template <class C, bool LOADER>
+template <class C>
 __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<C>& job, int row0, int rows,
                                               int n0, int cols, const void* xp = nullptr, uint32_t xbytes = 0)
 {
@@ -1344,33 +784,21 @@ __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<
     job.nk = (K + C::BK - 1) / C::BK;
     job.xp = xp ? xp : (const void*)a.x;
     job.xbytes = xp ? xbytes : a.x_bytes;
-    if constexpr (LOADER) {
-        if (job.nk == 0) return;
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
-        make_plan<C>(a, job.lp, row0, rows, n0, cols);
+    if (job.nk == 0) return;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
+    make_plan<C>(a, job.lp, row0, rows, n0, cols);
 #pragma unroll
-        for (int s = 0; s < C::NS - 1; ++s) issue_stage<C>(job.lp, rx, rw, lds + s * C::STAGE_BYTES, s * C::BK, K);
-    }
-}
-
-// Wait until this wave's epilogue stores have completed.
-template <bool LOADER>
-__device__ __forceinline__ void wait_own_stores(const Engine& eng)
-{
-    if constexpr (LOADER)
-        wait_vmcnt<0>();
-    else
-        wait_vmcnt_upto(eng.vm - eng.vm_stores);
+    for (int s = 0; s < C::NS - 1; ++s) issue_stage<C>(job.lp, rx, rw, lds + s * C::STAGE_BYTES, s * C::BK, K);
 }
 
 // Runs the K loop of a tile whose prologue has been issued.  The previous
 // tile's epilogue stores were issued after this tile's prologue and before the
 // first refill, so they have completed once the refill issued at step 0 has:
 // at step NS-1 (or after the loop) its flag is published.
-template <class C, bool LOADER, bool ROWS = false>
+template <class C, bool ROWS = false>
 __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
-                                           StepHooks& hk, Engine& eng)
+                                           StepHooks& hk)
 {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -1384,10 +812,7 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
     for (int kt = 0; kt < nk; ++kt) {
-        if constexpr (LOADER)
-            wait_stage<C>(hk.stores && kt < C::NS - 1);
-        else if (hk.stores && kt == C::NS - 1)
-            wait_own_stores<false>(eng);
+        wait_stage<C>(hk.stores && kt < C::NS - 1);
         stage_barrier();
         if (kt == C::NS - 1) {
             hk.stores = false;
@@ -1396,23 +821,14 @@ __device__ __forceinline__ void tile_kloop(const Args& a, char* lds, TileState<C
                 hk.pend_flag = -1;
             }
         }
-        if constexpr (!LOADER) {
-            if (hk.interleave && --hk.eng_countdown == 0) {
-                hk.eng_countdown = a.engine_every;
-                engine_step(eng, a, true);
-            }
-        }
         const int nxt = kt + C::NS - 1;
-        kstep<C, LOADER>(job.lp, rx, rw, lds + (nxt % C::NS) * C::STAGE_BYTES, nxt * C::BK, K,
-                         lds + (kt % C::NS) * C::STAGE_BYTES, st);
+        kstep<C, true>(job.lp, rx, rw, lds + (nxt % C::NS) * C::STAGE_BYTES, nxt * C::BK, K,
+                       lds + (kt % C::NS) * C::STAGE_BYTES, st);
     }
-    // loaders drain the zero-filling loads past the end; every wave finishes
-    // reading LDS before the next tile's loads overwrite it; a flag still
-    // pending (nk < NS) is published here
-    if constexpr (LOADER)
-        wait_vmcnt<0>();
-    else if (hk.stores)
-        wait_own_stores<false>(eng);
+    // the zero-filling loads past the end drain; every wave finishes reading
+    // LDS before the next tile's loads overwrite it; a flag still pending
+    // (nk < NS) is published here
+    wait_vmcnt<0>();
     stage_barrier();
     hk.stores = false;
     if (hk.pend_flag >= 0) {
@@ -1448,18 +864,12 @@ __device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
 // stage waited for (stages of the prologue).  The first barrier that covers
 // those stores (the one waiting for stage NS-1, the first refill) publishes
 // the previous tile's flag.
-//
-// With STREAM every step also runs one step of the reduce stream after its
-// refill (and its sched barriers keep those instructions younger than every
-// load of the refill), so a step's wait allows as many more outstanding
-// instructions as the previous step's stream issued.
-template <class C, bool STREAM, bool ROWS = false>
+template <class C, bool ROWS = false>
 __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
-                                              StepHooks& hk, Stream& rs)
+                                              StepHooks& hk)
 {
     static_assert(C::KSUB % 2 == 0, "substep s of every step uses fragment buffer s % 2");
     static_assert(C::EW == 0, "every wave loads stages");
-    static_assert(!STREAM || C::NS == 2, "the reduce stream's wait counts assume two stages");
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -1498,14 +908,10 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
                 }
-            if constexpr (STREAM) {
-                // (the previous step's stream instructions may stay in flight)
-                stream_wait<B>(rs);
-            } else if (hk.stores && kt + 1 < C::NS - 1) {
+            if (hk.stores && kt + 1 < C::NS - 1)
                 wait_vmcnt<B + C::STORES>();
-            } else {
+            else
                 wait_vmcnt<B>();
-            }
             wait_lgkm0();
             stage_barrier();
             if (kt + 1 == C::NS - 1) publish_pending<ROWS>(a, hk);
@@ -1526,7 +932,6 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
                 if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
             __builtin_amdgcn_s_setprio(0);
-            if constexpr (STREAM) stream_step(rs, a);
         }
         // the last step
         const char* cur = lds + ((nk - 1) % C::NS) * C::STAGE_BYTES;
@@ -1541,7 +946,6 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
     // (nk < NS) is published here
     wait_vmcnt<0>();
     stage_barrier();
-    if constexpr (STREAM) stream_settle(rs);
     publish_pending<ROWS>(a, hk);
 }
 
@@ -1565,33 +969,17 @@ __device__ __forceinline__ GroupSplit group_split(int grid, int reducers, int gr
     return s;
 }
 
-// The tile loop of one wave of a compute workgroup at position `pos` of a
-// round.  Round r covers slots [r*C, r*C + C).  A tile's flag is stored once
-// the next tile's waits have covered the tile's stores: publishing costs no
-// extra wait.  Loader and engine waves run the same loop (the same barriers);
-// engine waves also run the reduce engine.
-template <class C, bool FUSED, bool LOADER, bool STREAM, bool EPI = false, int VAR = 0>
+// The tile loop of a compute workgroup at position `pos` of a round.  Round r
+// covers slots [r*C, r*C + C).  A tile's flag is stored once the next tile's
+// waits have covered the tile's stores: publishing costs no extra wait.  With
+// `sum_tail` every wave then sums a share of the slice.
+template <class C, bool FUSED, int VAR = 0>
 __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos, uint32_t who, uint32_t epoch,
-                                              bool interleave)
+                                              bool sum_tail)
 {
-    static_assert(!EPI || (FUSED && C::WAVES == 4 && C::EW == 0), "the epilogue sum: four-wave fused tiles");
+    static_assert(C::EW == 0, "every wave loads stages");
     const int Ctot = a.num_compute;
-    const int wave = uni((int)(threadIdx.x >> 6));
-    Engine eng;
-    Stream rs;
-    if constexpr (STREAM) {
-        constexpr int SW = C::WAVES / kStreamOps;  // streaming waves
-        stream_init(rs, a, lds + C::LDS_BYTES + (wave % SW) * kStreamLds, pos * SW, pos * SW + wave % SW,
-                    Ctot * SW, wave < SW, epoch);
-    }
-    if constexpr (!LOADER) {
-        const int ew = wave - C::LW;
-        engine_init(eng, a, lds + C::LDS_BYTES + ew * kEngAreas * kEngAreaBytes, pos * C::EW + ew, Ctot * C::EW,
-                    epoch);
-    }
     StepHooks hk;
-    hk.interleave = interleave && C::EW > 0 && a.engine_every > 0;
-    hk.eng_countdown = 1;
     hk.stores = false;
     hk.pend_q = -1;
     hk.pend_flag = -1;
@@ -1599,30 +987,24 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     hk.epoch = epoch;
     TileState<C> st;
     TileJob<C> job;
-    PeerFrag<C> pf;
     int q = pos;
     TileCoord t;
     if (q < a.g.tiles) {
         t = decode_slot(a.g, q);
-        // (the peer values load ahead of the first stage, which waits for them)
-        if constexpr (EPI)
-            if (t.d == a.g.rank)
-                epi_load_peers<C>(a, pf, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
-        tile_prologue<C, LOADER>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN,
-                                 tile_cols(a.g, t));
+        tile_prologue<C>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
     }
     while (q < a.g.tiles) {
         if constexpr (C::XP)
-            tile_kloop_xp<C, STREAM, (VAR & kVarRows) != 0>(a, lds, st, job, hk, rs);
+            tile_kloop_xp<C, (VAR & kVarRows) != 0>(a, lds, st, job, hk);
         else
-            tile_kloop<C, LOADER, (VAR & kVarRows) != 0>(a, lds, st, job, hk, eng);
+            tile_kloop<C, (VAR & kVarRows) != 0>(a, lds, st, job, hk);
         // issue the next tile's first stages before this tile's stores
         const int qn = q + Ctot;
         TileCoord tn = t;
         if (qn < a.g.tiles) {
             tn = decode_slot(a.g, qn);
-            tile_prologue<C, LOADER>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
-                                     tile_cols(a.g, tn));
+            tile_prologue<C>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
+                             tile_cols(a.g, tn));
         }
         // the stage buffer the next tile's prologue left free holds the
         // epilogue staging areas
@@ -1630,23 +1012,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         store_tile<C, (VAR & kVarNt) ? kStoreDeviceNt : kStoreDevice>(
             a, st, lds + (C::NS - 1) * C::STAGE_BYTES, rd, t.tml * C::BM, tile_rows(a.g, t), t.tn * C::BN,
             tile_cols(a.g, t));
-        if constexpr (EPI) {
-            if (t.d == a.g.rank) {
-                TileState<C> os;
-                epi_sum<C>(pf, st, os);
-                epi_store<C>(a, os, lds + (C::NS - 1) * C::STAGE_BYTES, t.tml * C::BM, tile_rows(a.g, t),
-                             t.tn * C::BN, tile_cols(a.g, t));
-            }
-            // a later own tile's peer values load behind these stores (its
-            // stage waits then cover them)
-            if (qn < a.g.tiles && tn.d == a.g.rank)
-                epi_load_peers<C>(a, pf, tn.tml * C::BM, tile_rows(a.g, tn), tn.tn * C::BN, tile_cols(a.g, tn));
-        }
         hk.stores = true;
-        if constexpr (!LOADER) {
-            eng.vm += C::STORES;
-            eng.vm_stores = eng.vm;
-        }
         if (FUSED) {
             hk.pend_q = q;
             hk.pend_flag = t.flag;
@@ -1655,89 +1021,83 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         t = tn;
     }
     if (hk.pend_flag >= 0) {
-        wait_own_stores<LOADER>(eng);
+        wait_vmcnt<0>();
         stage_barrier();
         if (threadIdx.x == 0) publish<(VAR & kVarRows) != 0>(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
-    if constexpr (EPI) {
-        // every own tile was summed by its producer
-    } else if constexpr (STREAM) {
-        // the items the stream has not finished
-        __shared__ int s_progress[C::WAVES / kStreamOps];
-        stream_drain<C::WAVES>(rs, a, wave, s_progress);
-    } else if (interleave) {
-        if (hk.interleave) {
-            // in-loop slots: the engine waves own the items
-            if constexpr (!LOADER) engine_drain(eng, a);
-        } else {
-            // every wave sums a share of the slice after its last tile
-            const int wave = uni((int)(threadIdx.x >> 6));
-            // (sixteen items in flight per CU for the eight-wave and one-per-CU
-            // tiles; one per wave for four-wave tiles at two per CU, whose
-            // shapes leave about one item per wave: a second, empty slot of a
-            // batch still issues its eight loads and lengthens the wait)
-            drain_items<(C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64) ? 1 : 16 / C::WAVES, 2,
-                        (VAR & kVarRows) != 0>(a, item_map(a), pos * C::WAVES + wave, a.num_compute * C::WAVES,
-                                               epoch);
-        }
+    if (sum_tail) {
+        // every wave sums a share of the slice after its last tile (sixteen
+        // items in flight per CU for the eight-wave and one-per-CU tiles; one
+        // per wave for four-wave tiles at two per CU, whose shapes leave about
+        // one item per wave: a second, empty slot of a batch still issues its
+        // eight loads and lengthens the wait)
+        const int wave = uni((int)(threadIdx.x >> 6));
+        drain_items<(C::WAVES == 4 && C::LDS_BYTES <= 80 * 1024 - 64) ? 1 : 16 / C::WAVES, 2,
+                    (VAR & kVarRows) != 0>(a, item_map(a), pos * C::WAVES + wave, a.num_compute * C::WAVES, epoch);
     }
 }
 
 // Compute role of the l-th compute workgroup of group grp: its position in a
 // round is either the group's block offset + l (contiguous split) or
-// l * 8 + grp (strided, used when all C_x are equal).
-template <class C, bool FUSED, bool STREAM, bool EPI = false, int VAR = 0>
+// l * 8 + grp (strided, used when all C_x are equal).  Without dedicated
+// reducers the compute workgroups sum the slice after their last tile.
+template <class C, bool FUSED, int VAR = 0>
 __device__ __forceinline__ void compute_role(const Args& a, char* lds, int grp, int l, uint32_t epoch, int base)
 {
     const int pos = uni(a.strided ? (l * kGroups + grp) : (base + l));
     const uint32_t who = ((uint32_t)grp << 16) | (uint32_t)l;
-    // without dedicated reducers the compute workgroups reduce the slice
-    const bool interleave = FUSED && a.num_reducers == 0;
-    const int wave = uni((int)(threadIdx.x >> 6));
-    if (C::EW == 0 || wave < C::LW)
-        compute_waves<C, FUSED, true, STREAM, EPI, VAR>(a, lds, pos, who, epoch, interleave);
-    else if constexpr (C::EW > 0)
-        compute_waves<C, FUSED, false, false, false, VAR>(a, lds, pos, who, epoch, interleave);
+    compute_waves<C, FUSED, VAR>(a, lds, pos, who, epoch, FUSED && a.num_reducers == 0);
 }
 
 // Dedicated reducer role (used when reducers are requested): claim own-slice
-// tiles in schedule order, wait for each tile's flag (thread 0 polls with
-// device-scope loads and short sleeps, bounded by the watchdog), then sum the
-// tile, reading the local slice at device scope.
+// tiles in schedule order from this run's claim counter, wait for each tile's
+// flag (thread 0 polls with device-scope loads and short sleeps, bounded by the
+// watchdog), then sum the tile, reading the local slice at device scope.  The
+// first wait that exceeds the watchdog reports the tile and latches: later
+// unreleased tiles are skipped without waiting, so one reducer never waits
+// longer than one watchdog period in total.
 template <bool ROWS>
 __device__ void reducer_role(const Args& a, uint32_t epoch)
 {
     __shared__ int s_unit;
-    __shared__ int s_abort;
+    __shared__ int s_skip;
+    uint32_t* unit = &a.state->unit[epoch & 1u];
+    bool gave_up = false;  // (thread 0's)
     for (;;) {
         if (threadIdx.x == 0) {
-            const int u = (int)atomicAdd(&a.state->unit, 1u);
-            int abort_now = 0;
+            const int u = (int)atomicAdd(unit, 1u);
+            int skip = 0;
             if (u < a.g.ts) {
                 const TileCoord t = decode_slot(a.g, u);
                 const uint32_t* f = ready_word<ROWS>(a, t.flag);
                 if (!released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
-                    const uint64_t t0 = wall_clock64();
-                    while (!released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch)) {
-                        __builtin_amdgcn_s_sleep(2);
-                        if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
-                            abort_now = 1;
-                            break;
+                    if (gave_up) {
+                        skip = 1;
+                    } else {
+                        const uint64_t t0 = wall_clock64();
+                        while (!released<ROWS>(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                               epoch)) {
+                            __builtin_amdgcn_s_sleep(2);
+                            if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
+                                skip = 1;
+                                gave_up = true;
+                                if (atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
+                                    atomicExch(&a.state->status[1], t.flag);
+                                break;
+                            }
                         }
                     }
                 }
-                if (abort_now && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
-                    atomicExch(&a.state->status[1], t.flag);
             }
             s_unit = u;
-            s_abort = abort_now;
+            s_skip = skip;
         }
         __syncthreads();
         const int u = s_unit;
-        const int abort_now = s_abort;
-        __syncthreads();  // s_unit / s_abort are rewritten by the next claim
+        const int skip = s_skip;
+        __syncthreads();  // s_unit / s_skip are rewritten by the next claim
         if (u >= a.g.ts) return;
-        if (abort_now) continue;
+        if (skip) continue;
         const TileCoord t = decode_slot(a.g, u);
         const int rows = tile_rows(a.g, t), cols = tile_cols(a.g, t);
         const int cpr = cols >> 3;
@@ -1767,20 +1127,19 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
     }
 }
 
-// Role dispatch and end-of-launch bookkeeping, with no device atomics on the
-// default path.  Without dedicated reducers every workgroup computes and its
-// position follows from its index.  With reducers, per-group arrival tickets
-// hand out the roles (a reducer exists only once its group's compute
-// workgroups are all resident), and workgroup 0 resets the tickets once every
-// workgroup has finished.
+// Role dispatch, with no device atomics on the default path.  Without
+// dedicated reducers every workgroup computes and its position follows from
+// its index.  With reducers, per-group arrival tickets hand out the roles (a
+// reducer exists only once its group's compute workgroups are all resident).
 //
 // The run epoch: each workgroup keeps, in its own word of `finished`, the
 // epoch of the last fused launch it finished.  A launch reads that word at
 // the start and uses the next value; every workgroup of the previous fused
 // launch stored the same value, so all workgroups of a launch agree on its
-// epoch without communicating (the words change only at kernel ends).  A
-// GEMM-only launch has no flags and touches none of this.
-template <class C, bool FUSED, bool STREAM = false, bool EPI = false, int VAR = 0>
+// epoch without communicating (the words change only at kernel ends).  The
+// tickets and the claim counter of the next run are cleared by workgroup 0 of
+// this one.  A GEMM-only launch has no flags and touches none of this.
+template <class C, bool FUSED, int VAR = 0>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1791,18 +1150,26 @@ __device__ __forceinline__ void fused_body(const Args& a)
     // reducers), so they need no tickets
     const bool tickets = FUSED && a.num_reducers > 0 && !a.coresident;
     if (threadIdx.x == 0) {
-        s_ticket = tickets ? atomicAdd(&a.state->role[grp], 1u) : (uint32_t)(blockIdx.x / kGroups);
-        s_epoch = FUSED ? __hip_atomic_load(a.finished + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : 0u;
+        const uint32_t e = FUSED ? __hip_atomic_load(a.finished + blockIdx.x, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) + 1u
+                                 : 0u;
+        s_epoch = e;
+        s_ticket = tickets ? atomicAdd(&a.state->role[e & 1u][grp], 1u) : (uint32_t)(blockIdx.x / kGroups);
+        if (tickets && blockIdx.x == 0) {
+            const uint32_t nx = (e + 1u) & 1u;
+            for (int i = 0; i < kGroups; ++i)
+                __hip_atomic_store(&a.state->role[nx][i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.state->unit[nx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     // (read through readfirstlane so that the compiler sees them uniform: the
-    // tile loop and the reduce stream then stay in scalar registers)
+    // tile loop then stays in scalar registers)
     const uint32_t ticket = (uint32_t)uni((int)s_ticket);
-    const uint32_t epoch = (uint32_t)uni((int)s_epoch) + 1u;  // value this run's flags carry
+    const uint32_t epoch = (uint32_t)uni((int)s_epoch);  // value this run's flags carry
     const GroupSplit split = group_split((int)gridDim.x, uni(a.num_reducers), grp);
     if (ticket < (uint32_t)split.compute)
-        compute_role<C, FUSED, STREAM, EPI, VAR>(a, lds, grp, (int)ticket, epoch, split.base);
+        compute_role<C, FUSED, VAR>(a, lds, grp, (int)ticket, epoch, split.base);
     else if (FUSED && ticket - (uint32_t)split.compute < (uint32_t)split.reducers) {
         if (a.coresident) {
             // reducer r of R owns items r*W + wave, + R*W, ...: its peer chunks
@@ -1821,37 +1188,22 @@ __device__ __forceinline__ void fused_body(const Args& a)
         __syncthreads();
         if (threadIdx.x == 0)
             __hip_atomic_store(a.finished + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (tickets && blockIdx.x == 0) {
-            // every finish mark arrives (each workgroup's own waits are
-            // bounded by the watchdog; this one is bounded too)
-            const uint64_t t0 = wall_clock64();
-            for (int i = threadIdx.x; i < (int)gridDim.x; i += blockDim.x)
-                while (__hip_atomic_load(a.finished + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch &&
-                       (int64_t)(wall_clock64() - t0) <= 2 * a.watchdog_ticks)
-                    __builtin_amdgcn_s_sleep(2);
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                for (int i = 0; i < kGroups; ++i)
-                    __hip_atomic_store(&a.state->role[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.state->unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
     }
 }
 
 // Tiles that fit two workgroups per CU keep two waves per SIMD resident.
-template <class C, bool FUSED, bool EPI = false, int VAR = 0>
+template <class C, bool FUSED, int VAR = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel(Args a)
 {
-    fused_body<C, FUSED, false, EPI, VAR>(a);
+    fused_body<C, FUSED, VAR>(a);
 }
 
 // Eight-wave workgroups (one per CU): two waves per SIMD, so one wave's
-// MFMAs run while its sibling waits on LDS, a barrier or the reduce engine.
-template <class C, bool FUSED, bool STREAM = false, int VAR = 0>
+// MFMAs run while its sibling waits on LDS or a barrier.
+template <class C, bool FUSED, int VAR = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_kernel_8w(Args a)
 {
-    fused_body<C, FUSED, STREAM, false, VAR>(a);
+    fused_body<C, FUSED, VAR>(a);
 }
 
 // Large tiles run one workgroup (one wave per SIMD) per CU: let the compiler
@@ -1859,7 +1211,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <class C, bool FUSED, int VAR = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_kernel_1w(Args a)
 {
-    fused_body<C, FUSED, false, false, VAR>(a);
+    fused_body<C, FUSED, VAR>(a);
 }
 
 // Standalone slice sum: every workgroup reduces, no flags, grid-stride over the
@@ -1889,8 +1241,12 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(Args a)
 // gathered buffer left in an XCD's L2 by an earlier run would be stale, so
 // every workgroup invalidates its caches once at its start (agent-scope
 // acquire), before anything of this run is cached; later lines of the buffer
-// can only come from reads made after their rows were copied.  Output tiles
-// go to y [M][N]; there is no reduction.
+// can only come from reads made after their rows were copied.  That holds per
+// 128-byte line only if no line spans two tile-row blocks (a line cached when
+// the first block is read could miss the second block's copy), so the host
+// requires x_gathered to be 128-byte aligned and every slice, S * K * 2 bytes,
+// a whole number of lines (a block of BM >= 16 rows of K % 8 == 0 elements
+// always is).  Output tiles go to y [M][N]; there is no reduction.
 
 // Copies units first, first + stride, ... (all threads of the workgroup).
 template <class C>
@@ -1958,18 +1314,22 @@ __device__ __forceinline__ bool ag_wait(const Args& a, int blk, uint32_t target)
 
 // Issues the first stages of tile t: X rows from the local slice (own tile)
 // or from the gathered buffer once the block has arrived (FUSED) or because
-// the buffer is already complete (GEMM only).
+// the buffer is already complete (GEMM only).  If the block's counter never
+// arrives (the wait timed out and the status word says so), the tile reads
+// its X rows as zeros rather than rows that may be only partly copied.
 template <class C, bool FUSED>
 __device__ __forceinline__ void ag_prologue(const Args& a, char* lds, TileJob<C>& job, const TileCoord& t,
                                             uint32_t target)
 {
     const int rows = tile_rows(a.g, t), cols = tile_cols(a.g, t);
     if (t.d == a.g.rank) {
-        tile_prologue<C, true>(a, lds, job, t.tml * C::BM, rows, t.tn * C::BN, cols, a.xsrc[a.g.rank], a.xs_bytes);
+        tile_prologue<C>(a, lds, job, t.tml * C::BM, rows, t.tn * C::BN, cols, a.xsrc[a.g.rank], a.xs_bytes);
         return;
     }
-    if constexpr (FUSED) ag_wait(a, t.d * a.g.tms + t.tml, target);
-    tile_prologue<C, true>(a, lds, job, t.d * a.g.S + t.tml * C::BM, rows, t.tn * C::BN, cols, a.xg, a.x_bytes);
+    bool arrived = true;
+    if constexpr (FUSED) arrived = ag_wait(a, t.d * a.g.tms + t.tml, target);
+    tile_prologue<C>(a, lds, job, t.d * a.g.S + t.tml * C::BM, rows, t.tn * C::BN, cols, a.xg,
+                     arrived ? a.x_bytes : 0u);
 }
 
 template <class C, bool FUSED>
@@ -1996,15 +1356,11 @@ __device__ __forceinline__ void ag_body(const Args& a)
     const uint32_t target = run * (uint32_t)a.ag_units;
 
     StepHooks hk;
-    hk.interleave = false;
-    hk.eng_countdown = 1;
     hk.stores = false;
     hk.pend_q = -1;
     hk.pend_flag = -1;
     hk.who = 0;
     hk.epoch = run;
-    Engine eng;
-    Stream rs;
     TileState<C> st;
     TileJob<C> job;
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void*)a.y, 0, a.y_bytes, kRsrcFlags);
@@ -2016,9 +1372,9 @@ __device__ __forceinline__ void ag_body(const Args& a)
     }
     while (q < a.g.tiles) {
         if constexpr (C::XP)
-            tile_kloop_xp<C, false>(a, lds, st, job, hk, rs);
+            tile_kloop_xp<C>(a, lds, st, job, hk);
         else
-            tile_kloop<C, true>(a, lds, st, job, hk, eng);
+            tile_kloop<C>(a, lds, st, job, hk);
         const int qn = q + G;
         TileCoord tn = t;
         if (qn < a.g.tiles) {

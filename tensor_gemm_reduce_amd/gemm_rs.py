@@ -40,10 +40,8 @@ TILES = {"auto": 0, "16x64": 1, "64x128": 2, "128x128": 3, "128x256": 4, "256x12
 
 REDUCE_AUTO = 0
 REDUCE_TAIL = 1
-REDUCE_STREAM = 2
-REDUCE_CORESIDENT = 3
-REDUCE_EPILOGUE = 4
-REDUCE_MODES = {"auto": 0, "tail": 1, "stream": 2, "coresident": 3, "epilogue": 4}
+REDUCE_CORESIDENT = 2
+REDUCE_MODES = {"auto": 0, "tail": 1, "coresident": 2}
 
 STORES_DEVICE = 0
 STORES_NONTEMPORAL = 1
@@ -64,7 +62,7 @@ class gemm_rs_config(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K_local", ctypes.c_int32),
                 ("tp", ctypes.c_int32), ("rank", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("num_reducers", ctypes.c_int32),
-                ("engine_interval", ctypes.c_int32), ("debug_flags", ctypes.c_int32),
+                ("debug_flags", ctypes.c_int32),
                 ("drop_flag", ctypes.c_int32), ("flag_stride", ctypes.c_int32),
                 ("watchdog_us", ctypes.c_int64), ("reduce_mode", ctypes.c_int32),
                 ("tile_stores", ctypes.c_int32), ("flag_protocol", ctypes.c_int32)]
@@ -140,7 +138,7 @@ def _check(code: int, what: str) -> int:
 
 
 def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_reducers=-1,
-                engine_interval=0, debug_flags=0, drop_flag=-1, flag_stride=1,
+                debug_flags=0, drop_flag=-1, flag_stride=1,
                 watchdog_us=0, reduce_mode=REDUCE_AUTO, tile_stores=STORES_DEVICE,
                 flag_protocol=FLAGS_TILE) -> gemm_rs_config:
     if isinstance(tile, str):
@@ -151,7 +149,7 @@ def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_redu
         tile_stores = TILE_STORES[tile_stores]
     if isinstance(flag_protocol, str):
         flag_protocol = FLAG_PROTOCOLS[flag_protocol]
-    return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers, engine_interval,
+    return gemm_rs_config(M, N, K_local, tp, rank, tile, group_m, num_reducers,
                           debug_flags, drop_flag, flag_stride, watchdog_us, reduce_mode, tile_stores,
                           flag_protocol)
 

@@ -68,15 +68,12 @@ def cfg(**kw):
     (dict(rank=-1), gr.ERR_INVALID_ARG),
     (dict(M=-8), gr.ERR_INVALID_ARG),
     (dict(tile=7), gr.ERR_INVALID_ARG),
-    (dict(engine_interval=-1), gr.ERR_INVALID_ARG),
-    (dict(engine_interval=4097), gr.ERR_INVALID_ARG),
     (dict(flag_stride=2), gr.ERR_INVALID_ARG),
     (dict(debug_flags=4), gr.ERR_INVALID_ARG),
     (dict(drop_flag=100000), gr.ERR_INVALID_ARG),
     (dict(num_reducers=-3), gr.ERR_INVALID_ARG),
     (dict(num_reducers=-2), gr.OK),
-    (dict(num_reducers=-2, engine_interval=2), gr.ERR_INVALID_ARG),
-    (dict(num_reducers=-2, reduce_mode="stream"), gr.ERR_INVALID_ARG),
+    (dict(num_reducers=-2, reduce_mode="coresident"), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt"), gr.OK),
     (dict(tile_stores="nt", num_reducers=8), gr.OK),
     (dict(tile_stores=2), gr.ERR_INVALID_ARG),
@@ -84,31 +81,15 @@ def cfg(**kw):
     (dict(flag_protocol="row_counter"), gr.OK),
     (dict(flag_protocol="row_counter", num_reducers=8), gr.OK),
     (dict(flag_protocol="row_counter", num_reducers=-2), gr.OK),
-    (dict(flag_protocol="row_counter", engine_interval=1), gr.ERR_INVALID_ARG),
-    (dict(flag_protocol="row_counter", reduce_mode="stream"), gr.ERR_INVALID_ARG),
     (dict(flag_protocol=2), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt", flag_protocol="row_counter"), gr.ERR_INVALID_ARG),
-    (dict(tile_stores="nt", engine_interval=2), gr.ERR_INVALID_ARG),
-    (dict(tile_stores="nt", reduce_mode="stream"), gr.ERR_INVALID_ARG),
-    (dict(tile_stores="nt", tile="64x128", reduce_mode="epilogue"), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt", reduce_mode="coresident"), gr.OK),
-    (dict(flag_protocol="row_counter", tile="64x128", reduce_mode="epilogue"), gr.ERR_INVALID_ARG),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.OK),
-    (dict(reduce_mode="epilogue"), gr.ERR_UNSUPPORTED_SHAPE),            # 256x256 tile
-    (dict(reduce_mode="epilogue", tile="128x128"), gr.ERR_UNSUPPORTED_SHAPE),
-    (dict(reduce_mode="epilogue", M=512, K_local=1024, num_reducers=8), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=3), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="coresident"), gr.OK),
     (dict(reduce_mode="coresident", num_reducers=8), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode="coresident", engine_interval=1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=-1), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode="stream"), gr.OK),
     (dict(reduce_mode="tail"), gr.OK),
-    (dict(reduce_mode="stream", num_reducers=8), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode="stream", engine_interval=2), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode="stream", tile="128x128"), gr.ERR_UNSUPPORTED_SHAPE),
-    (dict(reduce_mode="stream", M=512, K_local=1024), gr.ERR_UNSUPPORTED_SHAPE),
     (dict(M=0), gr.OK),
     (dict(K_local=0), gr.OK),
 ])
@@ -162,13 +143,9 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
 
 @pytest.mark.parametrize("kw,mode", [
     (dict(), gr.REDUCE_TAIL),                        # automatic: the sum after the last tile
-    (dict(reduce_mode="stream"), gr.REDUCE_STREAM),  # 256x256 tile
     (dict(reduce_mode="tail"), gr.REDUCE_TAIL),
     (dict(reduce_mode="coresident"), gr.REDUCE_CORESIDENT),
-    (dict(reduce_mode="epilogue", M=512, K_local=1024), gr.REDUCE_EPILOGUE),
     (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
-    (dict(engine_interval=2), gr.REDUCE_TAIL),
-    (dict(tile="128x128"), gr.REDUCE_TAIL),           # no stream for this tile
     (dict(M=512, K_local=1024), gr.REDUCE_TAIL),     # o_proj: 64x128 tile
 ])
 def test_plan_resolves_reduce_mode(kw, mode):

@@ -175,4 +175,22 @@ def test_ag_argument_checks():
                                     b.y.data_ptr(), None) == gr.ERR_MISALIGNED
     assert gr.gemm_rs_run_allgather(op.h, 7, vp, b.w.data_ptr(), b.xg.data_ptr(),
                                     b.y.data_ptr(), None) == gr.ERR_INVALID_ARG
+    # the fused launch needs x_gathered on a 128-byte line boundary (16 is not
+    # enough), the separate copy and GEMM launches do not
+    big = torch.zeros(b.xg.numel() + 128, dtype=torch.int16, device="cuda")
+    base = (-big.data_ptr()) % 128 // 2
+    xg16 = big[base + 8: base + 8 + b.xg.numel()]
+    assert xg16.data_ptr() % 128 == 16
+    assert gr.gemm_rs_run_allgather(op.h, gr.MODE_FUSED, vp, b.w.data_ptr(), xg16.data_ptr(),
+                                    b.y.data_ptr(), None) == gr.ERR_MISALIGNED
+    assert gr.gemm_rs_run_allgather(op.h, gr.MODE_SEQUENTIAL, vp, b.w.data_ptr(), xg16.data_ptr(),
+                                    b.y.data_ptr(), None) == gr.OK
+    # and every slice a whole number of lines: S * K * 2 = 3 * 8 * 2 bytes is not
+    odd = gr.GemmRS(24, 64, 8, rank=0)
+    zs = [torch.zeros((3, 8), dtype=torch.int16, device="cuda") for _ in range(8)]
+    zg = torch.zeros((24, 8), dtype=torch.int16, device="cuda")
+    zw = torch.zeros((64, 8), dtype=torch.int16, device="cuda")
+    zy = torch.zeros((24, 64), dtype=torch.int16, device="cuda")
+    assert gr.gemm_rs_run_allgather(odd.h, gr.MODE_FUSED, [t.data_ptr() for t in zs], zw.data_ptr(),
+                                    zg.data_ptr(), zy.data_ptr(), None) == gr.ERR_UNSUPPORTED_SHAPE
     torch.cuda.synchronize()

@@ -13,7 +13,7 @@ from gpu_util import SENTINEL, Buffers, filled, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
-PLACEMENTS = {"tail": dict(num_reducers=0), "engine_loop1": dict(num_reducers=0, engine_interval=1),
+PLACEMENTS = {"tail": dict(num_reducers=0), "coresident": dict(reduce_mode="coresident"),
               "reducers8": dict(num_reducers=8)}
 
 

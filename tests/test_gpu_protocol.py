@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
     ("mixtral_down", 2048, dict(tile="128x128", group_m=3)),
     ("down_proj", None, dict(flag_stride=32)),
     ("down_proj", None, dict(num_reducers=8)),
-    ("mixtral_down", 2048, dict(engine_interval=2)),
+    ("mixtral_down", 2048, dict(num_reducers=16, flag_stride=32)),
 ])
 def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
     cfg = synthetic.CONFIGS[name]
@@ -58,8 +58,7 @@ def test_slot_log_and_flags_match_oracle_schedule(name, M, kw):
             assert np.all(s[1:] >= s[:-1]), c
 
 
-@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=0, engine_interval=1),
-                                 dict(num_reducers=8)], ids=["engine_tail", "engine_loop1", "reducers8"])
+@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=8)], ids=["tail", "reducers8"])
 def test_watchdog_reports_a_dropped_flag_and_kernel_exits(red):
     cfg = synthetic.CONFIGS["tiny"]
     rank = 2
@@ -88,6 +87,33 @@ def test_watchdog_reports_a_dropped_flag_and_kernel_exits(red):
     assert np.array_equal(host(b.out), out_o)
 
 
+def test_reducer_timeout_leaves_the_next_run_whole():
+    """One dedicated reducer claims every own tile in turn; the first tile's
+    release is dropped, so its wait gives up after the (short) watchdog while
+    the rest of the slice takes far longer to sum.  Both runs on the handle
+    report the timeout and must sum every other tile: the claim counter of a
+    run is never reset while that run may still claim from it."""
+    cfg = synthetic.Config("reducer_timeout", 22, 4096, 6144, 256)
+    rank = 1
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    plan = gr.gemm_rs_plan(gr.make_config(cfg.M, cfg.N, cfg.K_local, rank=rank))
+    sched = oracle.schedule(cfg.M, cfg.N, 8, rank, plan.bm, plan.bn, plan.group_m)
+    dropped = int(sched["flag"][0])  # first own tile: rows [0, bm), columns [0, bn)
+    op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, num_reducers=1, drop_flag=dropped, watchdog_us=100)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    _, local_o, out_o = oracle.gemm_rs(x, w, peers, tp=8, rank=rank)
+    mask = np.ones((cfg.S, cfg.N), bool)
+    mask[:plan.bm, :plan.bn] = False
+    for it in range(2):
+        b.refill()
+        run(op, b, check_status=False)
+        assert op.status() == gr.ERR_TIMEOUT, it
+        assert np.array_equal(host(b.local), local_o), it
+        got = host(b.out)
+        assert np.all(got[:plan.bm, :plan.bn] == SENTINEL), it
+        assert np.array_equal(got[mask], out_o[mask]), it
+
+
 def test_alternating_inputs_never_read_stale_tiles():
     """Back-to-back fused runs alternate two input sets on shared output
     buffers, with the local slice poisoned before each run: a reducer that read
@@ -101,8 +127,7 @@ def test_alternating_inputs_never_read_stale_tiles():
     bufs = [Buffers(x, w, p, base.S, base.N) for x, w, p in ins]
     shared_send, shared_local, shared_out = bufs[0].send, bufs[0].local, bufs[0].out
     for kw in (dict(num_reducers=0), dict(num_reducers=0, tile="128x128"), dict(num_reducers=8),
-               dict(num_reducers=1), dict(num_reducers=0, engine_interval=1),
-               dict(num_reducers=0, engine_interval=2, tile="128x128"), dict(tile_stores="nt"),
+               dict(num_reducers=1), dict(num_reducers=3, tile="128x128"), dict(tile_stores="nt"),
                dict(num_reducers=8, tile_stores="nt"), dict(flag_protocol="row_counter"),
                dict(num_reducers=8, flag_protocol="row_counter")):
         op = gr.GemmRS(base.M, base.N, base.K_local, rank=rank, **kw)
@@ -119,8 +144,7 @@ def test_alternating_inputs_never_read_stale_tiles():
         assert bad == 0, (kw, bad)
 
 
-@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=0, engine_interval=2),
-                                 dict(num_reducers=8)], ids=["engine_tail", "engine_loop2", "reducers8"])
+@pytest.mark.parametrize("red", [dict(num_reducers=0), dict(num_reducers=8)], ids=["tail", "reducers8"])
 def test_graph_replays_match_eager(red):
     """Runs captured into a HIP graph and replayed are new runs each time (the
     epoch and counters live on the device): every replay, with eager runs and
