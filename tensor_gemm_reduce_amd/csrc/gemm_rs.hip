@@ -396,6 +396,71 @@ static void free_state(gemm_rs_handle* h)
     if (h->agfinished) (void)hipFree(h->agfinished);
 }
 
+// The tile and kernel variant a (valid) config runs: the store policy or the
+// flag protocol selects a separate instantiation.
+static TileDesc variant_desc(const gemm_rs_config& c, int* variant)
+{
+    TileDesc td = tile_desc(resolve_tile(c));
+    *variant = 0;
+    if (c.tile_stores == GEMM_RS_STORES_NONTEMPORAL) {
+        td.kernel = td.kernel_nt;
+        td.gemm_kernel = td.gemm_kernel_nt;
+        *variant = 1;
+    } else if (c.flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER) {
+        td.kernel = td.kernel_rows;
+        *variant = 2;
+    }
+    return td;
+}
+
+// Gives the fused and GEMM-only kernels of td their dynamic LDS size and
+// returns in *occ how many fused workgroups fit on one CU.
+static int kernel_setup(const TileDesc& td, int* occ)
+{
+    HIP_TRY(hipFuncSetAttribute(td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.lds_bytes));
+    HIP_TRY(hipFuncSetAttribute(td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.lds_bytes));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, td.kernel, td.threads, td.lds_bytes));
+    return GEMM_RS_OK;
+}
+
+// Fills the launch plan of a handle for a valid config on device dev (no
+// allocation, no device call): tile, kernels, persistent grid, reducer split.
+// occ: fused workgroups per CU (kernel_setup).
+static int plan_launch(gemm_rs_handle* h, const gemm_rs_config* c, int dev, int num_cus, int occ)
+{
+    int variant = 0;
+    h->cfg = *c;
+    h->g = geometry_of(*c);
+    h->tile_id = resolve_tile(*c);
+    h->td = variant_desc(*c, &variant);
+    h->device = dev;
+    h->num_cus = num_cus;
+    h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
+    // automatic: no dedicated reducers, the compute workgroups sum the slice
+    const int red_req = c->num_reducers < 0 ? 0 : c->num_reducers;
+    h->reduce_mode = resolve_reduce_mode(*c);
+    h->fused_lds = h->td.lds_bytes;
+    // the persistent grid holds the workgroups per CU the kernel was built for
+    // (more would share a SIMD's registers between more waves than planned)
+    h->wgs_per_cu = occ < 1 ? 1 : (occ > h->td.wgs_per_cu ? h->td.wgs_per_cu : occ);
+    // a whole number of workgroups per XCD group
+    h->grid = (h->num_cus * h->wgs_per_cu) / kGroups * kGroups;
+    if (h->grid < kGroups) h->grid = kGroups;
+    h->gemm_grid = h->grid;
+    int red = red_req;
+    if (h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT) {
+        // one more workgroup per CU, which must fit beside the compute ones
+        if (occ < h->wgs_per_cu + 1) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
+        red = h->num_cus / kGroups * kGroups;
+        h->grid += red;
+        h->wgs_per_cu += 1;
+    }
+    if (red >= h->grid) red = h->grid - 1;
+    h->reduce_grid = h->num_cus * 8;
+    set_split(h, red);
+    return GEMM_RS_OK;
+}
+
 int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
 {
     if (!out) return GEMM_RS_ERR_INVALID_ARG;
@@ -409,53 +474,14 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     HIP_TRY(hipGetDeviceProperties(&prop, dev));
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_RS_ERR_NO_DEVICE;
 
+    int variant = 0, occ = 0;
+    rc = kernel_setup(variant_desc(*c, &variant), &occ);
+    if (rc != GEMM_RS_OK) return rc;
     gemm_rs_handle* h = new (std::nothrow) gemm_rs_handle();
     if (!h) return GEMM_RS_ERR_NO_MEMORY;
-    h->cfg = *c;
-    h->g = geometry_of(*c);
-    h->tile_id = resolve_tile(*c);
-    h->td = tile_desc(h->tile_id);
-    // the kernel variant of the requested store policy or flag protocol
-    if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL) {
-        h->td.kernel = h->td.kernel_nt;
-        h->td.gemm_kernel = h->td.gemm_kernel_nt;
-    } else if (c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER) {
-        h->td.kernel = h->td.kernel_rows;
-    }
-    h->device = dev;
-    h->num_cus = prop.multiProcessorCount;
-    h->flag_stride = c->flag_stride == 0 ? 1 : c->flag_stride;
-
-    // automatic: no dedicated reducers, the compute workgroups sum the slice
-    const int red_req = c->num_reducers < 0 ? 0 : c->num_reducers;
-    hipError_t e = hipFuncSetAttribute(h->td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute(h->td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
-    if (e != hipSuccess) { delete h; return hip_fail(e, "hipFuncSetAttribute"); }
-    h->reduce_mode = resolve_reduce_mode(*c);
-    int occ = 0;
-    const void* fk = h->td.kernel;
-    h->fused_lds = h->td.lds_bytes;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, h->td.threads, h->fused_lds);
-    if (e != hipSuccess) { delete h; return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor"); }
-    // the persistent grid holds the workgroups per CU the kernel was built for
-    // (more would share a SIMD's registers between more waves than planned)
-    h->wgs_per_cu = occ < 1 ? 1 : (occ > h->td.wgs_per_cu ? h->td.wgs_per_cu : occ);
-    // a whole number of workgroups per XCD group
-    h->grid = (h->num_cus * h->wgs_per_cu) / kGroups * kGroups;
-    if (h->grid < kGroups) h->grid = kGroups;
-    h->gemm_grid = h->grid;
-    int red = red_req;
-    if (h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT) {
-        // one more workgroup per CU, which must fit beside the compute ones
-        if (occ < h->wgs_per_cu + 1) { delete h; return GEMM_RS_ERR_UNSUPPORTED_SHAPE; }
-        red = h->num_cus / kGroups * kGroups;
-        h->grid += red;
-        h->wgs_per_cu += 1;
-    }
-    if (red >= h->grid) red = h->grid - 1;
-    h->reduce_grid = h->num_cus * 8;
-    set_split(h, red);
+    rc = plan_launch(h, c, dev, prop.multiProcessorCount, occ);
+    if (rc != GEMM_RS_OK) { delete h; return rc; }
+    hipError_t e = hipSuccess;
     h->split.on = c->num_reducers == -2;
     h->split.settled = !h->split.on;
     h->split.ncand = 0;
@@ -550,6 +576,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     for (int i = 0; i < kPeers; ++i) a.gather[i] = gather ? static_cast<uint16_t*>(gather[i]) : nullptr;
     a.flags = h->flags;
     a.state = h->state;
+    a.status = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->state) + offsetof(DeviceState, status));
     a.trace = h->trace;
     a.finished = h->finished;
     a.g = h->g;
@@ -614,18 +641,13 @@ static int launch_reduce(gemm_rs_handle* h, Args& a, hipStream_t s)
     return GEMM_RS_OK;
 }
 
-static int run_impl(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
-                    const void* const* peers, void* out, void* local_slice, void* const* gather, void* stream)
+// The buffers of a run of a valid mode on a non-empty problem: present where
+// the mode uses them, 16-byte aligned, and the current device the handle's.
+static int check_run(const gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                     const void* const* peers, const void* out, const void* local, void* const* gather)
 {
-    if (!h) return GEMM_RS_ERR_INVALID_ARG;
-    if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    h->last_stream = s;
-    // an empty slice or no columns: nothing is read or written, buffers may be NULL
-    if (h->g.S == 0 || h->g.N == 0) return GEMM_RS_OK;
     const bool needs_gemm = mode != GEMM_RS_MODE_REDUCE_ONLY;
     const bool needs_sum = mode != GEMM_RS_MODE_GEMM_ONLY;
-    uint16_t* local = static_cast<uint16_t*>(local_slice ? local_slice : h->scratch);
     if (!aligned16(local)) return GEMM_RS_ERR_MISALIGNED;
     if (needs_gemm) {
         // with K_local == 0 the inputs are never read and may be NULL
@@ -653,9 +675,18 @@ static int run_impl(gemm_rs_handle* h, int32_t mode, const void* x, const void* 
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
     if (dev != h->device) return GEMM_RS_ERR_INVALID_ARG;
+    return GEMM_RS_OK;
+}
 
+// Enqueues a checked run; status, if set, replaces the handle's status words.
+static int launch_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                      const void* const* peers, void* out, uint16_t* local, void* const* gather, int32_t* status,
+                      hipStream_t s)
+{
+    const bool needs_sum = mode != GEMM_RS_MODE_GEMM_ONLY;
     Args a;
     fill_args(h, a, x, w, send, peers, out, local, needs_sum ? gather : nullptr);
+    if (status) a.status = status;
     int rc = GEMM_RS_OK;
     switch (mode) {
     case GEMM_RS_MODE_FUSED: rc = launch_gemm(h, a, true, s); break;
@@ -667,6 +698,21 @@ static int run_impl(gemm_rs_handle* h, int32_t mode, const void* x, const void* 
         break;
     }
     return rc;
+}
+
+static int run_impl(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,
+                    const void* const* peers, void* out, void* local_slice, void* const* gather, void* stream)
+{
+    if (!h) return GEMM_RS_ERR_INVALID_ARG;
+    if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    h->last_stream = s;
+    // an empty slice or no columns: nothing is read or written, buffers may be NULL
+    if (h->g.S == 0 || h->g.N == 0) return GEMM_RS_OK;
+    uint16_t* local = static_cast<uint16_t*>(local_slice ? local_slice : h->scratch);
+    const int rc = check_run(h, mode, x, w, send, peers, out, local, gather);
+    if (rc != GEMM_RS_OK) return rc;
+    return launch_run(h, mode, x, w, send, peers, out, local, gather, nullptr, s);
 }
 
 int gemm_rs_run(gemm_rs_handle* h, int32_t mode, const void* x, const void* w, void* const* send,

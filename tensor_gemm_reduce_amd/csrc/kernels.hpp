@@ -103,6 +103,7 @@ struct Args {
     int32_t gather_on;       // 1: every summed chunk is also stored into gather[]
     uint32_t* flags;         // ready flags, flag_stride words apart
     DeviceState* state;
+    int32_t* status;         // [0] error code, [1] flag index that timed out
     uint32_t* trace;         // 4 words per slot (debug)
     uint32_t* finished;      // per workgroup: epoch of the last fused launch it finished
     Geometry g;
@@ -682,8 +683,8 @@ __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, 
         __builtin_amdgcn_s_sleep(SLEEP);
         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
             gave_up = true;
-            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
-                atomicExch(&a.state->status[1], flag);
+            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.status[0], 0, kStatusTimeout) == 0)
+                atomicExch(&a.status[1], flag);
             return false;
         }
     }
@@ -1081,8 +1082,8 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
                             if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
                                 skip = 1;
                                 gave_up = true;
-                                if (atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
-                                    atomicExch(&a.state->status[1], t.flag);
+                                if (atomicCAS(&a.status[0], 0, kStatusTimeout) == 0)
+                                    atomicExch(&a.status[1], t.flag);
                                 break;
                             }
                         }
@@ -1138,7 +1139,8 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
 // launch stored the same value, so all workgroups of a launch agree on its
 // epoch without communicating (the words change only at kernel ends).  The
 // tickets and the claim counter of the next run are cleared by workgroup 0 of
-// this one.  A GEMM-only launch has no flags and touches none of this.
+// every fused run (the next run may use them even if this one does not).  A
+// GEMM-only launch has no flags and touches none of this.
 template <class C, bool FUSED, int VAR = 0>
 __device__ __forceinline__ void fused_body(const Args& a)
 {
@@ -1155,7 +1157,9 @@ __device__ __forceinline__ void fused_body(const Args& a)
                                  : 0u;
         s_epoch = e;
         s_ticket = tickets ? atomicAdd(&a.state->role[e & 1u][grp], 1u) : (uint32_t)(blockIdx.x / kGroups);
-        if (tickets && blockIdx.x == 0) {
+        // (every fused run clears the next run's set, whether or not it uses
+        // tickets itself: the next run may)
+        if (FUSED && blockIdx.x == 0) {
             const uint32_t nx = (e + 1u) & 1u;
             for (int i = 0; i < kGroups; ++i)
                 __hip_atomic_store(&a.state->role[nx][i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1304,8 +1308,8 @@ __device__ __forceinline__ bool ag_wait(const Args& a, int blk, uint32_t target)
     while ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
         __builtin_amdgcn_s_sleep(1);
         if ((int64_t)(wall_clock64() - t0) > a.watchdog_ticks) {
-            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.state->status[0], 0, kStatusTimeout) == 0)
-                atomicExch(&a.state->status[1], blk);
+            if ((threadIdx.x & 63) == 0 && atomicCAS(&a.status[0], 0, kStatusTimeout) == 0)
+                atomicExch(&a.status[1], blk);
             return false;
         }
     }

@@ -54,8 +54,8 @@ FLAG_PROTOCOLS = {"tile": 0, "row_counter": 1}
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather", "gemm_rs_status", "gemm_rs_query",
-           "gemm_rs_debug_read", "gemm_rs_destroy", "gemm_rs_strerror")
+           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather",
+           "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read", "gemm_rs_destroy", "gemm_rs_strerror")
 
 
 class gemm_rs_config(ctypes.Structure):
@@ -118,8 +118,8 @@ def lib():
         L.gemm_rs_strerror.argtypes = [ctypes.c_int]
         L.gemm_rs_strerror.restype = ctypes.c_char_p
         for name in ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather", "gemm_rs_status",
-                     "gemm_rs_query", "gemm_rs_debug_read"):
+                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather",
+                     "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
