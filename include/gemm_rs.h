@@ -78,6 +78,11 @@ extern "C" {
 #define GEMM_RS_ERR_HIP (-5)               /* a HIP runtime call failed         */
 #define GEMM_RS_ERR_TIMEOUT (-6)           /* a reducer gave up waiting (watchdog) */
 #define GEMM_RS_ERR_NO_MEMORY (-7)         /* device or host allocation failed  */
+#define GEMM_RS_ERR_SCRATCH (-8)           /* gemm_rs_run_static: the problem's
+                                              state exceeds the static scratch   */
+
+/* Device bytes of the static scratch gemm_rs_run_static uses per GPU. */
+#define GEMM_RS_STATIC_SCRATCH_BYTES 1048576 /* 1 MiB */
 
 /* ---- run modes ---------------------------------------------------------- */
 #define GEMM_RS_MODE_FUSED 0       /* one persistent kernel: compute + reducers  */
@@ -284,6 +289,30 @@ int gemm_rs_run_allreduce(gemm_rs_handle *h, int32_t mode, const void *x, const 
  * not overlap another run of the same handle on the device. */
 int gemm_rs_run_allgather(gemm_rs_handle *h, int32_t mode, const void *const *x_slices, const void *w,
                           void *x_gathered, void *y, void *stream);
+
+/* gemm_rs_run without a handle and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It calls no hipMalloc, hipFree or
+ * other allocating routine.  The run state, the per-workgroup finish marks and
+ * the ready flags live in a static device array of
+ * GEMM_RS_STATIC_SCRATCH_BYTES per GPU, kept until the process ends; a run
+ * whose state does not fit (ready flags: tiles x flag_stride words, finish
+ * marks: one word per workgroup of the grid) returns GEMM_RS_ERR_SCRATCH.
+ * Every call on one GPU shares that GPU's array: each run first clears it
+ * with a small kernel on `stream`, so calls that overlap on one GPU race and
+ * must be ordered by the caller (one stream, or synchronisation).
+ *   cfg          as for gemm_rs_create; num_reducers == -2 (adaptive) and any
+ *                debug_flags are refused (GEMM_RS_ERR_INVALID_ARG).
+ *   mode, x, w, send, peers, out, stream: as for gemm_rs_run.
+ *   local_slice  required (there is no handle scratch): device [S][N].
+ *   status       NULL, or a 4-byte aligned device array of 2 int32 that the
+ *                run zeroes first and in which a watchdog timeout leaves
+ *                GEMM_RS_ERR_TIMEOUT and the flag index (read it after the
+ *                stream work is done); with NULL a timeout is not reported.
+ * Results are those of gemm_rs_run with the same config and buffers. */
+int gemm_rs_run_static(const gemm_rs_config *cfg, int32_t mode, const void *x, const void *w,
+                       void *const *send, const void *const *peers, void *out,
+                       void *local_slice, int32_t *status, void *stream);
 
 /* Waits for the handle's last run and returns its device status:
  * GEMM_RS_OK, or GEMM_RS_ERR_TIMEOUT if a reducer gave up waiting for a ready

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "gemm_rs.h"
@@ -328,6 +329,9 @@ const char* gemm_rs_strerror(int code)
     case GEMM_RS_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP runtime error";
     case GEMM_RS_ERR_TIMEOUT: return "a reducer timed out waiting for a tile's ready flag";
     case GEMM_RS_ERR_NO_MEMORY: return "out of memory";
+    case GEMM_RS_ERR_SCRATCH:
+        return "the problem needs more device scratch (ready flags, finish marks, run state) than the "
+               "allocation-free entry point's static array holds (GEMM_RS_STATIC_SCRATCH_BYTES)";
     default: return "unknown error";
     }
 }
@@ -875,3 +879,115 @@ void gemm_rs_destroy(gemm_rs_handle* h)
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free runs
+//
+// gemm_rs_run_static keeps what a handle allocates (the run state, the
+// per-workgroup finish marks and the ready flags) in this array instead.  In
+// host code `scratch` names a host-side stand-in: its device address on each
+// GPU comes from hipGetSymbolAddress, taken once per device and used for
+// every kernel argument.
+static __device__ __align__(256) uint32_t scratch[GEMM_RS_STATIC_SCRATCH_BYTES / 4];
+
+// Zeroes n words at p and, if st is set, the two status words there (a kernel
+// rather than a memset, so that a captured graph holds no memset node).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, uint32_t n, int32_t* st)
+{
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+    if (st && blockIdx.x == 0 && threadIdx.x < 2) st[threadIdx.x] = 0;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kVariants = 3;
+
+// Per device, filled on the first allocation-free call there.
+struct StaticDevice {
+    bool ready;
+    bool gfx950;
+    int num_cus;
+    uint32_t* ptr;                                  // the device's copy of `scratch`
+    int occ[GEMM_RS_TILE_COUNT][kVariants];         // fused workgroups per CU; -1: not yet set up
+};
+
+std::mutex g_static_mu;
+StaticDevice g_static[kMaxDevices];
+
+}  // namespace
+
+extern "C" int gemm_rs_run_static(const gemm_rs_config* c, int32_t mode, const void* x, const void* w,
+                                  void* const* send, const void* const* peers, void* out, void* local_slice,
+                                  int32_t* status, void* stream)
+{
+    int rc = gemm_rs_validate(c);
+    if (rc != GEMM_RS_OK) return rc;
+    if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
+    // no adaptive split (its timing events), no trace log (its buffer)
+    if (c->num_reducers == -2 || c->debug_flags != 0) return GEMM_RS_ERR_INVALID_ARG;
+    if (!local_slice) return GEMM_RS_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return GEMM_RS_ERR_MISALIGNED;
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_RS_ERR_INVALID_ARG;
+    int variant = 0;
+    const TileDesc td = variant_desc(*c, &variant);
+    const int tile = resolve_tile(*c);
+    StaticDevice sd;
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        StaticDevice& e = g_static[dev];
+        if (!e.ready) {
+            hipDeviceProp_t prop;
+            HIP_TRY(hipGetDeviceProperties(&prop, dev));
+            void* p = nullptr;
+            HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+            e.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            e.num_cus = prop.multiProcessorCount;
+            e.ptr = static_cast<uint32_t*>(p);
+            for (int i = 0; i < GEMM_RS_TILE_COUNT; ++i)
+                for (int j = 0; j < kVariants; ++j) e.occ[i][j] = -1;
+            e.ready = true;
+        }
+        if (e.gfx950 && e.occ[tile][variant] < 0) {
+            int occ = 0;
+            rc = kernel_setup(td, &occ);
+            if (rc != GEMM_RS_OK) return rc;
+            e.occ[tile][variant] = occ;
+        }
+        sd = e;
+    }
+    if (!sd.gfx950) return GEMM_RS_ERR_NO_DEVICE;
+
+    gemm_rs_handle h{};
+    rc = plan_launch(&h, c, dev, sd.num_cus, sd.occ[tile][variant]);
+    if (rc != GEMM_RS_OK) return rc;
+    // layout: run state, finish marks, ready flags (each 256-byte aligned)
+    const size_t state_words = (sizeof(DeviceState) + 255) / 256 * 64;
+    const size_t fin_words = ((size_t)h.grid + 63) / 64 * 64;
+    const size_t flag_words = (size_t)(h.g.tiles > 0 ? h.g.tiles : 1) * (size_t)h.flag_stride;
+    if (state_words + fin_words + flag_words > GEMM_RS_STATIC_SCRATCH_BYTES / 4) return GEMM_RS_ERR_SCRATCH;
+    h.state = reinterpret_cast<DeviceState*>(sd.ptr);
+    h.finished = sd.ptr + state_words;
+    h.flags = h.finished + fin_words;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    h.last_stream = s;
+    if (h.g.S == 0 || h.g.N == 0) return GEMM_RS_OK;
+    uint16_t* local = static_cast<uint16_t*>(local_slice);
+    rc = check_run(&h, mode, x, w, send, peers, out, local, nullptr);
+    if (rc != GEMM_RS_OK) return rc;
+    // every run starts from zeroed flags and finish marks (run epoch 1): a
+    // call before it may have had another geometry
+    const uint32_t nclear = (uint32_t)(state_words + fin_words + flag_words);
+    {
+        void* args[] = {&sd.ptr, const_cast<uint32_t*>(&nclear), &status};
+        const int blocks = (int)((nclear + 255) / 256 < 1024 ? (nclear + 255) / 256 : 1024);
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&clear_words_kernel), dim3(blocks), dim3(256), args, 0,
+                                s));
+    }
+    // the kernels report a timeout into the caller's words, if any
+    int32_t* st_dev = status ? status
+                             : reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h.state) + offsetof(DeviceState, status));
+    return launch_run(&h, mode, x, w, send, peers, out, local, nullptr, st_dev, s);
+}

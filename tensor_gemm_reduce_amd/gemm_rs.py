@@ -23,6 +23,9 @@ ERR_NO_DEVICE = -4
 ERR_HIP = -5
 ERR_TIMEOUT = -6
 ERR_NO_MEMORY = -7
+ERR_SCRATCH = -8
+
+STATIC_SCRATCH_BYTES = 1 << 20
 
 MODE_FUSED = 0
 MODE_GEMM_ONLY = 1
@@ -54,7 +57,7 @@ FLAG_PROTOCOLS = {"tile": 0, "row_counter": 1}
 DEBUG_TRACE = 1
 
 EXPORTS = ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather",
+           "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather", "gemm_rs_run_static",
            "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read", "gemm_rs_destroy", "gemm_rs_strerror")
 
 
@@ -110,6 +113,8 @@ def lib():
         L.gemm_rs_run_allreduce.argtypes = [vp, ctypes.c_int32, vp, vp, ctypes.POINTER(vp),
                                             ctypes.POINTER(vp), vp, vp, ctypes.POINTER(vp), vp]
         L.gemm_rs_run_allgather.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(vp), vp, vp, vp, vp]
+        L.gemm_rs_run_static.argtypes = [cfgp, ctypes.c_int32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                         vp, vp, vp, vp]
         L.gemm_rs_status.argtypes = [vp]
         L.gemm_rs_query.argtypes = [vp, infop]
         L.gemm_rs_debug_read.argtypes = [vp, u32p, ctypes.c_size_t, u32p, ctypes.c_size_t]
@@ -118,7 +123,7 @@ def lib():
         L.gemm_rs_strerror.argtypes = [ctypes.c_int]
         L.gemm_rs_strerror.restype = ctypes.c_char_p
         for name in ("gemm_rs_validate", "gemm_rs_plan", "gemm_rs_plan_slots", "gemm_rs_create",
-                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather",
+                     "gemm_rs_run", "gemm_rs_run_allreduce", "gemm_rs_run_allgather", "gemm_rs_run_static",
                      "gemm_rs_status", "gemm_rs_query", "gemm_rs_debug_read"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
@@ -209,6 +214,17 @@ def gemm_rs_run_allgather(h, mode: int, x_slices, w: int | None, x_gathered: int
     vp = ctypes.c_void_p
     xs = (vp * len(x_slices))(*x_slices) if x_slices is not None else None
     return lib().gemm_rs_run_allgather(h, mode, xs, w, x_gathered, y, stream)
+
+
+def gemm_rs_run_static(cfg: gemm_rs_config, mode: int, x: int | None, w: int | None, send, peers,
+                       out: int | None, local: int | None, status: int | None, stream: int | None) -> int:
+    """The allocation-free run: no handle; pointers are integers (device
+    addresses), send/peers lists of 7 of them, status the device address of
+    two int32 words (or None)."""
+    vp = ctypes.c_void_p
+    send_arr = (vp * 7)(*send) if send is not None else None
+    peer_arr = (vp * 7)(*peers) if peers is not None else None
+    return lib().gemm_rs_run_static(ctypes.byref(cfg), mode, x, w, send_arr, peer_arr, out, local, status, stream)
 
 
 def gemm_rs_status(h) -> int:
