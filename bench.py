@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--tile", default="auto")
     p.add_argument("--reducers", type=int, default=-1,
                    help="dedicated reducer workgroups: -1 the plan's default, -2 adaptive")
-    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "coresident"],
+    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "coresident", "stream"],
                    help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--tile-stores", default="device", choices=["device", "nt"],
                    help="cache policy of the routed tile stores (nt: non-temporal hint)")
@@ -312,7 +312,7 @@ def measure_case(c: Case, warmup, iters):
         "reduce_pct_hbm": 100.0 * cfg.reduce_bytes / tr * 1e-3 / PEAK_HBM_GBS,
         "overlap": 1.0 - (tf - tg) / tr,
         "speedup_vs_sequential": seq["median_us"] / tf,
-        "reduce_mode": {0: "auto", 1: "tail", 2: "coresident"}[c.op.info.reduce_mode],
+        "reduce_mode": {0: "auto", 1: "tail", 2: "coresident", 3: "stream"}[c.op.info.reduce_mode],
         **extra,
     }
 

@@ -111,6 +111,15 @@ extern "C" {
                                    sums the peers of its items while the GEMM runs,
                                    then adds the local chunk once the tile's flag
                                    is set                                          */
+#define GEMM_RS_REDUCE_STREAM 3 /* 256x256 tile, K_local >= 384: four of the eight
+                                   waves of each compute workgroup issue no stage
+                                   loads and stream the slice sum between their
+                                   MFMAs (two loads and a store per K step, each
+                                   load in flight for three steps) once the
+                                   workgroup's own tiles are released; the rest
+                                   is summed after the last tile.  Tile flags and
+                                   device-scope stores only; not with the
+                                   all-reduce's FUSED runs                        */
 
 /* ---- cache policy of the routed tile stores ------------------------------ */
 #define GEMM_RS_STORES_DEVICE 0      /* device scope, written through L2        */

@@ -9,6 +9,7 @@
 
 #include <mutex>
 #include <new>
+#include <type_traits>
 
 #include "gemm_rs.h"
 #include "kernels.hpp"
@@ -40,6 +41,8 @@ typedef TileCfg<128, 128, 32, 3, 2, 2, 32> Tile128x128;
 typedef TileCfg<128, 256, 32, 4, 2, 2, 32> Tile128x256;
 typedef TileCfg<256, 128, 32, 4, 2, 2, 32> Tile256x128;
 typedef TileCfg<256, 256, 64, 2, 2, 4, 32> Tile256x256;
+// the stream kernel of the 256x256 tile: four loader waves, four stream waves
+typedef TileCfg<256, 256, 64, 2, 2, 4, 32, 4> Tile256x256S;
 
 struct TileDesc {
     int bm, bn, bk;
@@ -53,6 +56,9 @@ struct TileDesc {
     const void* kernel_rows;   // `kernel` reading row counters
     const void* ag_kernel;     // all-gather + GEMM: copy phase, then the GEMM waiting for rows
     const void* ag_gemm_kernel;  // the same GEMM over an already gathered buffer
+    const void* stream_kernel;   // fused, reduce_mode STREAM (or null)
+    int stream_lds_bytes;        // its stages, stream slots and probe area
+    int fused_lds_bytes;         // LDS of `kernel` (set by variant_desc)
 };
 
 // Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
@@ -80,17 +86,25 @@ const void* ag_kernel_for()
         return reinterpret_cast<const void*>(&ag_kernel_1w<C, FUSED>);
 }
 
-template <class C>
+template <class C, class CS = void>
 TileDesc desc()
 {
     static_assert(C::LDS_BYTES <= 160 * 1024 - 64, "LDS of one workgroup");
     // occupancy is set by the stages
     constexpr bool two = C::LDS_BYTES <= 80 * 1024 - 64;
+    const void* sk = nullptr;
+    int slds = 0;
+    if constexpr (!std::is_void<CS>::value) {
+        static_assert(CS::LDS_BYTES == C::LDS_BYTES && CS::LDS_BYTES + kStreamLds <= 160 * 1024 - 256,
+                      "the stream kernel's LDS");
+        sk = reinterpret_cast<const void*>(&fused_kernel_8w<CS, true>);
+        slds = CS::LDS_BYTES + kStreamLds;
+    }
     return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, C::LDS_BYTES,
                     kernel_for<C, true, two>(), kernel_for<C, false, two>(),
                     kernel_for<C, true, two, kVarNt>(), kernel_for<C, false, two, kVarNt>(),
                     kernel_for<C, true, two, kVarRows>(),
-                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>()};
+                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), sk, slds, C::LDS_BYTES};
 }
 
 TileDesc tile_desc(int id)
@@ -101,8 +115,8 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x128: return desc<Tile128x128>();
     case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
-    case GEMM_RS_TILE_256x256: return desc<Tile256x256>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256S>();
+    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
     }
 }
 
@@ -254,7 +268,11 @@ int gemm_rs_validate(const gemm_rs_config* c)
     // the GEMM-only kernel); one at a time
     if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL && c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER)
         return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_CORESIDENT)
+    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_STREAM)
+        return GEMM_RS_ERR_INVALID_ARG;
+    // the stream kernel is the default store policy with tile flags
+    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM &&
+        (c->tile_stores != GEMM_RS_STORES_DEVICE || c->flag_protocol != GEMM_RS_FLAGS_TILE))
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL && c->num_reducers > 0)
         return GEMM_RS_ERR_INVALID_ARG;
@@ -279,6 +297,12 @@ int gemm_rs_validate(const gemm_rs_config* c)
     const int64_t tiles = (int64_t)c->tp * ((S + bm - 1) / bm) * (((int64_t)c->N + bn - 1) / bn);
     if (tiles > (1 << 30)) return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     if (c->drop_flag >= 0 && c->drop_flag >= tiles) return GEMM_RS_ERR_INVALID_ARG;
+    // the stream kernel: the 256x256 tile, and at least kProbe + 2 K steps per
+    // tile (its waits count the stream loads of the previous tile's last
+    // steps, and the readiness probe is read at step kProbe)
+    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM &&
+        (resolve_tile(*c) != GEMM_RS_TILE_256x256 || c->K_local < (kProbe + 2) * 64))
+        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return GEMM_RS_OK;
 }
 
@@ -400,13 +424,18 @@ static void free_state(gemm_rs_handle* h)
     if (h->agfinished) (void)hipFree(h->agfinished);
 }
 
-// The tile and kernel variant a (valid) config runs: the store policy or the
-// flag protocol selects a separate instantiation.
+// The tile and kernel variant a (valid) config runs: the store policy, the
+// flag protocol or the stream selects a separate instantiation of the fused
+// kernel.
 static TileDesc variant_desc(const gemm_rs_config& c, int* variant)
 {
     TileDesc td = tile_desc(resolve_tile(c));
     *variant = 0;
-    if (c.tile_stores == GEMM_RS_STORES_NONTEMPORAL) {
+    if (resolve_reduce_mode(c) == GEMM_RS_REDUCE_STREAM) {
+        td.kernel = td.stream_kernel;
+        td.fused_lds_bytes = td.stream_lds_bytes;
+        *variant = 3;
+    } else if (c.tile_stores == GEMM_RS_STORES_NONTEMPORAL) {
         td.kernel = td.kernel_nt;
         td.gemm_kernel = td.gemm_kernel_nt;
         *variant = 1;
@@ -421,9 +450,9 @@ static TileDesc variant_desc(const gemm_rs_config& c, int* variant)
 // returns in *occ how many fused workgroups fit on one CU.
 static int kernel_setup(const TileDesc& td, int* occ)
 {
-    HIP_TRY(hipFuncSetAttribute(td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.lds_bytes));
+    HIP_TRY(hipFuncSetAttribute(td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.fused_lds_bytes));
     HIP_TRY(hipFuncSetAttribute(td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.lds_bytes));
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, td.kernel, td.threads, td.lds_bytes));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, td.kernel, td.threads, td.fused_lds_bytes));
     return GEMM_RS_OK;
 }
 
@@ -443,7 +472,7 @@ static int plan_launch(gemm_rs_handle* h, const gemm_rs_config* c, int dev, int 
     // automatic: no dedicated reducers, the compute workgroups sum the slice
     const int red_req = c->num_reducers < 0 ? 0 : c->num_reducers;
     h->reduce_mode = resolve_reduce_mode(*c);
-    h->fused_lds = h->td.lds_bytes;
+    h->fused_lds = h->td.fused_lds_bytes;
     // the persistent grid holds the workgroups per CU the kernel was built for
     // (more would share a SIMD's registers between more waves than planned)
     h->wgs_per_cu = occ < 1 ? 1 : (occ > h->td.wgs_per_cu ? h->td.wgs_per_cu : occ);
@@ -462,6 +491,11 @@ static int plan_launch(gemm_rs_handle* h, const gemm_rs_config* c, int dev, int 
     if (red >= h->grid) red = h->grid - 1;
     h->reduce_grid = h->num_cus * 8;
     set_split(h, red);
+    // a stream workgroup probes the flags of its items' own tiles in one
+    // 64-lane load: its items may span at most 64 tiles
+    if (h->reduce_mode == GEMM_RS_REDUCE_STREAM && h->g.ts > 0 &&
+        (h->g.ts + h->compute_wgs - 1) / h->compute_wgs + 1 > 64)
+        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return GEMM_RS_OK;
 }
 
@@ -730,6 +764,9 @@ int gemm_rs_run_allreduce(gemm_rs_handle* h, int32_t mode, const void* x, const 
                           void* stream)
 {
     if (mode != GEMM_RS_MODE_GEMM_ONLY && !gather) return GEMM_RS_ERR_INVALID_ARG;
+    // the stream kernel's sum stores into `out` only
+    if (h && mode == GEMM_RS_MODE_FUSED && h->reduce_mode == GEMM_RS_REDUCE_STREAM)
+        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return run_impl(h, mode, x, w, send, peers, out, local_slice, gather, stream);
 }
 
@@ -900,7 +937,7 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, uint32_t 
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 3;
+constexpr int kVariants = 4;
 
 // Per device, filled on the first allocation-free call there.
 struct StaticDevice {

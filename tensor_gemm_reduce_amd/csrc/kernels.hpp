@@ -177,7 +177,7 @@ struct TileCfg {
     static_assert((NS - 2) * LPS + STORES <= 63, "vmcnt range");
     // One workgroup per CU (four waves whose stages fit only once, or eight
     // waves) with every wave loading: the K loop is pipelined across steps.
-    static constexpr bool XP = EW == 0 && LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
+    static constexpr bool XP = LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
 };
 
 template <int MF> struct AccT;
@@ -267,36 +267,32 @@ struct TileState {
     typename AccT<C::MF>::type acc[C::FM][C::FN];
 };
 
-// Per-thread load plan of one tile (loader threads): byte offset of each chunk
-// this thread moves at k = 0 (kOob for rows past the tile's valid extent) and
-// the chunk's k offset (for the K tail).
+// Per-thread load plan of one tile (loader threads).  Thread tid moves the
+// chunks p = i * LTHREADS + tid (i = 0 .. LD-1) of each operand: tile row
+// r_i = tid / CPR + i * LTHREADS / CPR and 16-byte column c = (tid % CPR) ^
+// swz(r_i).  The swizzle depends on r mod 16 only and LTHREADS / CPR is a
+// multiple of 16, so c is the same for every i, and the plan is one byte
+// offset per operand (chunk i = 0 at k = 0) plus the chunk's k offset.  Rows
+// past the tile's valid extent are loaded like the others: they are rows of
+// the next slice or columns of the next tile, never stored, or lie past the
+// end of the buffer and read as zero.
 template <class C>
 struct LoadPlan {
-    uint32_t a_off[C::A_LD], b_off[C::B_LD];
-    uint16_t a_k[C::A_LD], b_k[C::B_LD];
+    uint32_t a_off, b_off;
+    int kc;
 };
 
 template <class C>
-__device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int row0, int rows, int n0, int cols)
+__device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int row0, int n0)
 {
+    static_assert((C::LTHREADS / C::CPR) % 16 == 0, "one swizzled column per thread");
     const int tid = threadIdx.x;
     const uint32_t K = (uint32_t)a.g.K;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-        const int p = i * C::LTHREADS + tid;
-        const int r = p / C::CPR;
-        const int c = (p % C::CPR) ^ swz<C::CPR>(r);
-        lp.a_k[i] = (uint16_t)(c * 8);
-        lp.a_off[i] = r < rows ? ((uint32_t)(row0 + r) * K + (uint32_t)c * 8u) * 2u : kOob;
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-        const int p = i * C::LTHREADS + tid;
-        const int r = p / C::CPR;
-        const int c = (p % C::CPR) ^ swz<C::CPR>(r);
-        lp.b_k[i] = (uint16_t)(c * 8);
-        lp.b_off[i] = r < cols ? ((uint32_t)(n0 + r) * K + (uint32_t)c * 8u) * 2u : kOob;
-    }
+    const int r = tid / C::CPR;
+    const int c = (tid % C::CPR) ^ swz<C::CPR>(r);
+    lp.kc = c * 8;
+    lp.a_off = ((uint32_t)(row0 + r) * K + (uint32_t)c * 8u) * 2u;
+    lp.b_off = ((uint32_t)(n0 + r) * K + (uint32_t)c * 8u) * 2u;
 }
 
 // Issue the LDS-direct loads of the BK slice starting at k0 into stage buffer
@@ -304,32 +300,37 @@ __device__ __forceinline__ void make_plan(const Args& a, LoadPlan<C>& lp, int ro
 // LDS: lane l writes bytes [16 l, 16 l + 16) after the wave's base.
 //
 // Branch-free: a chunk whose k lies at or past K (the K tail, or a whole stage
-// past the end) gets an offset past the resource and reads as zero; rows past
-// the tile carry kOob already, and kOob + 2 k0 stays past the resource.
+// past the end) gets an offset past the resource and reads as zero (kOob plus
+// the rows of a tile stays past any resource of these kernels).
 template <class C>
 __device__ __forceinline__ void issue_stage(const LoadPlan<C>& lp, __amdgpu_buffer_rsrc_t rx,
                                             __amdgpu_buffer_rsrc_t rw, char* stage, int k0, int K)
 {
     // (uniform: the LDS destination, and with it M0, is scalar arithmetic)
     const int wave = uni((int)(threadIdx.x >> 6));
-    const int lim = K - k0;  // chunks with k offset >= lim are past K
+    const bool in_k = lp.kc < K - k0;
+    const uint32_t a0 = in_k ? lp.a_off + (uint32_t)k0 * 2u : kOob;
+    const uint32_t b0 = in_k ? lp.b_off + (uint32_t)k0 * 2u : kOob;
+    // bytes between the rows of chunks i and i + 1
+    const uint32_t step = (uint32_t)uni((C::LTHREADS / C::CPR) * K * 2);
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-        const uint32_t off = (int)lp.a_k[i] < lim ? lp.a_off[i] + (uint32_t)k0 * 2u : kOob;
+    for (int i = 0; i < C::A_LD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (lds_void_t*)(stage + (i * C::LTHREADS + wave * 64) * 16), 16, off, 0, 0, 0);
-    }
+            rx, (lds_void_t*)(stage + (i * C::LTHREADS + wave * 64) * 16), 16, a0 + (uint32_t)i * step, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-        const uint32_t off = (int)lp.b_k[i] < lim ? lp.b_off[i] + (uint32_t)k0 * 2u : kOob;
+    for (int i = 0; i < C::B_LD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rw, (lds_void_t*)(stage + C::A_BYTES + (i * C::LTHREADS + wave * 64) * 16), 16, off, 0, 0, 0);
-    }
+            rw, (lds_void_t*)(stage + C::A_BYTES + (i * C::LTHREADS + wave * 64) * 16), 16, b0 + (uint32_t)i * step,
+            0, 0, 0);
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedAlu = 0x001;
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedSalu = 0x004;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedVmemWrite = 0x040;
 constexpr int kSchedDsRead = 0x100;
 
 // Fragments of one MFMA k-substep s of a stage: FM X fragments and FN W
@@ -736,6 +737,233 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
 }
 
 
+// ---------------------------------------------------------------- slice-sum stream
+//
+// reduce_mode STREAM (256x256 tile, eight waves): waves 0-3 issue every stage
+// load of the GEMM ("loader" waves), waves 4-7 issue none and instead stream
+// the slice sum while all eight run the MFMAs.  Vector-memory operations of a
+// wave retire in issue order, so a wave that waits for its stage loads every
+// K step could not keep an HBM load in flight across steps; a stream wave
+// only ever waits for its own stream operations, so each can stay in flight
+// for kSD steps.
+//
+// Stream wave w of the TW in the grid owns items [n w / TW, n (w + 1) / TW)
+// and takes them in order, four K steps per item (two loads per step, in the
+// oracle's sum order): peers 0, 1 | peers 2, 3 | peers 4, 5 | peer 6, local.
+// Every step of a stream wave issues exactly kSVm vector-memory
+// instructions, the same whether it has work or not (an idle load reads as
+// zero through an empty buffer resource, an idle store goes past its
+// resource), so that its waits are constants and the step's code has no
+// branch: it is interleaved with the step's MFMAs.  A step:
+//   before its MFMAs: wait until the loads issued kSD steps ago have landed
+//     (kSVm * (kSD - 1) younger instructions, plus the tile's epilogue stores
+//     in the first kSD steps of a tile);
+//   after the barrier: read them from their LDS slot pair, add them to the
+//     running FP32 sum (reset at the item's first step), and at the item's
+//     last step store the rounded sum to out; then issue this step's two loads
+//     into the slot pair read one step earlier (kSD + 1 pairs, so a pair is
+//     refilled only after the step that read it has used the values).
+// Loads carry device scope, so the local slice is read from the memory side,
+// never from a stale line of this XCD's L2.
+//
+// The local partial of an item may be read only once its tile is released.
+// A workgroup's four stream waves own consecutive items, spanning own tiles
+// t_lo .. t_hi; until all of them are released (latched once seen), stream
+// waves issue idle operations.  Loader wave 0 probes the tiles' flags with
+// device-scope loads into LDS right after the barrier of step kProbe - 1,
+// while the workgroup has not latched; the wait of step kProbe covers them,
+// and after its barrier every wave reads the probe and latches together.
+// The previous tile's flag is published after the barrier of step kPub = kSD:
+// the stream waves' epilogue stores are older than the loads that step's wait
+// covers.  Items a stream wave has not finished after the workgroup's last
+// tile are summed there by the stream wave and its SIMD's loader wave.
+constexpr int kSD = 2;                 // steps between a stream load's issue and its use
+constexpr int kSVm = 3;                // vector-memory instructions per stream step
+constexpr int kSPairs = kSD + 1;       // slot pairs per stream wave
+constexpr int kSSlots = 2 * kSPairs;   // 1 KiB LDS slots per stream wave
+constexpr int kSWaveLds = kSSlots * 1024;
+constexpr int kProbeLds = 256;         // 64 flags
+constexpr int kProbe = 4;              // step whose barrier certifies the probe
+constexpr int kPub = kSD;              // step whose barrier publishes the previous tile's flag
+constexpr int kStreamLds = 4 * kSWaveLds + kProbeLds;
+
+struct Stream {
+    char* slots;          // this wave's kSSlots 1 KiB LDS slots
+    const char* probe;    // the workgroup's probe area (one flag per lane)
+    ItemMap m;
+    int first, end;       // this wave's item range
+    int issued;           // steps that issued real loads: next item first + issued / 4, part issued % 4
+    int consumed;         // real steps consumed
+    uint32_t rbits;       // bit k: the step k + 1 back issued real loads
+    int it;               // steps run (the loads of step i go to slot pair i % kSPairs)
+    bool latched;         // every own tile of the workgroup's items is released
+    int t_lo, t_hi;       // own tiles of the workgroup's items (t_hi < t_lo: none)
+    uint32_t epoch;
+    uint32_t slice_bytes;
+    uint32_t src_lo, src_hi;  // lane l < 8: base address of source l (7 peers, then the local slice)
+    f32x8 acc;
+};
+
+// Item range of stream wave gw of tw over n items.
+__device__ __forceinline__ int stream_bound(int64_t n, int gw, int tw) { return (int)(n * gw / tw); }
+
+// Every wave of a stream workgroup sets this up (the loader waves use the
+// probe fields only).  pos: the workgroup's position in a round, sw: the
+// stream wave index 0..3 (loader waves pass 0), C: compute workgroups.
+__device__ __forceinline__ void stream_init(Stream& s, const Args& a, char* stream_lds, int pos, int sw, int C,
+                                            uint32_t epoch)
+{
+    s.m = item_map(a);
+    const int64_t n = s.m.nitems;
+    const int tw = 4 * C;
+    s.slots = stream_lds + sw * kSWaveLds;
+    s.probe = stream_lds + 4 * kSWaveLds;
+    s.first = uni(stream_bound(n, pos * 4 + sw, tw));
+    s.end = uni(stream_bound(n, pos * 4 + sw + 1, tw));
+    const int wfirst = stream_bound(n, pos * 4, tw), wend = stream_bound(n, pos * 4 + 4, tw);
+    s.t_lo = uni(wfirst >> s.m.ipt_log2);
+    s.t_hi = uni(wend > wfirst ? (wend - 1) >> s.m.ipt_log2 : s.t_lo - 1);
+    s.issued = 0;
+    s.consumed = 0;
+    s.rbits = 0;
+    s.it = 0;
+    s.latched = s.t_hi < s.t_lo;  // nothing to wait for
+    s.epoch = (uint32_t)uni((int)epoch);
+    s.slice_bytes = a.slice_bytes;
+    const int lane = threadIdx.x & 63;
+    const uint16_t* p = a.dst[a.g.rank];
+#pragma unroll
+    for (int i = 0; i < kPeers; ++i) p = lane == i ? a.peers[i] : p;
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    s.src_lo = (uint32_t)v;
+    s.src_hi = (uint32_t)(v >> 32);
+    s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// Loader wave 0: device-scope loads of the flags of own tiles t_lo + lane
+// (lanes past t_hi read zero) into the probe area.
+__device__ __forceinline__ void stream_probe_issue(const Stream& s, const Args& a)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = s.t_lo + lane;
+    const uint32_t fbytes = (uint32_t)a.g.tiles * (uint32_t)a.flag_stride * 4u;
+    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc((void*)a.flags, 0, fbytes, kRsrcFlags);
+    const uint32_t off = t <= s.t_hi ? (uint32_t)((a.g.rank * a.g.ts + t) * a.flag_stride) * 4u : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, (lds_void_t*)s.probe, 4, off, 0, 0, kAuxSc1);
+}
+
+// Every wave, after the barrier that certifies the probe: latch once every
+// probed tile holds this run's epoch.
+__device__ __forceinline__ void stream_probe_read(Stream& s)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t f = *reinterpret_cast<const uint32_t*>(s.probe + lane * 4);
+    const bool ok = s.t_lo + lane > s.t_hi || f == s.epoch;
+    s.latched = __builtin_amdgcn_ballot_w64(ok) == ~0ull;
+}
+
+// Stream wave, before the step's MFMAs: wait for the loads of the step kSD
+// back (recent: the tile's epilogue stores are younger than them).
+template <int STORES>
+__device__ __forceinline__ void stream_wait(bool recent)
+{
+    if (recent)
+        wait_vmcnt<kSVm * (kSD - 1) + STORES>();
+    else
+        wait_vmcnt<kSVm * (kSD - 1)>();
+}
+
+// Slot pair of the loads issued at step i.
+__device__ __forceinline__ char* stream_pair(const Stream& s, int i)
+{
+    return s.slots + (i % kSPairs) * 2048;
+}
+
+// Eight BF16 values to FP32 (exact).
+__device__ __forceinline__ f32x8 widen8(const u32x4& v)
+{
+    f32x8 b;
+    b[0] = bf16_bits_to_f32(v.x & 0xFFFFu);
+    b[1] = bf16_bits_to_f32(v.x >> 16);
+    b[2] = bf16_bits_to_f32(v.y & 0xFFFFu);
+    b[3] = bf16_bits_to_f32(v.y >> 16);
+    b[4] = bf16_bits_to_f32(v.z & 0xFFFFu);
+    b[5] = bf16_bits_to_f32(v.z >> 16);
+    b[6] = bf16_bits_to_f32(v.w & 0xFFFFu);
+    b[7] = bf16_bits_to_f32(v.w >> 16);
+    return b;
+}
+
+// Stream wave, after the barrier: add the fetched loads (if they were real) to
+// the running sum, store it at the item's last step (else an idle store), then
+// issue this step's loads into the slots just read.  Branch-free.
+__device__ __forceinline__ void stream_step(Stream& s, const Args& a)
+{
+    // consume the loads of step it - kSD
+    const char* cpair = stream_pair(s, s.it + kSPairs - kSD) + (threadIdx.x & 63) * 16;
+    const u32x4 va = *reinterpret_cast<const u32x4*>(cpair);
+    const u32x4 vb = *reinterpret_cast<const u32x4*>(cpair + 1024);
+    const bool real_c = (s.rbits >> (kSD - 1)) & 1u;
+    const int part_c = s.consumed & 3;
+    const int item_c = s.first + (s.consumed >> 2);
+    const f32x8 z = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x8 base = part_c == 0 ? z : s.acc;
+    const f32x8 sum = (base + widen8(va)) + widen8(vb);
+    s.acc = real_c ? sum : s.acc;
+    const bool last = real_c && part_c == 3;
+    const uint32_t soff = last ? item_boff(s.m, a, item_c) : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(pack8(s.acc), __builtin_amdgcn_make_buffer_rsrc(a.out, 0, s.slice_bytes, kRsrcFlags),
+                                           soff, 0, kAuxNt);
+    s.consumed += real_c ? 1 : 0;
+    // issue
+    const int part = s.issued & 3;
+    const int item = s.first + (s.issued >> 2);
+    const bool real = s.latched && item < s.end;
+    const uint32_t boff = real ? item_boff(s.m, a, item) : kOob;
+    const int sa = 2 * part, sb = part < 3 ? 2 * part + 1 : kPeers;
+    const uint64_t pa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)s.src_hi, sa) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)s.src_lo, sa);
+    const uint64_t pb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)s.src_hi, sb) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)s.src_lo, sb);
+    const uint32_t nrec = real ? s.slice_bytes : 0u;
+    char* pair = stream_pair(s, s.it);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pa), 0, nrec, kRsrcFlags), (lds_void_t*)pair, 16,
+        boff, 0, 0, kAuxSc1 | kAuxNt);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pb), 0, nrec, kRsrcFlags),
+        (lds_void_t*)(pair + 1024), 16, boff, 0, 0, kAuxSc1 | kAuxNt);
+    s.issued += real ? 1 : 0;
+    s.rbits = ((s.rbits << 1) | (real ? 1u : 0u)) & ((1u << kSD) - 1u);
+    ++s.it;
+}
+
+// Stream wave, after its last tile: wait for everything in flight and consume
+// the kSD steps not yet consumed (stores of items they complete included).
+__device__ __forceinline__ void stream_settle(Stream& s, const Args& a)
+{
+    wait_vmcnt<0>();
+#pragma unroll 1
+    for (int k = 0; k < kSD; ++k) {
+        const char* pair = stream_pair(s, s.it + kSPairs - kSD) + (threadIdx.x & 63) * 16;
+        const u32x4 va = *reinterpret_cast<const u32x4*>(pair);
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(pair + 1024);
+        const bool real_c = (s.rbits >> (kSD - 1)) & 1u;
+        const int part_c = s.consumed & 3;
+        const int item_c = s.first + (s.consumed >> 2);
+        const f32x8 z = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x8 sum = ((part_c == 0 ? z : s.acc) + widen8(va)) + widen8(vb);
+        s.acc = real_c ? sum : s.acc;
+        const uint32_t soff = real_c && part_c == 3 ? item_boff(s.m, a, item_c) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(pack8(s.acc),
+                                               __builtin_amdgcn_make_buffer_rsrc(a.out, 0, s.slice_bytes, kRsrcFlags),
+                                               soff, 0, kAuxNt);
+        s.consumed += real_c ? 1 : 0;
+        s.rbits = (s.rbits << 1) & ((1u << kSD) - 1u);
+        ++s.it;
+    }
+}
+
 // ---------------------------------------------------------------- tile loop
 
 // State carried from one tile to the next: whether the previous tile's
@@ -777,7 +1005,9 @@ struct TileJob {
 };
 
 // X rows come from `xp` (xbytes long, row0 counted in it); by default from a.x.
-template <class C>
+// ISSUE: this wave issues stage loads (every wave but a stream kernel's
+// stream waves).
+template <class C, bool ISSUE = true>
 __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<C>& job, int row0, int rows,
                                               int n0, int cols, const void* xp = nullptr, uint32_t xbytes = 0)
 {
@@ -785,10 +1015,10 @@ __device__ __forceinline__ void tile_prologue(const Args& a, char* lds, TileJob<
     job.nk = (K + C::BK - 1) / C::BK;
     job.xp = xp ? xp : (const void*)a.x;
     job.xbytes = xp ? xbytes : a.x_bytes;
-    if (job.nk == 0) return;
+    if (!ISSUE || job.nk == 0) return;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
-    make_plan<C>(a, job.lp, row0, rows, n0, cols);
+    make_plan<C>(a, job.lp, row0, n0);
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s) issue_stage<C>(job.lp, rx, rw, lds + s * C::STAGE_BYTES, s * C::BK, K);
 }
@@ -950,6 +1180,114 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
     publish_pending<ROWS>(a, hk);
 }
 
+// The K loop of a tile in the stream kernel (four loader waves, four stream
+// waves, two stages), pipelined across steps like tile_kloop_xp.  Loader waves
+// wait for their stage loads (and at step 0 for their previous epilogue
+// stores); stream waves wait only for their own stream loads (stream_fetch)
+// and run a stream step where loader waves issue the refill.  The previous
+// tile's flag is published after the barrier of step kPub, the first that
+// certifies the stream waves' epilogue stores (at the tile's end if the loop
+// is shorter).
+template <class C, bool STREAMER>
+__device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
+                                                 StepHooks& hk, Stream& s)
+{
+    static_assert(C::KSUB % 2 == 0 && C::NS == 2 && C::WAVES == 8 && C::LW == 4, "stream kernel tile");
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < AccT<C::MF>::N; ++e) st.acc[i][j][e] = 0.0f;
+
+    const int K = a.g.K;
+    const int nk = job.nk;
+    constexpr int kMf = C::FM * C::FN;   // MFMAs per substep
+    constexpr int kDs = C::FM + C::FN;   // fragment reads per substep
+    const int wave = uni((int)(threadIdx.x >> 6));
+    if (nk > 0) {
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
+        bf16x8 xf[2][C::FM], wf[2][C::FN];
+        // stage 0 came from the prologue, before the previous tile's stores
+        if constexpr (!STREAMER) {
+            if (hk.stores)
+                wait_vmcnt<C::STORES>();
+            else
+                wait_vmcnt<0>();
+        }
+        stage_barrier();
+        if constexpr (!STREAMER) issue_stage<C>(job.lp, rx, rw, lds + C::STAGE_BYTES, C::BK, K);
+        load_frags<C>(lds, 0, xf[0], wf[0]);
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            const char* cur = lds + (kt & 1) * C::STAGE_BYTES;
+            if constexpr (STREAMER) stream_wait<C::STORES>(kt < kSD);
+#pragma unroll
+            for (int ss = 0; ss + 1 < C::KSUB; ++ss) {
+                load_frags<C>(cur, ss + 1, xf[(ss + 1) & 1], wf[(ss + 1) & 1]);
+                mfma_substep<C>(st, xf[ss & 1], wf[ss & 1]);
+            }
+#pragma unroll
+            for (int ss = 0; ss + 1 < C::KSUB; ++ss)
+#pragma unroll
+                for (int m = 0; m < kMf; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+            if constexpr (!STREAMER) wait_vmcnt<0>();
+            wait_lgkm0();
+            stage_barrier();
+            if (kt == kPub) publish_pending<false>(a, hk);
+            if (!s.latched) {
+                if (kt == kProbe - 1 && !STREAMER && wave == 0) stream_probe_issue(s, a);
+                if (kt == kProbe) stream_probe_read(s);
+            }
+            __builtin_amdgcn_s_setprio(1);
+            if constexpr (STREAMER)
+                stream_step(s, a);
+            else
+                issue_stage<C>(job.lp, rx, rw, lds + (kt & 1) * C::STAGE_BYTES, (kt + 2) * C::BK, K);
+            load_frags<C>(lds + ((kt + 1) & 1) * C::STAGE_BYTES, 0, xf[0], wf[0]);
+            mfma_substep<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1]);
+            if constexpr (STREAMER) {
+                // the stream step's arithmetic, its loads and store and the
+                // next step's first fragments spread over the MFMAs
+#pragma unroll
+                for (int m = 0; m < kMf; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+                    if (m < kSVm) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead | kSchedVmemWrite, 1, 0);
+                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+            } else {
+                // the refill's loads, two per MFMA, then the next step's
+                // first fragments
+#pragma unroll
+                for (int m = 0; m < kMf; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    if (2 * m < C::LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        // the last step
+        const char* cur = lds + ((nk - 1) & 1) * C::STAGE_BYTES;
+#pragma unroll
+        for (int ss = 0; ss < C::KSUB; ++ss) {
+            if (ss + 1 < C::KSUB) load_frags<C>(cur, ss + 1, xf[(ss + 1) & 1], wf[(ss + 1) & 1]);
+            mfma_substep<C>(st, xf[ss & 1], wf[ss & 1]);
+        }
+    }
+    // loader waves drain the zero-filling loads past the end; stream waves
+    // keep their loads in flight unless the previous tile's flag is still to
+    // be published (a loop shorter than kPub + 1 steps); every wave finishes
+    // reading LDS before the next tile's loads overwrite it
+    if (!STREAMER || hk.pend_flag >= 0) wait_vmcnt<0>();
+    stage_barrier();
+    publish_pending<false>(a, hk);
+}
+
 // Every group holds G/8 workgroups; group x has R_x = R/8 + (x < R%8) reducers
 // and C_x = G/8 - R_x compute workgroups, so the groups' compute counts add up
 // to C = G - R whatever R is.
@@ -978,8 +1316,12 @@ template <class C, bool FUSED, int VAR = 0>
 __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos, uint32_t who, uint32_t epoch,
                                               bool sum_tail)
 {
-    static_assert(C::EW == 0, "every wave loads stages");
+    // the stream kernel: waves 0..LW-1 load stages, the others stream the sum
+    constexpr bool SPLIT = C::EW > 0;
+    static_assert(!SPLIT || (FUSED && VAR == 0), "the stream kernel is a fused kernel");
     const int Ctot = a.num_compute;
+    const int wave = uni((int)(threadIdx.x >> 6));
+    const bool loader = !SPLIT || wave < C::LW;
     StepHooks hk;
     hk.stores = false;
     hk.pend_q = -1;
@@ -988,24 +1330,40 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     hk.epoch = epoch;
     TileState<C> st;
     TileJob<C> job;
+    Stream sm;
+    if constexpr (SPLIT) stream_init(sm, a, lds + C::LDS_BYTES, pos, loader ? 0 : wave - C::LW, Ctot, epoch);
     int q = pos;
     TileCoord t;
     if (q < a.g.tiles) {
         t = decode_slot(a.g, q);
-        tile_prologue<C>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
+        if (loader)
+            tile_prologue<C>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN, tile_cols(a.g, t));
+        else
+            tile_prologue<C, false>(a, lds, job, tile_row0(a.g, t), tile_rows(a.g, t), t.tn * C::BN,
+                                    tile_cols(a.g, t));
     }
     while (q < a.g.tiles) {
-        if constexpr (C::XP)
+        if constexpr (SPLIT) {
+            if (loader)
+                tile_kloop_split<C, false>(a, lds, st, job, hk, sm);
+            else
+                tile_kloop_split<C, true>(a, lds, st, job, hk, sm);
+        } else if constexpr (C::XP) {
             tile_kloop_xp<C, (VAR & kVarRows) != 0>(a, lds, st, job, hk);
-        else
+        } else {
             tile_kloop<C, (VAR & kVarRows) != 0>(a, lds, st, job, hk);
+        }
         // issue the next tile's first stages before this tile's stores
         const int qn = q + Ctot;
         TileCoord tn = t;
         if (qn < a.g.tiles) {
             tn = decode_slot(a.g, qn);
-            tile_prologue<C>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
-                             tile_cols(a.g, tn));
+            if (loader)
+                tile_prologue<C>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
+                                 tile_cols(a.g, tn));
+            else
+                tile_prologue<C, false>(a, lds, job, tile_row0(a.g, tn), tile_rows(a.g, tn), tn.tn * C::BN,
+                                        tile_cols(a.g, tn));
         }
         // the stage buffer the next tile's prologue left free holds the
         // epilogue staging areas
@@ -1026,7 +1384,25 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         stage_barrier();
         if (threadIdx.x == 0) publish<(VAR & kVarRows) != 0>(a, hk.pend_q, hk.pend_flag, who, epoch);
     }
-    if (sum_tail) {
+    if constexpr (SPLIT) {
+        // the stream waves settle their loads in flight; the items they have
+        // not finished (an item begun restarts) are split between each stream
+        // wave and the loader wave on its SIMD
+        __shared__ int s_progress[C::EW];
+        if (!loader) {
+            stream_settle(sm, a);
+            if ((threadIdx.x & 63) == 0) s_progress[wave - C::LW] = sm.first + (sm.consumed >> 2);
+        }
+        __syncthreads();
+        const int sw = wave % C::EW, half = wave / C::EW;
+        const int64_t n = sm.m.nitems;
+        const int end = stream_bound(n, pos * C::EW + sw + 1, C::EW * Ctot);
+        const int cur = uni(s_progress[sw]);
+        const int mid = cur + (end - cur) / 2;
+        ItemMap m = sm.m;
+        m.nitems = half ? end : mid;
+        drain_items<2>(a, m, half ? mid : cur, 1, epoch);
+    } else if (sum_tail) {
         // every wave sums a share of the slice after its last tile (sixteen
         // items in flight per CU for the eight-wave and one-per-CU tiles; one
         // per wave for four-wave tiles at two per CU, whose shapes leave about

@@ -44,7 +44,8 @@ TILES = {"auto": 0, "16x64": 1, "64x128": 2, "128x128": 3, "128x256": 4, "256x12
 REDUCE_AUTO = 0
 REDUCE_TAIL = 1
 REDUCE_CORESIDENT = 2
-REDUCE_MODES = {"auto": 0, "tail": 1, "coresident": 2}
+REDUCE_STREAM = 3
+REDUCE_MODES = {"auto": 0, "tail": 1, "coresident": 2, "stream": 3}
 
 STORES_DEVICE = 0
 STORES_NONTEMPORAL = 1

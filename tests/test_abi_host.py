@@ -85,9 +85,18 @@ def cfg(**kw):
     (dict(tile_stores="nt", flag_protocol="row_counter"), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt", reduce_mode="coresident"), gr.OK),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode=3), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=4), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="coresident"), gr.OK),
     (dict(reduce_mode="coresident", num_reducers=8), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream"), gr.OK),                                   # 256x256 tile
+    (dict(reduce_mode="stream", K_local=384), gr.OK),
+    (dict(reduce_mode="stream", K_local=320), gr.ERR_UNSUPPORTED_SHAPE),   # too few K steps
+    (dict(reduce_mode="stream", tile="128x128"), gr.ERR_UNSUPPORTED_SHAPE),
+    (dict(reduce_mode="stream", M=512, K_local=1024), gr.ERR_UNSUPPORTED_SHAPE),  # o_proj: 64x128
+    (dict(reduce_mode="stream", num_reducers=8), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream", num_reducers=-2), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream", tile_stores="nt"), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="stream", flag_protocol="row_counter"), gr.ERR_INVALID_ARG),
     (dict(reduce_mode=-1), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="tail"), gr.OK),
     (dict(M=0), gr.OK),
@@ -145,6 +154,7 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
     (dict(), gr.REDUCE_TAIL),                        # automatic: the sum after the last tile
     (dict(reduce_mode="tail"), gr.REDUCE_TAIL),
     (dict(reduce_mode="coresident"), gr.REDUCE_CORESIDENT),
+    (dict(reduce_mode="stream"), gr.REDUCE_STREAM),
     (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
     (dict(M=512, K_local=1024), gr.REDUCE_TAIL),     # o_proj: 64x128 tile
 ])
