@@ -394,7 +394,6 @@ __device__ __forceinline__ void kstep(const LoadPlan<C>& lp, __amdgpu_buffer_rsr
         mfma_substep<C>(st, xf[s & 1], wf[s & 1]);
     }
     constexpr int kMfmas = C::KSUB * C::FM * C::FN;
-    constexpr int kFill = (C::KSUB - 1) * (C::FM + C::FN) + (LOADER ? C::LPS : 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FM + C::FN, 0);
     if constexpr (LOADER) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, C::LPS, 0);
     constexpr int kFillDs = (C::KSUB - 1) * (C::FM + C::FN);
@@ -744,65 +743,81 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
 // the slice sum while all eight run the MFMAs.  Vector-memory operations of a
 // wave retire in issue order, so a wave that waits for its stage loads every
 // K step could not keep an HBM load in flight across steps; a stream wave
-// only ever waits for its own stream operations, so each can stay in flight
-// for kSD steps.
+// only ever waits for its own stream operations.
 //
 // Stream wave w of the TW in the grid owns items [n w / TW, n (w + 1) / TW)
-// and takes them in order, four K steps per item (two loads per step, in the
-// oracle's sum order): peers 0, 1 | peers 2, 3 | peers 4, 5 | peer 6, local.
-// Every step of a stream wave issues exactly kSVm vector-memory
-// instructions, the same whether it has work or not (an idle load reads as
-// zero through an empty buffer resource, an idle store goes past its
-// resource), so that its waits are constants and the step's code has no
-// branch: it is interleaved with the step's MFMAs.  A step:
-//   before its MFMAs: wait until the loads issued kSD steps ago have landed
-//     (kSVm * (kSD - 1) younger instructions, plus the tile's epilogue stores
-//     in the first kSD steps of a tile);
-//   after the barrier: read them from their LDS slot pair, add them to the
-//     running FP32 sum (reset at the item's first step), and at the item's
-//     last step store the rounded sum to out; then issue this step's two loads
-//     into the slot pair read one step earlier (kSD + 1 pairs, so a pair is
-//     refilled only after the step that read it has used the values).
-// Loads carry device scope, so the local slice is read from the memory side,
-// never from a stale line of this XCD's L2.
+// and sums one item per group of four K steps.  Step PH of a group (0..3)
+// issues two device-scope loads of the group's item, in the oracle's sum
+// order: peers 0, 1 | peers 2, 3 | peers 4, 5 | peer 6, local; and consumes
+// the two loads issued two steps earlier (from the previous group at PH 0, 1):
+//   PH 0: acc = (acc + p4) + p5                        (previous item)
+//   PH 1: acc = (acc + p6) + local, stored to out     (previous item)
+//   PH 2: acc = ((0 + p0) + p1)                        (this item)
+//   PH 3: acc = (acc + p2) + p3                        (this item)
+// The stream waves' K loop is unrolled by four, so the sources, the reset,
+// the store and the wait counts are constants of the step's code, which has
+// no branch and is interleaved with the step's MFMAs.  A tile runs the
+// groups only if the workgroup has latched (below) when the tile begins and
+// the wave still has items; other tiles run the plain loop, and a wave whose
+// last item was begun in the previous tile finishes it first.  A group past
+// the wave's last item issues the same instructions through an empty buffer
+// resource (they read zeros) and its store goes past its resource.  Loads land in two 2 KiB LDS slot pairs, pair PH & 1: a step
+// reads the pair of the step two back at its start and refills it once the
+// values are used.  The stream step runs after the step's first substep, not
+// right after the barrier, where the loader waves' refill fills the load
+// queue.  The steps of a
+// tile that do not fill a group run without stream code; the loads of a
+// group's last two steps are consumed in the next group, possibly after the
+// tile's epilogue stores (counted in the waits of a tile's first group).
 //
 // The local partial of an item may be read only once its tile is released.
 // A workgroup's four stream waves own consecutive items, spanning own tiles
-// t_lo .. t_hi; until all of them are released (latched once seen), stream
-// waves issue idle operations.  Loader wave 0 probes the tiles' flags with
-// device-scope loads into LDS right after the barrier of step kProbe - 1,
-// while the workgroup has not latched; the wait of step kProbe covers them,
-// and after its barrier every wave reads the probe and latches together.
-// The previous tile's flag is published after the barrier of step kPub = kSD:
-// the stream waves' epilogue stores are older than the loads that step's wait
-// covers.  Items a stream wave has not finished after the workgroup's last
-// tile are summed there by the stream wave and its SIMD's loader wave.
-constexpr int kSD = 2;                 // steps between a stream load's issue and its use
-constexpr int kSVm = 3;                // vector-memory instructions per stream step
-constexpr int kSPairs = kSD + 1;       // slot pairs per stream wave
-constexpr int kSSlots = 2 * kSPairs;   // 1 KiB LDS slots per stream wave
-constexpr int kSWaveLds = kSSlots * 1024;
+// t_lo .. t_hi; until all of them are released (latched once seen), tiles
+// run the plain loop.  Loader wave 0 probes the tiles' flags with device-scope loads
+// into LDS right after the barrier of step kProbe - 1, while the workgroup
+// has not latched; the wait of step kProbe covers them, and after its
+// barrier every wave reads the probe and latches together.  The previous
+// tile's flag is published after the barrier of step kPub: the stream waves'
+// epilogue stores are older than the loads its wait covers.  Items a stream
+// wave has not finished after the workgroup's last tile are summed there by
+// the stream wave and its SIMD's loader wave.
+constexpr int kSPairLds = 2048;        // two 1 KiB slots
+constexpr int kSWaveLds = 2 * kSPairLds;
 constexpr int kProbeLds = 256;         // 64 flags
 constexpr int kProbe = 4;              // step whose barrier certifies the probe
-constexpr int kPub = kSD;              // step whose barrier publishes the previous tile's flag
+constexpr int kPub = 2;                // step whose barrier publishes the previous tile's flag
 constexpr int kStreamLds = 4 * kSWaveLds + kProbeLds;
 
 struct Stream {
-    char* slots;          // this wave's kSSlots 1 KiB LDS slots
+    char* slots;          // this wave's two slot pairs
     const char* probe;    // the workgroup's probe area (one flag per lane)
     ItemMap m;
     int first, end;       // this wave's item range
-    int issued;           // steps that issued real loads: next item first + issued / 4, part issued % 4
-    int consumed;         // real steps consumed
-    uint32_t rbits;       // bit k: the step k + 1 back issued real loads
-    int it;               // steps run (the loads of step i go to slot pair i % kSPairs)
+    int item;             // next item to begin
+    int real_cur;         // this group's loads are real (its item exists and is released)
+    int real_prev;        // the previous group's
+    uint32_t ioff, coff;  // this lane's byte offset of this / the previous group's item (kOob: none)
     bool latched;         // every own tile of the workgroup's items is released
     int t_lo, t_hi;       // own tiles of the workgroup's items (t_hi < t_lo: none)
     uint32_t epoch;
     uint32_t slice_bytes;
-    uint32_t src_lo, src_hi;  // lane l < 8: base address of source l (7 peers, then the local slice)
     f32x8 acc;
 };
+
+// Eight BF16 values to FP32 (exact).
+__device__ __forceinline__ f32x8 widen8(const u32x4& v)
+{
+    f32x8 b;
+    b[0] = bf16_bits_to_f32(v.x & 0xFFFFu);
+    b[1] = bf16_bits_to_f32(v.x >> 16);
+    b[2] = bf16_bits_to_f32(v.y & 0xFFFFu);
+    b[3] = bf16_bits_to_f32(v.y >> 16);
+    b[4] = bf16_bits_to_f32(v.z & 0xFFFFu);
+    b[5] = bf16_bits_to_f32(v.z >> 16);
+    b[6] = bf16_bits_to_f32(v.w & 0xFFFFu);
+    b[7] = bf16_bits_to_f32(v.w >> 16);
+    return b;
+}
 
 // Item range of stream wave gw of tw over n items.
 __device__ __forceinline__ int stream_bound(int64_t n, int gw, int tw) { return (int)(n * gw / tw); }
@@ -823,20 +838,14 @@ __device__ __forceinline__ void stream_init(Stream& s, const Args& a, char* stre
     const int wfirst = stream_bound(n, pos * 4, tw), wend = stream_bound(n, pos * 4 + 4, tw);
     s.t_lo = uni(wfirst >> s.m.ipt_log2);
     s.t_hi = uni(wend > wfirst ? (wend - 1) >> s.m.ipt_log2 : s.t_lo - 1);
-    s.issued = 0;
-    s.consumed = 0;
-    s.rbits = 0;
-    s.it = 0;
+    s.item = s.first;
+    s.real_cur = 0;
+    s.real_prev = 0;
+    s.ioff = kOob;
+    s.coff = kOob;
     s.latched = s.t_hi < s.t_lo;  // nothing to wait for
     s.epoch = (uint32_t)uni((int)epoch);
     s.slice_bytes = a.slice_bytes;
-    const int lane = threadIdx.x & 63;
-    const uint16_t* p = a.dst[a.g.rank];
-#pragma unroll
-    for (int i = 0; i < kPeers; ++i) p = lane == i ? a.peers[i] : p;
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    s.src_lo = (uint32_t)v;
-    s.src_hi = (uint32_t)(v >> 32);
     s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 }
 
@@ -862,106 +871,124 @@ __device__ __forceinline__ void stream_probe_read(Stream& s)
     s.latched = __builtin_amdgcn_ballot_w64(ok) == ~0ull;
 }
 
-// Stream wave, before the step's MFMAs: wait for the loads of the step kSD
-// back (recent: the tile's epilogue stores are younger than them).
-template <int STORES>
-__device__ __forceinline__ void stream_wait(bool recent)
+// A wave-uniform mask the compiler cannot see through: selects written as
+// bit operations on it stay selects (a known 0 / -1 mask would be folded into
+// a select, and a select between expensive values into a branch, which would
+// split the step's code from the MFMAs it is meant to run between).
+__device__ __forceinline__ uint32_t opaque_mask(int cond)
 {
-    if (recent)
-        wait_vmcnt<kSVm * (kSD - 1) + STORES>();
-    else
-        wait_vmcnt<kSVm * (kSD - 1)>();
+    uint32_t m = (uint32_t)uni(cond ? -1 : 0);
+    __asm__("" : "+s"(m));
+    return m;
 }
 
-// Slot pair of the loads issued at step i.
-__device__ __forceinline__ char* stream_pair(const Stream& s, int i)
+__device__ __forceinline__ uint32_t bsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+// This lane's byte offset of item `item`'s chunk (kOob outside the ragged
+// tile or past the last item), branch-free: item_boff with its selects as bit
+// operations.
+__device__ __forceinline__ uint32_t item_boff_nb(const ItemMap& m, const Args& a, int item)
 {
-    return s.slots + (i % kSPairs) * 2048;
+    const uint32_t t = (uint32_t)(item >> m.ipt_log2);
+    const int j = item & ((1 << m.ipt_log2) - 1);
+    const int tml = (int)((__umulhi(t, m.div_m) + t) >> m.div_l);
+    const int tn = (int)t - tml * a.g.tnc;
+    const int row = j * m.rpi;
+    const int trows = min(a.g.bm, a.g.S - tml * a.g.bm);
+    const int tcols = min(a.g.bn, a.g.N - tn * a.g.bn);
+    const uint32_t base = (uint32_t)(tml * a.g.bm + row) * (uint32_t)a.g.N + (uint32_t)(tn * a.g.bn);
+    const uint32_t in_item = opaque_mask(item < m.nitems ? 1 : 0);
+    const uint32_t in_tile = (row + m.lane_row < trows && m.lane_col < tcols) ? ~0u : 0u;
+    return bsel(in_item & in_tile, (base + (uint32_t)m.lane_off) * 2u, kOob);
 }
 
-// Eight BF16 values to FP32 (exact).
-__device__ __forceinline__ f32x8 widen8(const u32x4& v)
+// Stream wave, before the step's MFMAs: wait for the loads of the step two
+// back.  Younger vector-memory instructions: the step one back's two loads,
+// plus the store of a group's step 1 (consumed at steps 2 and 3), plus the
+// previous tile's epilogue stores in a tile's first group (steps 0 and 1).
+template <int PH, int STORES>
+__device__ __forceinline__ void stream_wait(bool first_group)
 {
-    f32x8 b;
-    b[0] = bf16_bits_to_f32(v.x & 0xFFFFu);
-    b[1] = bf16_bits_to_f32(v.x >> 16);
-    b[2] = bf16_bits_to_f32(v.y & 0xFFFFu);
-    b[3] = bf16_bits_to_f32(v.y >> 16);
-    b[4] = bf16_bits_to_f32(v.z & 0xFFFFu);
-    b[5] = bf16_bits_to_f32(v.z >> 16);
-    b[6] = bf16_bits_to_f32(v.w & 0xFFFFu);
-    b[7] = bf16_bits_to_f32(v.w >> 16);
-    return b;
+    constexpr int kYoung = (PH == 0 || PH == 1) ? 2 : 3;
+    if constexpr (PH <= 1) {
+        if (first_group)
+            wait_vmcnt<kYoung + STORES>();
+        else
+            wait_vmcnt<kYoung>();
+    } else {
+        wait_vmcnt<kYoung>();
+    }
 }
 
-// Stream wave, after the barrier: add the fetched loads (if they were real) to
-// the running sum, store it at the item's last step (else an idle store), then
-// issue this step's loads into the slots just read.  Branch-free.
-__device__ __forceinline__ void stream_step(Stream& s, const Args& a)
+// Stream wave, at the start of a step (after stream_wait): read the loads of
+// the step two back (pair PH & 1); stream_step uses them before it refills
+// the pair.
+template <int PH>
+__device__ __forceinline__ void stream_read(const Stream& s, u32x4& va, u32x4& vb)
 {
-    // consume the loads of step it - kSD
-    const char* cpair = stream_pair(s, s.it + kSPairs - kSD) + (threadIdx.x & 63) * 16;
-    const u32x4 va = *reinterpret_cast<const u32x4*>(cpair);
-    const u32x4 vb = *reinterpret_cast<const u32x4*>(cpair + 1024);
-    const bool real_c = (s.rbits >> (kSD - 1)) & 1u;
-    const int part_c = s.consumed & 3;
-    const int item_c = s.first + (s.consumed >> 2);
-    const f32x8 z = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x8 base = part_c == 0 ? z : s.acc;
-    const f32x8 sum = (base + widen8(va)) + widen8(vb);
-    s.acc = real_c ? sum : s.acc;
-    const bool last = real_c && part_c == 3;
-    const uint32_t soff = last ? item_boff(s.m, a, item_c) : kOob;
-    __builtin_amdgcn_raw_buffer_store_b128(pack8(s.acc), __builtin_amdgcn_make_buffer_rsrc(a.out, 0, s.slice_bytes, kRsrcFlags),
-                                           soff, 0, kAuxNt);
-    s.consumed += real_c ? 1 : 0;
-    // issue
-    const int part = s.issued & 3;
-    const int item = s.first + (s.issued >> 2);
-    const bool real = s.latched && item < s.end;
-    const uint32_t boff = real ? item_boff(s.m, a, item) : kOob;
-    const int sa = 2 * part, sb = part < 3 ? 2 * part + 1 : kPeers;
-    const uint64_t pa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)s.src_hi, sa) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)s.src_lo, sa);
-    const uint64_t pb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)s.src_hi, sb) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)s.src_lo, sb);
-    const uint32_t nrec = real ? s.slice_bytes : 0u;
-    char* pair = stream_pair(s, s.it);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pa), 0, nrec, kRsrcFlags), (lds_void_t*)pair, 16,
-        boff, 0, 0, kAuxSc1 | kAuxNt);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pb), 0, nrec, kRsrcFlags),
-        (lds_void_t*)(pair + 1024), 16, boff, 0, 0, kAuxSc1 | kAuxNt);
-    s.issued += real ? 1 : 0;
-    s.rbits = ((s.rbits << 1) | (real ? 1u : 0u)) & ((1u << kSD) - 1u);
-    ++s.it;
+    const char* pair = s.slots + (PH & 1) * kSPairLds + (threadIdx.x & 63) * 16;
+    va = *reinterpret_cast<const u32x4*>(pair);
+    vb = *reinterpret_cast<const u32x4*>(pair + 1024);
 }
 
-// Stream wave, after its last tile: wait for everything in flight and consume
-// the kSD steps not yet consumed (stores of items they complete included).
-__device__ __forceinline__ void stream_settle(Stream& s, const Args& a)
+// Stream wave, after the first substep of step PH of a group: begin the group
+// (PH 0), consume the loads read at the step's start, issue the step's two
+// loads into the same pair PH & 1, store the previous item (PH 1).
+template <int PH>
+__device__ __forceinline__ void stream_step(Stream& s, const Args& a, const u32x4& va, const u32x4& vb)
 {
-    wait_vmcnt<0>();
-#pragma unroll 1
-    for (int k = 0; k < kSD; ++k) {
-        const char* pair = stream_pair(s, s.it + kSPairs - kSD) + (threadIdx.x & 63) * 16;
-        const u32x4 va = *reinterpret_cast<const u32x4*>(pair);
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(pair + 1024);
-        const bool real_c = (s.rbits >> (kSD - 1)) & 1u;
-        const int part_c = s.consumed & 3;
-        const int item_c = s.first + (s.consumed >> 2);
+    if constexpr (PH == 0) {
+        const int item = uni(s.item);
+        const int real = (s.latched ? 1 : 0) & (item < s.end ? 1 : 0);
+        s.real_prev = s.real_cur;
+        s.real_cur = uni(real);
+        s.coff = s.ioff;
+        s.ioff = item_boff_nb(s.m, a, item);
+        s.item = item + real;
+    }
+    // consume (an idle step's loads read zeros and leave the sum as it is)
+    const f32x8 wa = widen8(va), wb = widen8(vb);
+    if constexpr (PH == 2) {
         const f32x8 z = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        const f32x8 sum = ((part_c == 0 ? z : s.acc) + widen8(va)) + widen8(vb);
-        s.acc = real_c ? sum : s.acc;
-        const uint32_t soff = real_c && part_c == 3 ? item_boff(s.m, a, item_c) : kOob;
+        s.acc = (z + wa) + wb;
+    } else {
+        s.acc = (s.acc + wa) + wb;
+    }
+    // (the slot pair is refilled below only after its values were used)
+    __builtin_amdgcn_sched_barrier(0);
+    // issue
+    const uint16_t* pa = PH == 0 ? a.peers[0] : PH == 1 ? a.peers[2] : PH == 2 ? a.peers[4] : a.peers[6];
+    const uint16_t* pb = PH == 0 ? a.peers[1] : PH == 1 ? a.peers[3] : PH == 2 ? a.peers[5] : a.dst[a.g.rank];
+    const uint32_t nrec = s.slice_bytes & opaque_mask(s.real_cur);
+    char* pair = s.slots + (PH & 1) * kSPairLds;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)pa, 0, nrec, kRsrcFlags),
+                                             (lds_void_t*)pair, 16, s.ioff, 0, 0, kAuxSc1 | kAuxNt);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)pb, 0, nrec, kRsrcFlags),
+                                             (lds_void_t*)(pair + 1024), 16, s.ioff, 0, 0, kAuxSc1 | kAuxNt);
+    if constexpr (PH == 1) {
+        const uint32_t soff = bsel(opaque_mask(s.real_prev), s.coff, kOob);
         __builtin_amdgcn_raw_buffer_store_b128(pack8(s.acc),
                                                __builtin_amdgcn_make_buffer_rsrc(a.out, 0, s.slice_bytes, kRsrcFlags),
                                                soff, 0, kAuxNt);
-        s.consumed += real_c ? 1 : 0;
-        s.rbits = (s.rbits << 1) & ((1u << kSD) - 1u);
-        ++s.it;
     }
+}
+
+// Stream wave, after its last tile: wait for everything in flight, then
+// finish the last group (its steps 2 and 3 were never consumed) and store its
+// item if it was real.
+__device__ __forceinline__ void stream_settle(Stream& s, const Args& a)
+{
+    wait_vmcnt<0>();
+    const int lane16 = (threadIdx.x & 63) * 16;
+    const f32x8 w4 = widen8(*reinterpret_cast<const u32x4*>(s.slots + lane16));
+    const f32x8 w5 = widen8(*reinterpret_cast<const u32x4*>(s.slots + 1024 + lane16));
+    const f32x8 w6 = widen8(*reinterpret_cast<const u32x4*>(s.slots + kSPairLds + lane16));
+    const f32x8 wl = widen8(*reinterpret_cast<const u32x4*>(s.slots + kSPairLds + 1024 + lane16));
+    const f32x8 acc = (((s.acc + w4) + w5) + w6) + wl;
+    const uint32_t soff = s.real_cur ? s.ioff : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(pack8(acc), __builtin_amdgcn_make_buffer_rsrc(a.out, 0, s.slice_bytes, kRsrcFlags),
+                                           soff, 0, kAuxNt);
+    s.real_cur = 0;
 }
 
 // ---------------------------------------------------------------- tile loop
@@ -1183,16 +1210,147 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
 // The K loop of a tile in the stream kernel (four loader waves, four stream
 // waves, two stages), pipelined across steps like tile_kloop_xp.  Loader waves
 // wait for their stage loads (and at step 0 for their previous epilogue
-// stores); stream waves wait only for their own stream loads (stream_fetch)
-// and run a stream step where loader waves issue the refill.  The previous
-// tile's flag is published after the barrier of step kPub, the first that
-// certifies the stream waves' epilogue stores (at the tile's end if the loop
-// is shorter).
+// stores) and issue the refill; stream waves issue no stage loads, wait only
+// for their own stream loads, and run the steps of a tile in groups of four
+// (a stream step each), then the remaining steps without stream code.  The
+// previous tile's flag is published after the barrier of step kPub, the first
+// that certifies the stream waves' epilogue stores (at the tile's end if the
+// loop is shorter).
+template <class C>
+struct SplitLoop {
+    static_assert(C::KSUB % 2 == 0 && C::NS == 2 && C::WAVES == 8 && C::LW == 4, "stream kernel tile");
+    static constexpr int kMf = C::FM * C::FN;   // MFMAs per substep
+    static constexpr int kDs = C::FM + C::FN;   // fragment reads per substep
+
+    // Substeps 0 .. KSUB-2 of step kt (MFMAs with the next substep's
+    // fragment reads between them).
+    static __device__ __forceinline__ void head(TileState<C>& st, const char* cur, bf16x8 (&xf)[2][C::FM],
+                                                bf16x8 (&wf)[2][C::FN])
+    {
+#pragma unroll
+        for (int ss = 0; ss + 1 < C::KSUB; ++ss) {
+            load_frags<C>(cur, ss + 1, xf[(ss + 1) & 1], wf[(ss + 1) & 1]);
+            mfma_substep<C>(st, xf[ss & 1], wf[ss & 1]);
+        }
+#pragma unroll
+        for (int ss = 0; ss + 1 < C::KSUB; ++ss)
+#pragma unroll
+            for (int m = 0; m < kMf; ++m) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+    }
+
+    // After the barrier of step kt: the flag publish and the readiness probe.
+    static __device__ __forceinline__ void control(const Args& a, StepHooks& hk, Stream& s, int kt, bool prober)
+    {
+        if (kt == kPub) publish_pending<false>(a, hk);
+        if (!s.latched) {
+            if (kt == kProbe - 1 && prober) stream_probe_issue(s, a);
+            if (kt == kProbe) stream_probe_read(s);
+        }
+    }
+
+    // The last substep of step kt and the next step's first fragments.
+    static __device__ __forceinline__ void tail(TileState<C>& st, const char* lds, int kt, bf16x8 (&xf)[2][C::FM],
+                                                bf16x8 (&wf)[2][C::FN])
+    {
+        load_frags<C>(lds + ((kt + 1) & 1) * C::STAGE_BYTES, 0, xf[0], wf[0]);
+        mfma_substep<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1]);
+    }
+
+    // One step of a stream wave with stream phase PH.  The stream step runs
+    // after the step's first substep, away from the barrier, where the loader
+    // waves' refill (issued right after it) has left the load queue.
+    template <int PH>
+    static __device__ __forceinline__ void stream_step_k(const Args& a, char* lds, TileState<C>& st, StepHooks& hk,
+                                                         Stream& s, int kt, bool first_group,
+                                                         bf16x8 (&xf)[2][C::FM], bf16x8 (&wf)[2][C::FN])
+    {
+        stream_wait<PH, C::STORES>(first_group);
+        u32x4 va, vb;
+        stream_read<PH>(s, va, vb);
+        const char* cur = lds + (kt & 1) * C::STAGE_BYTES;
+        load_frags<C>(cur, 1, xf[1], wf[1]);
+        mfma_substep<C>(st, xf[0], wf[0]);
+#pragma unroll
+        for (int m = 0; m < kMf; ++m) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stream_step<PH>(s, a, va, vb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ss = 1; ss + 1 < C::KSUB; ++ss) {
+            load_frags<C>(cur, ss + 1, xf[(ss + 1) & 1], wf[(ss + 1) & 1]);
+            mfma_substep<C>(st, xf[ss & 1], wf[ss & 1]);
+        }
+#pragma unroll
+        for (int ss = 1; ss + 1 < C::KSUB; ++ss)
+#pragma unroll
+            for (int m = 0; m < kMf; ++m) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+        wait_lgkm0();
+        stage_barrier();
+        control(a, hk, s, kt, false);
+        tail(st, lds, kt, xf, wf);
+#pragma unroll
+        for (int m = 0; m < kMf; ++m) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+    }
+
+    // One step of a stream wave without stream code.
+    static __device__ __forceinline__ void plain_step(const Args& a, char* lds, TileState<C>& st, StepHooks& hk,
+                                                      Stream& s, int kt, bf16x8 (&xf)[2][C::FM],
+                                                      bf16x8 (&wf)[2][C::FN])
+    {
+        head(st, lds + (kt & 1) * C::STAGE_BYTES, xf, wf);
+        wait_lgkm0();
+        stage_barrier();
+        control(a, hk, s, kt, false);
+        tail(st, lds, kt, xf, wf);
+#pragma unroll
+        for (int m = 0; m < kMf; ++m) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+    }
+
+    // One step of a loader wave: wait for the stage, refill, compute.
+    static __device__ __forceinline__ void loader_step(const Args& a, char* lds, TileState<C>& st, StepHooks& hk,
+                                                       Stream& s, const TileJob<C>& job, __amdgpu_buffer_rsrc_t rx,
+                                                       __amdgpu_buffer_rsrc_t rw, int kt, bool prober,
+                                                       bf16x8 (&xf)[2][C::FM], bf16x8 (&wf)[2][C::FN])
+    {
+        head(st, lds + (kt & 1) * C::STAGE_BYTES, xf, wf);
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        stage_barrier();
+        control(a, hk, s, kt, prober);
+        __builtin_amdgcn_s_setprio(1);
+        issue_stage<C>(job.lp, rx, rw, lds + (kt & 1) * C::STAGE_BYTES, (kt + 2) * C::BK, a.g.K);
+        tail(st, lds, kt, xf, wf);
+        // the refill's loads, two per MFMA, then the next step's first fragments
+#pragma unroll
+        for (int m = 0; m < kMf; ++m) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (2 * m < C::LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+            if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    }
+};
+
 template <class C, bool STREAMER>
 __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
                                                  StepHooks& hk, Stream& s)
 {
-    static_assert(C::KSUB % 2 == 0 && C::NS == 2 && C::WAVES == 8 && C::LW == 4, "stream kernel tile");
+    typedef SplitLoop<C> L;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -1200,76 +1358,40 @@ __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileS
 #pragma unroll
             for (int e = 0; e < AccT<C::MF>::N; ++e) st.acc[i][j][e] = 0.0f;
 
-    const int K = a.g.K;
     const int nk = job.nk;
-    constexpr int kMf = C::FM * C::FN;   // MFMAs per substep
-    constexpr int kDs = C::FM + C::FN;   // fragment reads per substep
     const int wave = uni((int)(threadIdx.x >> 6));
     if (nk > 0) {
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
         bf16x8 xf[2][C::FM], wf[2][C::FN];
-        // stage 0 came from the prologue, before the previous tile's stores
         if constexpr (!STREAMER) {
+            const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
+            // stage 0 came from the prologue, before the previous tile's stores
             if (hk.stores)
                 wait_vmcnt<C::STORES>();
             else
                 wait_vmcnt<0>();
-        }
-        stage_barrier();
-        if constexpr (!STREAMER) issue_stage<C>(job.lp, rx, rw, lds + C::STAGE_BYTES, C::BK, K);
-        load_frags<C>(lds, 0, xf[0], wf[0]);
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            const char* cur = lds + (kt & 1) * C::STAGE_BYTES;
-            if constexpr (STREAMER) stream_wait<C::STORES>(kt < kSD);
-#pragma unroll
-            for (int ss = 0; ss + 1 < C::KSUB; ++ss) {
-                load_frags<C>(cur, ss + 1, xf[(ss + 1) & 1], wf[(ss + 1) & 1]);
-                mfma_substep<C>(st, xf[ss & 1], wf[ss & 1]);
-            }
-#pragma unroll
-            for (int ss = 0; ss + 1 < C::KSUB; ++ss)
-#pragma unroll
-                for (int m = 0; m < kMf; ++m) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                }
-            if constexpr (!STREAMER) wait_vmcnt<0>();
-            wait_lgkm0();
             stage_barrier();
-            if (kt == kPub) publish_pending<false>(a, hk);
-            if (!s.latched) {
-                if (kt == kProbe - 1 && !STREAMER && wave == 0) stream_probe_issue(s, a);
-                if (kt == kProbe) stream_probe_read(s);
+            issue_stage<C>(job.lp, rx, rw, lds + C::STAGE_BYTES, C::BK, a.g.K);
+            load_frags<C>(lds, 0, xf[0], wf[0]);
+            for (int kt = 0; kt + 1 < nk; ++kt) L::loader_step(a, lds, st, hk, s, job, rx, rw, kt, wave == 0, xf, wf);
+        } else {
+            // a tile runs the stream's groups only while this wave has items
+            // to sum and the slice's tiles are ready; otherwise the plain
+            // loop, after finishing an item begun in the previous tile
+            const bool active = s.latched && s.item < s.end;
+            if (!active && s.real_cur) stream_settle(s, a);
+            stage_barrier();
+            load_frags<C>(lds, 0, xf[0], wf[0]);
+            int kt = 0;
+            if (active)
+            for (; kt + 4 < nk; kt += 4) {
+                const bool first = kt == 0;
+                L::template stream_step_k<0>(a, lds, st, hk, s, kt, first, xf, wf);
+                L::template stream_step_k<1>(a, lds, st, hk, s, kt + 1, first, xf, wf);
+                L::template stream_step_k<2>(a, lds, st, hk, s, kt + 2, first, xf, wf);
+                L::template stream_step_k<3>(a, lds, st, hk, s, kt + 3, first, xf, wf);
             }
-            __builtin_amdgcn_s_setprio(1);
-            if constexpr (STREAMER)
-                stream_step(s, a);
-            else
-                issue_stage<C>(job.lp, rx, rw, lds + (kt & 1) * C::STAGE_BYTES, (kt + 2) * C::BK, K);
-            load_frags<C>(lds + ((kt + 1) & 1) * C::STAGE_BYTES, 0, xf[0], wf[0]);
-            mfma_substep<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1]);
-            if constexpr (STREAMER) {
-                // the stream step's arithmetic, its loads and store and the
-                // next step's first fragments spread over the MFMAs
-#pragma unroll
-                for (int m = 0; m < kMf; ++m) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-                    if (m < kSVm) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead | kSchedVmemWrite, 1, 0);
-                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                }
-            } else {
-                // the refill's loads, two per MFMA, then the next step's
-                // first fragments
-#pragma unroll
-                for (int m = 0; m < kMf; ++m) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    if (2 * m < C::LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
-                    if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                }
-            }
-            __builtin_amdgcn_s_setprio(0);
+            for (; kt + 1 < nk; ++kt) L::plain_step(a, lds, st, hk, s, kt, xf, wf);
         }
         // the last step
         const char* cur = lds + ((nk - 1) & 1) * C::STAGE_BYTES;
@@ -1391,7 +1513,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         __shared__ int s_progress[C::EW];
         if (!loader) {
             stream_settle(sm, a);
-            if ((threadIdx.x & 63) == 0) s_progress[wave - C::LW] = sm.first + (sm.consumed >> 2);
+            if ((threadIdx.x & 63) == 0) s_progress[wave - C::LW] = sm.item;
         }
         __syncthreads();
         const int sw = wave % C::EW, half = wave / C::EW;
