@@ -101,7 +101,10 @@ extern "C" {
 #define GEMM_RS_TILE_COUNT 7
 
 /* ---- where the slice sum runs without dedicated reducers ------------------ */
-#define GEMM_RS_REDUCE_AUTO 0   /* TAIL                                             */
+#define GEMM_RS_REDUCE_AUTO 0   /* STREAM for the 256x256 tile with K_local >= 384
+                                   and at least 768 tiles (three rounds of a
+                                   256-CU device) unless num_reducers is -2;
+                                   TAIL otherwise                                 */
 #define GEMM_RS_REDUCE_TAIL 1   /* each compute workgroup sums its share of the
                                    slice after its last tile                      */
 #define GEMM_RS_REDUCE_CORESIDENT 2 /* one reducer workgroup per CU beside the
@@ -118,8 +121,9 @@ extern "C" {
                                    load in flight for three steps) once the
                                    workgroup's own tiles are released; the rest
                                    is summed after the last tile.  Tile flags and
-                                   device-scope stores only; not with the
-                                   all-reduce's FUSED runs                        */
+                                   device-scope stores only.  The all-reduce's
+                                   FUSED runs on such a handle sum after the last
+                                   tile (TAIL)                                    */
 
 /* ---- cache policy of the routed tile stores ------------------------------ */
 #define GEMM_RS_STORES_DEVICE 0      /* device scope, written through L2        */

@@ -95,7 +95,8 @@ TileDesc desc()
     const void* sk = nullptr;
     int slds = 0;
     if constexpr (!std::is_void<CS>::value) {
-        static_assert(CS::LDS_BYTES == C::LDS_BYTES && CS::LDS_BYTES + kStreamLds <= 160 * 1024 - 256,
+        static_assert(CS::LDS_BYTES == C::LDS_BYTES && CS::THREADS == C::THREADS &&
+                          CS::LDS_BYTES + kStreamLds <= 160 * 1024 - 256,
                       "the stream kernel's LDS");
         sk = reinterpret_cast<const void*>(&fused_kernel_8w<CS, true>);
         slds = CS::LDS_BYTES + kStreamLds;
@@ -141,10 +142,23 @@ int auto_tile(const gemm_rs_config& c)
 int resolve_tile(const gemm_rs_config& c) { return c.tile == GEMM_RS_TILE_AUTO ? auto_tile(c) : c.tile; }
 
 // Where the slice sum of a fused run without dedicated reducers runs.
+// AUTO: the stream where it can run beside the GEMM: the 256x256 tile, at
+// least kProbe + 2 K steps, and three or more rounds of tiles on a 256-CU
+// device (768 tiles; the own slice, an eighth of them, is released during the
+// first rounds and the stream runs in the later ones).  Otherwise the sum after
+// the last tile.
+constexpr int kAutoStreamTiles = 3 * 256;
+
 int resolve_reduce_mode(const gemm_rs_config& c)
 {
     if (c.num_reducers > 0) return GEMM_RS_REDUCE_TAIL;
-    if (c.reduce_mode == GEMM_RS_REDUCE_AUTO) return GEMM_RS_REDUCE_TAIL;
+    if (c.reduce_mode == GEMM_RS_REDUCE_AUTO) {
+        if (c.num_reducers == -2 || resolve_tile(c) != GEMM_RS_TILE_256x256 || c.K_local < (kProbe + 2) * 64)
+            return GEMM_RS_REDUCE_TAIL;
+        const int64_t S = c.M / c.tp;
+        const int64_t tiles = (int64_t)c.tp * ((S + 255) / 256) * (((int64_t)c.N + 255) / 256);
+        return tiles >= kAutoStreamTiles ? GEMM_RS_REDUCE_STREAM : GEMM_RS_REDUCE_TAIL;
+    }
     return c.reduce_mode;
 }
 
@@ -178,6 +192,10 @@ struct gemm_rs_handle {
     int wgs_per_cu;
     int fused_lds;
     int gemm_grid;         // workgroups of a GEMM-only launch
+    // a STREAM handle's all-reduce runs: the tile's kernel summing after the
+    // last tile (the stream stores only into `out`)
+    const void* tail_kernel;
+    int tail_lds;
     // all-gather + GEMM runs
     uint32_t* agflags;     // tp * tile rows per slice copy counters
     uint32_t* agfinished;  // per workgroup of ag_grid
@@ -473,6 +491,11 @@ static int plan_launch(gemm_rs_handle* h, const gemm_rs_config* c, int dev, int 
     const int red_req = c->num_reducers < 0 ? 0 : c->num_reducers;
     h->reduce_mode = resolve_reduce_mode(*c);
     h->fused_lds = h->td.fused_lds_bytes;
+    {
+        const TileDesc base = tile_desc(h->tile_id);
+        h->tail_kernel = base.kernel;
+        h->tail_lds = base.lds_bytes;
+    }
     // the persistent grid holds the workgroups per CU the kernel was built for
     // (more would share a SIMD's registers between more waves than planned)
     h->wgs_per_cu = occ < 1 ? 1 : (occ > h->td.wgs_per_cu ? h->td.wgs_per_cu : occ);
@@ -513,8 +536,13 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_RS_ERR_NO_DEVICE;
 
     int variant = 0, occ = 0;
-    rc = kernel_setup(variant_desc(*c, &variant), &occ);
+    const TileDesc vd = variant_desc(*c, &variant);
+    rc = kernel_setup(vd, &occ);
     if (rc != GEMM_RS_OK) return rc;
+    if (variant == 3) {
+        const TileDesc base = tile_desc(resolve_tile(*c));
+        HIP_TRY(hipFuncSetAttribute(base.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, base.lds_bytes));
+    }
     gemm_rs_handle* h = new (std::nothrow) gemm_rs_handle();
     if (!h) return GEMM_RS_ERR_NO_MEMORY;
     rc = plan_launch(h, c, dev, prop.multiProcessorCount, occ);
@@ -630,7 +658,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.coresident = h->reduce_mode == GEMM_RS_REDUCE_CORESIDENT ? 1 : 0;
 }
 
-static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
+static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s, bool tail = false)
 {
     // adaptive split: time the candidates on the first uncaptured fused runs
     int timed = -1;
@@ -656,13 +684,13 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s)
     // GEMM_ONLY has no reducers, so its groups always split evenly
     if (!fused) a.strided = h->strided;
     void* params[] = {&a};
-    const void* k = fused ? h->td.kernel : h->td.gemm_kernel;
+    const void* k = fused ? (tail ? h->tail_kernel : h->td.kernel) : h->td.gemm_kernel;
     // (a GEMM-only launch runs on the compute workgroups' grid: the
     // co-resident reducers' extra workgroup per CU is not part of the GEMM)
     if (!fused) a.num_compute = h->gemm_grid;
     if (timed >= 0) HIP_TRY(hipEventRecord(h->split.ev[timed][0], s));
     HIP_TRY(hipLaunchKernel(k, dim3(fused ? h->grid : h->gemm_grid), dim3(h->td.threads), params,
-                            fused ? h->fused_lds : h->td.lds_bytes, s));
+                            fused ? (tail ? h->tail_lds : h->fused_lds) : h->td.lds_bytes, s));
     if (timed >= 0) HIP_TRY(hipEventRecord(h->split.ev[timed][1], s));
     return GEMM_RS_OK;
 }
@@ -727,7 +755,11 @@ static int launch_run(gemm_rs_handle* h, int32_t mode, const void* x, const void
     if (status) a.status = status;
     int rc = GEMM_RS_OK;
     switch (mode) {
-    case GEMM_RS_MODE_FUSED: rc = launch_gemm(h, a, true, s); break;
+    case GEMM_RS_MODE_FUSED:
+        // (the all-reduce's sum also stores every gather buffer: on a STREAM
+        // handle it runs after the last tile)
+        rc = launch_gemm(h, a, true, s, needs_sum && gather && h->reduce_mode == GEMM_RS_REDUCE_STREAM);
+        break;
     case GEMM_RS_MODE_GEMM_ONLY: rc = launch_gemm(h, a, false, s); break;
     case GEMM_RS_MODE_REDUCE_ONLY: rc = launch_reduce(h, a, s); break;
     case GEMM_RS_MODE_SEQUENTIAL:
@@ -764,9 +796,6 @@ int gemm_rs_run_allreduce(gemm_rs_handle* h, int32_t mode, const void* x, const 
                           void* stream)
 {
     if (mode != GEMM_RS_MODE_GEMM_ONLY && !gather) return GEMM_RS_ERR_INVALID_ARG;
-    // the stream kernel's sum stores into `out` only
-    if (h && mode == GEMM_RS_MODE_FUSED && h->reduce_mode == GEMM_RS_REDUCE_STREAM)
-        return GEMM_RS_ERR_UNSUPPORTED_SHAPE;
     return run_impl(h, mode, x, w, send, peers, out, local_slice, gather, stream);
 }
 

@@ -157,6 +157,15 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
     (dict(reduce_mode="stream"), gr.REDUCE_STREAM),
     (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
     (dict(M=512, K_local=1024), gr.REDUCE_TAIL),     # o_proj: 64x128 tile
+    # automatic: the stream from 768 tiles of 256x256 (three rounds of 256 CUs)
+    (dict(M=8192, N=6144, K_local=2048), gr.REDUCE_STREAM),          # 768 tiles
+    (dict(M=32768, N=8192, K_local=3584), gr.REDUCE_STREAM),
+    (dict(M=8192, N=5888, K_local=2048), gr.REDUCE_TAIL),            # 736 tiles
+    (dict(M=8192, N=6144, K_local=320), gr.REDUCE_TAIL),             # five K steps
+    (dict(M=8192, N=6144, K_local=2048, num_reducers=-2), gr.REDUCE_TAIL),  # adaptive split
+    (dict(M=8192, N=6144, K_local=2048, num_reducers=8), gr.REDUCE_TAIL),
+    (dict(M=8192, N=6144, K_local=2048, tile="128x128"), gr.REDUCE_TAIL),
+    (dict(M=8192, N=6144, K_local=2048, reduce_mode="tail"), gr.REDUCE_TAIL),
 ])
 def test_plan_resolves_reduce_mode(kw, mode):
     assert gr.gemm_rs_plan(cfg(**kw)).reduce_mode == mode

@@ -138,7 +138,10 @@ def test_stream_watchdog_reports_a_dropped_flag():
     assert np.array_equal(got[mask], out_o[mask])
 
 
-def test_stream_modes_agree_and_all_reduce_is_refused():
+def test_stream_modes_agree_and_all_reduce_sums_after_the_last_tile():
+    """FUSED equals SEQUENTIAL on a stream handle; the all-reduce's FUSED run
+    on the same handle (whose sum also stores every gather buffer) runs the
+    sum after the last tile and gives the same slice in out and in gather[]."""
     cfg = SHAPES["two_rounds"]
     x, w, peers = synthetic.make_inputs(cfg, "integer")
     op = _op(cfg, 1, **STREAM)
@@ -149,7 +152,16 @@ def test_stream_modes_agree_and_all_reduce_is_refused():
     run(op, b, gr.MODE_SEQUENTIAL)
     for i, t in enumerate(b.send + [b.local, b.out]):
         assert np.array_equal(host(t), fused[i]), i
-    g = [torch.zeros((cfg.S, cfg.N), dtype=torch.int16, device="cuda") for _ in range(7)]
-    with pytest.raises(gr.GemmRSError) as e:
-        op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local, gather=g)
-    assert e.value.code == gr.ERR_UNSUPPORTED_SHAPE
+    b.refill()
+    g = [torch.full((cfg.S, cfg.N), SENTINEL, dtype=torch.int16, device="cuda") for _ in range(7)]
+    op.run(gr.MODE_FUSED, b.x, b.w, b.send, b.peers, b.out, b.local, gather=g)
+    torch.cuda.synchronize()
+    assert op.status() == 0
+    for i, t in enumerate(b.send + [b.local, b.out]):
+        assert np.array_equal(host(t), fused[i]), i
+    for i, t in enumerate(g):
+        assert np.array_equal(host(t), fused[-1]), i
+    # and the stream kernel again after it
+    b.refill()
+    run(op, b, gr.MODE_FUSED)
+    assert np.array_equal(host(b.out), fused[-1])
