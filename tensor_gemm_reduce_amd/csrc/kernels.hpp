@@ -324,6 +324,57 @@ __device__ __forceinline__ void issue_stage(const LoadPlan<C>& lp, __amdgpu_buff
             0, 0, 0);
 }
 
+// The last substep of an XP step after its barrier, with the refill of the
+// stage buffer just read and the next step's first fragments: MFMA m is
+// followed by direct load m and fragment read m, in that order (scheduling
+// fences hold it; left to the scheduler, the loads bunch together and the
+// fragment reads come last).  The fragments are read in load_frags' order.
+template <class C>
+__device__ __forceinline__ void xp_tail(TileState<C>& st, const bf16x8 (&xl)[C::FM], const bf16x8 (&wl)[C::FN],
+                                        bf16x8 (&xn)[C::FM], bf16x8 (&wn)[C::FN], const char* next,
+                                        const LoadPlan<C>& lp, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                                        char* refill, int k0, int K)
+{
+    constexpr int kMf = C::FM * C::FN, kDs = C::FM + C::FN;
+    constexpr int kSlots = kMf > C::LPS ? kMf : C::LPS;
+    const int wave = uni((int)(threadIdx.x >> 6));
+    // the refill, as in issue_stage
+    const bool in_k = lp.kc < K - k0;
+    const uint32_t a0 = in_k ? lp.a_off + (uint32_t)k0 * 2u : kOob;
+    const uint32_t b0 = in_k ? lp.b_off + (uint32_t)k0 * 2u : kOob;
+    const uint32_t step = (uint32_t)uni((C::LTHREADS / C::CPR) * K * 2);
+    // the fragments, as in load_frags (substep 0)
+    const int lane = threadIdx.x & 63;
+    const int wm = wave / C::WAVES_N, wc = wave % C::WAVES_N;
+    const int lr = lane % C::MF, c = lane / C::MF;
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        if (m < kMf) {
+            const int i = m / C::FN, j = m % C::FN;
+            if constexpr (C::MF == 32)
+                st.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[j], xl[i], st.acc[i][j], 0, 0, 0);
+            else
+                st.acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl[j], xl[i], st.acc[i][j], 0, 0, 0);
+        }
+        if (m < C::A_LD)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(refill + (m * C::LTHREADS + wave * 64) * 16), 16,
+                                                     a0 + (uint32_t)m * step, 0, 0, 0);
+        else if (m < C::LPS)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_void_t*)(refill + C::A_BYTES + ((m - C::A_LD) * C::LTHREADS + wave * 64) * 16), 16,
+                b0 + (uint32_t)(m - C::A_LD) * step, 0, 0, 0);
+        if (m < C::FM) {
+            const int r = wm * C::WTM + m * C::MF + lr;
+            xn[m] = *reinterpret_cast<const bf16x8*>(next + r * C::ROW_BYTES + ((c ^ swz<C::CPR>(r)) << 4));
+        } else if (m < kDs) {
+            const int r = wc * C::WTN + (m - C::FM) * C::MF + lr;
+            wn[m - C::FM] =
+                *reinterpret_cast<const bf16x8*>(next + C::A_BYTES + r * C::ROW_BYTES + ((c ^ swz<C::CPR>(r)) << 4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedAlu = 0x001;
 constexpr int kSchedValu = 0x002;
@@ -1177,18 +1228,9 @@ __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileStat
             // while the wave issues the refill (measured: ~1% faster than
             // without, and than raising it over the MFMA-only part)
             __builtin_amdgcn_s_setprio(1);
-            issue_stage<C>(job.lp, rx, rw, lds + (kt % C::NS) * C::STAGE_BYTES, (kt + C::NS) * C::BK, K);
-            load_frags<C>(lds + ((kt + 1) % C::NS) * C::STAGE_BYTES, 0, xf[0], wf[0]);
-            mfma_substep<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1]);
-            // the refill's loads one per MFMA (any excess first), then the
-            // next step's first fragments
-            if constexpr (C::LPS > kMf) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, C::LPS - kMf, 0);
-#pragma unroll
-            for (int m = 0; m < kMf; ++m) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                if (m < C::LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-                if (m < kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            }
+            xp_tail<C>(st, xf[(C::KSUB - 1) & 1], wf[(C::KSUB - 1) & 1], xf[0], wf[0],
+                       lds + ((kt + 1) % C::NS) * C::STAGE_BYTES, job.lp, rx, rw, lds + (kt % C::NS) * C::STAGE_BYTES,
+                       (kt + C::NS) * C::BK, K);
             __builtin_amdgcn_s_setprio(0);
         }
         // the last step
