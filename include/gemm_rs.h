@@ -124,6 +124,20 @@ extern "C" {
                                    device-scope stores only.  The all-reduce's
                                    FUSED runs on such a handle sum after the last
                                    tile (TAIL)                                    */
+#define GEMM_RS_REDUCE_ADAPTIVE 4 /* every compute workgroup changes role at its
+                                   tile boundaries and sums a share of the slice
+                                   there: each wave owns every (W G)-th 512-
+                                   element item in release order and, at a
+                                   boundary, sums an even share of what it has
+                                   left over the boundaries it has left, limited
+                                   to released rounds and, by its cycle counter,
+                                   to a quarter of a tile's time; the last
+                                   boundary sums the rest (mKernel, "mKernel:
+                                   Fast Multi-GPU, Multi-Node Fused Kernels",
+                                   section 3.2: roles change at task boundaries
+                                   under a target from progress and cost
+                                   counters).  Also selected by num_reducers ==
+                                   -2.  Tile flags and device-scope stores only   */
 
 /* ---- cache policy of the routed tile stores ------------------------------ */
 #define GEMM_RS_STORES_DEVICE 0      /* device scope, written through L2        */
@@ -156,12 +170,10 @@ typedef struct gemm_rs_config {
     int32_t rank;         /* this rank, 0 <= rank < tp                        */
     int32_t tile;         /* GEMM_RS_TILE_*                                   */
     int32_t group_m;      /* tile rows per raster group; 0 = automatic        */
-    int32_t num_reducers; /* reducer workgroups in FUSED mode; -1 = automatic
-                             (none); -2 = adaptive: the first uncaptured FUSED
-                             runs are timed with 0, 8, 16, 32 and 64 dedicated
-                             reducers (two runs each), and once all have
-                             completed the fastest count is kept (results
-                             are identical for every count)                  */
+    int32_t num_reducers; /* dedicated reducer workgroups in FUSED mode (they
+                             sum while the others compute, then stop);
+                             -1 = automatic (none); -2 = the adaptive
+                             controller (GEMM_RS_REDUCE_ADAPTIVE)             */
     int32_t debug_flags;  /* GEMM_RS_DEBUG_* bits                             */
     int32_t drop_flag;    /* debug: index of a ready flag the producer never
                              releases, to exercise the watchdog; -1 = none    */
@@ -195,9 +207,8 @@ typedef struct gemm_rs_info {
                                  (read from the device; waits for the stream) */
     int32_t reduce_mode;      /* resolved GEMM_RS_REDUCE_* of a FUSED run with
                                  no dedicated reducers                        */
-    int32_t split_state;      /* 0: fixed reducer count; 1: adaptive, still
-                                 timing candidates; 2: adaptive, settled on
-                                 reducer_wgs                                  */
+    int32_t split_state;      /* 0: fixed reducer count; 1: the adaptive
+                                 controller decides on the device           */
 } gemm_rs_info;
 
 typedef struct gemm_rs_handle gemm_rs_handle;
@@ -314,8 +325,8 @@ int gemm_rs_run_allgather(gemm_rs_handle *h, int32_t mode, const void *const *x_
  * Every call on one GPU shares that GPU's array: each run first clears it
  * with a small kernel on `stream`, so calls that overlap on one GPU race and
  * must be ordered by the caller (one stream, or synchronisation).
- *   cfg          as for gemm_rs_create; num_reducers == -2 (adaptive) and any
- *                debug_flags are refused (GEMM_RS_ERR_INVALID_ARG).
+ *   cfg          as for gemm_rs_create; any debug_flags are refused
+ *                (GEMM_RS_ERR_INVALID_ARG).
  *   mode, x, w, send, peers, out, stream: as for gemm_rs_run.
  *   local_slice  required (there is no handle scratch): device [S][N].
  *   status       NULL, or a 4-byte aligned device array of 2 int32 that the
@@ -352,6 +363,15 @@ int gemm_rs_query(gemm_rs_handle *h, gemm_rs_info *info);
  *              the compute workgroup's ticket, and the 64-bit release time
  *              (100 MHz counter; low word then high word).  Written only when
  *              the run had GEMM_RS_DEBUG_TRACE; slot_words >= 4 * tiles.
+ *              With slot_words >= 4 * (tiles + T_s + 1) (T_s: tiles per
+ *              slice) the slice-sum stamps of the last FUSED run follow: per
+ *              own tile (slice order, row-major) the earliest flag check, the
+ *              earliest time it was seen released, the latest sum store and
+ *              the number of 512-element items summed (low words of the same
+ *              counter; all ones / zero where none), then the launch's first
+ *              workgroup start, an unused word, its last workgroup end and an
+ *              unused word.  The stream records a wave's items at the tile
+ *              boundary after it has summed them all.
  *   flags      if non-NULL, the current value of each ready flag;
  *              flag_words >= tiles. */
 int gemm_rs_debug_read(gemm_rs_handle *h, uint32_t *slot_log, size_t slot_words,

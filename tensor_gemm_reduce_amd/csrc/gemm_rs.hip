@@ -57,6 +57,7 @@ struct TileDesc {
     const void* ag_kernel;     // all-gather + GEMM: copy phase, then the GEMM waiting for rows
     const void* ag_gemm_kernel;  // the same GEMM over an already gathered buffer
     const void* stream_kernel;   // fused, reduce_mode STREAM (or null)
+    const void* kernel_dyn;      // fused, reduce_mode ADAPTIVE (the sum between the tiles)
     int stream_lds_bytes;        // its stages, stream slots and probe area
     int fused_lds_bytes;         // LDS of `kernel` (set by variant_desc)
 };
@@ -105,7 +106,8 @@ TileDesc desc()
                     kernel_for<C, true, two>(), kernel_for<C, false, two>(),
                     kernel_for<C, true, two, kVarNt>(), kernel_for<C, false, two, kVarNt>(),
                     kernel_for<C, true, two, kVarRows>(),
-                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), sk, slds, C::LDS_BYTES};
+                    ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), sk,
+                    kernel_for<C, true, two, kVarDyn>(), slds, C::LDS_BYTES};
 }
 
 TileDesc tile_desc(int id)
@@ -117,7 +119,9 @@ TileDesc tile_desc(int id)
     case GEMM_RS_TILE_128x256: return desc<Tile128x256>();
     case GEMM_RS_TILE_256x128: return desc<Tile256x128>();
     case GEMM_RS_TILE_256x256: return desc<Tile256x256, Tile256x256S>();
-    default: return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+    default:
+        return TileDesc{0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, 0, 0};
     }
 }
 
@@ -152,8 +156,9 @@ constexpr int kAutoStreamTiles = 3 * 256;
 int resolve_reduce_mode(const gemm_rs_config& c)
 {
     if (c.num_reducers > 0) return GEMM_RS_REDUCE_TAIL;
+    if (c.num_reducers == -2) return GEMM_RS_REDUCE_ADAPTIVE;
     if (c.reduce_mode == GEMM_RS_REDUCE_AUTO) {
-        if (c.num_reducers == -2 || resolve_tile(c) != GEMM_RS_TILE_256x256 || c.K_local < (kProbe + 2) * 64)
+        if (resolve_tile(c) != GEMM_RS_TILE_256x256 || c.K_local < (kProbe + 2) * 64)
             return GEMM_RS_REDUCE_TAIL;
         const int64_t S = c.M / c.tp;
         const int64_t tiles = (int64_t)c.tp * ((S + 255) / 256) * (((int64_t)c.N + 255) / 256);
@@ -175,10 +180,6 @@ Geometry geometry_of(const gemm_rs_config& c)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Adaptive split: candidate dedicated-reducer counts and runs timed per candidate.
-constexpr int kSplitCands = 5;
-constexpr int kSplitReps = 2;
-constexpr int kSplitChoices[kSplitCands] = {0, 8, 16, 32, 64};
 
 }  // namespace
 
@@ -199,14 +200,6 @@ struct gemm_rs_handle {
     // all-gather + GEMM runs
     uint32_t* agflags;     // tp * tile rows per slice copy counters
     uint32_t* agfinished;  // per workgroup of ag_grid
-    // adaptive split (num_reducers == -2): the first fused runs cycle through
-    // candidate reducer counts, timed with events; the fastest is kept
-    struct {
-        bool on, settled;
-        int ncand, reps, launched;
-        int cand[kSplitCands];
-        hipEvent_t ev[kSplitCands * kSplitReps][2];
-    } split;
     int ag_grid;
     int ag_strided;
     int ag_units;
@@ -271,8 +264,8 @@ int gemm_rs_validate(const gemm_rs_config* c)
     if (c->tile < 0 || c->tile >= GEMM_RS_TILE_COUNT) return GEMM_RS_ERR_INVALID_ARG;
     if (c->group_m < 0) return GEMM_RS_ERR_INVALID_ARG;
     if (c->num_reducers < -2) return GEMM_RS_ERR_INVALID_ARG;
-    // the adaptive split chooses among dedicated-reducer counts
-    if (c->num_reducers == -2 && c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL)
+    // num_reducers -2 is the adaptive controller, as reduce_mode ADAPTIVE
+    if (c->num_reducers == -2 && c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_ADAPTIVE)
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->debug_flags & ~GEMM_RS_DEBUG_TRACE) return GEMM_RS_ERR_INVALID_ARG;
     if (c->drop_flag < -1) return GEMM_RS_ERR_INVALID_ARG;
@@ -286,10 +279,12 @@ int gemm_rs_validate(const gemm_rs_config* c)
     // the GEMM-only kernel); one at a time
     if (c->tile_stores == GEMM_RS_STORES_NONTEMPORAL && c->flag_protocol == GEMM_RS_FLAGS_ROW_COUNTER)
         return GEMM_RS_ERR_INVALID_ARG;
-    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_STREAM)
+    if (c->reduce_mode < GEMM_RS_REDUCE_AUTO || c->reduce_mode > GEMM_RS_REDUCE_ADAPTIVE)
         return GEMM_RS_ERR_INVALID_ARG;
-    // the stream kernel is the default store policy with tile flags
-    if (c->reduce_mode == GEMM_RS_REDUCE_STREAM &&
+    // the stream and the adaptive kernels are the default store policy with
+    // tile flags
+    const bool adaptive = c->num_reducers == -2 || c->reduce_mode == GEMM_RS_REDUCE_ADAPTIVE;
+    if ((c->reduce_mode == GEMM_RS_REDUCE_STREAM || adaptive) &&
         (c->tile_stores != GEMM_RS_STORES_DEVICE || c->flag_protocol != GEMM_RS_FLAGS_TILE))
         return GEMM_RS_ERR_INVALID_ARG;
     if (c->reduce_mode != GEMM_RS_REDUCE_AUTO && c->reduce_mode != GEMM_RS_REDUCE_TAIL && c->num_reducers > 0)
@@ -391,48 +386,8 @@ static void set_split(gemm_rs_handle* h, int red)
                      ? 1 : 0;
 }
 
-// Adaptive split: once every timed run has completed, keep the candidate with
-// the shortest run (the fastest of its repetitions).  Until then fused runs
-// use no dedicated reducers.
-static void split_try_settle(gemm_rs_handle* h)
-{
-    const int n = h->split.ncand * h->split.reps;
-    for (int i = 0; i < n; ++i) {
-        const hipError_t q = hipEventQuery(h->split.ev[i][1]);
-        if (q != hipSuccess) {
-            (void)hipGetLastError();  // a pending event is not an error
-            set_split(h, 0);
-            return;
-        }
-    }
-    int best = 0;
-    float best_ms = -1.0f;
-    for (int c = 0; c < h->split.ncand; ++c) {
-        float cand_ms = -1.0f;
-        for (int r = 0; r < h->split.reps; ++r) {
-            const int i = r * h->split.ncand + c;
-            float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, h->split.ev[i][0], h->split.ev[i][1]) == hipSuccess &&
-                (cand_ms < 0.0f || ms < cand_ms))
-                cand_ms = ms;
-        }
-        if (cand_ms >= 0.0f && (best_ms < 0.0f || cand_ms < best_ms)) {
-            best_ms = cand_ms;
-            best = h->split.cand[c];
-        }
-    }
-    for (int i = 0; i < n; ++i)
-        for (int j = 0; j < 2; ++j) (void)hipEventDestroy(h->split.ev[i][j]);
-    h->split.settled = true;
-    set_split(h, best);
-}
-
 static void free_state(gemm_rs_handle* h)
 {
-    if (h->split.on && !h->split.settled)
-        for (int i = 0; i < h->split.ncand * h->split.reps; ++i)
-            for (int j = 0; j < 2; ++j)
-                if (h->split.ev[i][j]) (void)hipEventDestroy(h->split.ev[i][j]);
     if (h->flags) (void)hipFree(h->flags);
     if (h->state) (void)hipFree(h->state);
     if (h->trace) (void)hipFree(h->trace);
@@ -449,10 +404,14 @@ static TileDesc variant_desc(const gemm_rs_config& c, int* variant)
 {
     TileDesc td = tile_desc(resolve_tile(c));
     *variant = 0;
-    if (resolve_reduce_mode(c) == GEMM_RS_REDUCE_STREAM) {
+    const int mode = resolve_reduce_mode(c);
+    if (mode == GEMM_RS_REDUCE_STREAM) {
         td.kernel = td.stream_kernel;
         td.fused_lds_bytes = td.stream_lds_bytes;
         *variant = 3;
+    } else if (mode == GEMM_RS_REDUCE_ADAPTIVE) {
+        td.kernel = td.kernel_dyn;
+        *variant = 4;
     } else if (c.tile_stores == GEMM_RS_STORES_NONTEMPORAL) {
         td.kernel = td.kernel_nt;
         td.gemm_kernel = td.gemm_kernel_nt;
@@ -548,28 +507,6 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     rc = plan_launch(h, c, dev, prop.multiProcessorCount, occ);
     if (rc != GEMM_RS_OK) { delete h; return rc; }
     hipError_t e = hipSuccess;
-    h->split.on = c->num_reducers == -2;
-    h->split.settled = !h->split.on;
-    h->split.ncand = 0;
-    h->split.reps = kSplitReps;
-    h->split.launched = 0;
-    if (h->split.on) {
-        for (int i = 0; i < kSplitCands; ++i)
-            if (kSplitChoices[i] < h->grid) h->split.cand[h->split.ncand++] = kSplitChoices[i];
-        for (int i = 0; i < h->split.ncand * h->split.reps; ++i)
-            for (int j = 0; j < 2; ++j) {
-                hipError_t ee = hipEventCreate(&h->split.ev[i][j]);
-                if (ee != hipSuccess) {
-                    // (the handle was value-initialised: events not created are null)
-                    for (int k = 0; k < h->split.ncand * h->split.reps; ++k)
-                        for (int l = 0; l < 2; ++l)
-                            if (h->split.ev[k][l]) (void)hipEventDestroy(h->split.ev[k][l]);
-                    delete h;
-                    return hip_fail(ee, "hipEventCreate");
-                }
-            }
-    }
-
     // all-gather + GEMM launches: the compute grid of the same tile (no reducers)
     for (const void* k : {h->td.ag_kernel, h->td.ag_gemm_kernel}) {
         e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, h->td.lds_bytes);
@@ -595,12 +532,14 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
     const size_t agblocks = (size_t)h->g.tp * (size_t)(h->g.tms > 0 ? h->g.tms : 1);
 
     const size_t tiles = (size_t)(h->g.tiles > 0 ? h->g.tiles : 1);
+    // the slot log, then the slice-sum stamps of the own tiles and the launch
+    const size_t trace_words = ((size_t)h->g.tiles + (size_t)h->g.ts + 1) * 4;
     const size_t slice = (size_t)h->g.S * (size_t)h->g.N;
     if (hipMalloc(&h->agflags, agblocks * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->agfinished, (size_t)h->ag_grid * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->flags, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->state, sizeof(DeviceState)) != hipSuccess ||
-        hipMalloc(&h->trace, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&h->trace, trace_words * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->finished, (size_t)h->grid * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc(&h->scratch, (slice > 0 ? slice : 8) * sizeof(uint16_t)) != hipSuccess) {
         free_state(h);
@@ -611,7 +550,7 @@ int gemm_rs_create(const gemm_rs_config* c, gemm_rs_handle** out)
         hipMemset(h->agfinished, 0, (size_t)h->ag_grid * sizeof(uint32_t)) != hipSuccess ||
         hipMemset(h->flags, 0, tiles * h->flag_stride * sizeof(uint32_t)) != hipSuccess ||
         hipMemset(h->state, 0, sizeof(DeviceState)) != hipSuccess ||
-        hipMemset(h->trace, 0, tiles * 4 * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->trace, 0, trace_words * sizeof(uint32_t)) != hipSuccess ||
         hipMemset(h->finished, 0, (size_t)h->grid * sizeof(uint32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_state(h);
@@ -644,6 +583,7 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
     a.state = h->state;
     a.status = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->state) + offsetof(DeviceState, status));
     a.trace = h->trace;
+    a.sum_trace = h->trace ? h->trace + (int64_t)h->g.tiles * 4 : nullptr;
     a.finished = h->finished;
     a.g = h->g;
     a.x_bytes = (uint32_t)((int64_t)h->g.M * h->g.K * 2);
@@ -660,24 +600,6 @@ static void fill_args(gemm_rs_handle* h, Args& a, const void* x, const void* w, 
 
 static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s, bool tail = false)
 {
-    // adaptive split: time the candidates on the first uncaptured fused runs
-    int timed = -1;
-    if (fused && h->split.on && !h->split.settled) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        HIP_TRY(hipStreamIsCapturing(s, &cs));
-        if (cs == hipStreamCaptureStatusNone) {
-            const int n = h->split.ncand * h->split.reps;
-            if (h->split.launched < n) {
-                timed = h->split.launched++;
-                set_split(h, h->split.cand[timed % h->split.ncand]);
-            } else {
-                split_try_settle(h);
-            }
-        } else {
-            set_split(h, 0);
-        }
-        a.strided = h->strided;
-    }
     a.fused = fused ? 1 : 0;
     a.num_compute = fused ? h->compute_wgs : h->grid;
     a.num_reducers = fused ? h->reducer_wgs : 0;
@@ -688,10 +610,8 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s, bo
     // (a GEMM-only launch runs on the compute workgroups' grid: the
     // co-resident reducers' extra workgroup per CU is not part of the GEMM)
     if (!fused) a.num_compute = h->gemm_grid;
-    if (timed >= 0) HIP_TRY(hipEventRecord(h->split.ev[timed][0], s));
     HIP_TRY(hipLaunchKernel(k, dim3(fused ? h->grid : h->gemm_grid), dim3(h->td.threads), params,
                             fused ? (tail ? h->tail_lds : h->fused_lds) : h->td.lds_bytes, s));
-    if (timed >= 0) HIP_TRY(hipEventRecord(h->split.ev[timed][1], s));
     return GEMM_RS_OK;
 }
 
@@ -753,6 +673,12 @@ static int launch_run(gemm_rs_handle* h, int32_t mode, const void* x, const void
     Args a;
     fill_args(h, a, x, w, send, peers, out, local, needs_sum ? gather : nullptr);
     if (status) a.status = status;
+    if (mode == GEMM_RS_MODE_FUSED && a.trace_on) {
+        // the slice-sum stamps start empty (a fill kernel: safe in a captured graph)
+        void* params[] = {&a.sum_trace, &h->g.ts};
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&sum_trace_clear_kernel), dim3(1), dim3(256), params, 0,
+                                s));
+    }
     int rc = GEMM_RS_OK;
     switch (mode) {
     case GEMM_RS_MODE_FUSED:
@@ -908,7 +834,7 @@ int gemm_rs_query(gemm_rs_handle* h, gemm_rs_info* info)
     info->reduce_grid = h->reduce_grid;
     info->xcd_split = h->strided;
     info->reduce_mode = h->reduce_mode;
-    info->split_state = !h->split.on ? 0 : (h->split.settled ? 2 : 1);
+    info->split_state = h->reduce_mode == GEMM_RS_REDUCE_ADAPTIVE ? 1 : 0;
     // every workgroup's finish mark holds the epoch of the last fused launch
     HIP_TRY(hipStreamSynchronize(h->last_stream));
     HIP_TRY(hipMemcpy(&info->epoch, h->finished, sizeof info->epoch, hipMemcpyDeviceToHost));
@@ -923,8 +849,11 @@ int gemm_rs_debug_read(gemm_rs_handle* h, uint32_t* slot_log, size_t slot_words,
     if (slot_log && slot_words < 4 * tiles) return GEMM_RS_ERR_INVALID_ARG;
     if (flags && flag_words < tiles) return GEMM_RS_ERR_INVALID_ARG;
     HIP_TRY(hipStreamSynchronize(h->last_stream));
+    // with room for them, the slice-sum stamps follow the slot log
+    const size_t words = 4 * (tiles + (size_t)h->g.ts + 1);
     if (slot_log && tiles)
-        HIP_TRY(hipMemcpy(slot_log, h->trace, 4 * tiles * sizeof(uint32_t), hipMemcpyDeviceToHost));
+        HIP_TRY(hipMemcpy(slot_log, h->trace, (slot_words >= words ? words : 4 * tiles) * sizeof(uint32_t),
+                          hipMemcpyDeviceToHost));
     if (flags && tiles) {
         if (h->flag_stride == 1) {
             HIP_TRY(hipMemcpy(flags, h->flags, tiles * sizeof(uint32_t), hipMemcpyDeviceToHost));
@@ -966,7 +895,7 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, uint32_t 
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 4;
+constexpr int kVariants = 5;
 
 // Per device, filled on the first allocation-free call there.
 struct StaticDevice {
@@ -989,8 +918,8 @@ extern "C" int gemm_rs_run_static(const gemm_rs_config* c, int32_t mode, const v
     int rc = gemm_rs_validate(c);
     if (rc != GEMM_RS_OK) return rc;
     if (mode < GEMM_RS_MODE_FUSED || mode > GEMM_RS_MODE_SEQUENTIAL) return GEMM_RS_ERR_INVALID_ARG;
-    // no adaptive split (its timing events), no trace log (its buffer)
-    if (c->num_reducers == -2 || c->debug_flags != 0) return GEMM_RS_ERR_INVALID_ARG;
+    // no trace log (its buffer)
+    if (c->debug_flags != 0) return GEMM_RS_ERR_INVALID_ARG;
     if (!local_slice) return GEMM_RS_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return GEMM_RS_ERR_MISALIGNED;
     int dev = 0;

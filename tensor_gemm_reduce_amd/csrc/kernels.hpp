@@ -76,9 +76,12 @@ constexpr int kStoreDeviceNt = kStoreDevice | kAuxNt;
 
 // Kernel variants (a template parameter of the fused and GEMM kernels, so that
 // the default kernel carries no code of the others): bit 0 stores routed tiles
-// with kStoreDeviceNt, bit 1 reads row counters instead of tile flags.
+// with kStoreDeviceNt, bit 1 reads row counters instead of tile flags, bit 2
+// interleaves the slice sum with the tiles under the adaptive controller
+// (sum_units).
 constexpr int kVarNt = 1;
 constexpr int kVarRows = 2;
+constexpr int kVarDyn = 4;
 
 
 // Handle-owned device state, zeroed at creation.  The arrival tickets and the
@@ -105,6 +108,7 @@ struct Args {
     DeviceState* state;
     int32_t* status;         // [0] error code, [1] flag index that timed out
     uint32_t* trace;         // 4 words per slot (debug)
+    uint32_t* sum_trace;     // 4 words per own tile, then 4 for the launch (debug)
     uint32_t* finished;      // per workgroup: epoch of the last fused launch it finished
     Geometry g;
     uint32_t x_bytes, w_bytes;
@@ -742,47 +746,97 @@ __device__ __forceinline__ bool wait_tile(const Args& a, uint32_t epoch, int t, 
     return true;
 }
 
-// Sums items first, first + stride, ... with plain loads (no LDS), BATCH items
-// at a time: a batch's peer chunks are loaded before its tiles' flags are
-// checked (they need none), then its local chunks, in the sum order.  A tile
-// whose flag does not arrive within the watchdog limit is reported and its
-// items are skipped.
+// Fills the slice-sum stamps of ts own tiles and the launch (below) with
+// their starting values, before a traced fused run.
+__global__ void sum_trace_clear_kernel(uint32_t* st, int ts)
+{
+    for (int i = threadIdx.x; i < (ts + 1) * 4; i += blockDim.x) st[i] = (i & 3) < 2 ? 0xFFFFFFFFu : 0u;
+}
+
+// Slice-sum trace (debug runs only): per own tile t, words 4t .. 4t+3 hold the
+// earliest time a wave checked its flag for a sum, the earliest time a wave
+// saw it released, the latest time a wave stored a sum of it, and the number
+// of items summed (100 MHz counter, low words); words 4 ts, 4 ts + 1 hold the
+// launch's first and last workgroup times.  The host fills the minima with
+// all ones and the rest with zeros before a traced run.
+__device__ __forceinline__ uint32_t now32() { return (uint32_t)wall_clock64(); }
+
+__device__ __forceinline__ void trace_sum(const Args& a, int t, uint32_t poll, uint32_t acq, uint32_t done, uint32_t n)
+{
+    uint32_t* w = a.sum_trace + (int64_t)t * 4;
+    atomicMin(w, poll);
+    atomicMin(w + 1, acq);
+    atomicMax(w + 2, done);
+    atomicAdd(w + 3, n);
+}
+
+// Sums the items item[0 .. B-1] (slice item indices; past the last item or
+// negative: none) with plain loads: every peer chunk first (they need no flag),
+// then each item's tile flag is checked and its local chunk loaded, in the sum
+// order.  An item whose flag does not arrive within the watchdog limit is
+// reported and skipped (`gave_up` then skips later unreleased items without
+// waiting).
+template <int B, int SLEEP = 2, bool ROWS = false>
+__device__ __forceinline__ void sum_batch(const Args& a, const ItemMap& m, const int (&item)[B], uint32_t epoch,
+                                          bool& gave_up)
+{
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.dst[a.g.rank], 0, a.slice_bytes, kRsrcFlags);
+    uint32_t boff[B];
+    u32x4 v[B][kPeers + 1];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        boff[b] = item[b] >= 0 ? item_boff(m, a, item[b]) : kOob;
+#pragma unroll
+        for (int s = 0; s < kPeers; ++s) {
+            const __amdgpu_buffer_rsrc_t rp =
+                __builtin_amdgcn_make_buffer_rsrc((void*)a.peers[s], 0, a.slice_bytes, kRsrcFlags);
+            v[b][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, boff[b], 0, kAuxNt));
+        }
+    }
+    // every item's ready word first, in one round trip; a tile not yet
+    // released is then waited for
+    uint32_t tp[B], ta[B], fw[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const bool in = item[b] >= 0 && item[b] < m.nitems;
+        fw[b] = in ? __hip_atomic_load(ready_word<ROWS>(a, a.g.rank * a.g.ts + (item[b] >> m.ipt_log2)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const bool in = item[b] >= 0 && item[b] < m.nitems;
+        if (a.trace_on) tp[b] = now32();
+        const bool ok = in && (released<ROWS>(a, fw[b], epoch) ||
+                               wait_tile<SLEEP, ROWS>(a, epoch, item[b] >> m.ipt_log2, gave_up));
+        if (a.trace_on) ta[b] = ok ? now32() : 0xFFFFFFFFu;
+        boff[b] = ok ? boff[b] : kOob;
+        v[b][kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, boff[b], 0, kAuxSc1));
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[b][s]);
+        store_sum(a, pack8(acc), boff[b]);
+        if (a.trace_on && item[b] >= 0 && item[b] < m.nitems && (threadIdx.x & 63) == 0)
+            trace_sum(a, item[b] >> m.ipt_log2, tp[b], ta[b], now32(), ta[b] != 0xFFFFFFFFu ? 1u : 0u);
+    }
+}
+
+// Sums items first, first + stride, ... BATCH at a time (sum_batch).
 // SLEEP: s_sleep argument between flag polls (64 clocks each); ROWS: the
 // row-counter protocol.
 template <int BATCH, int SLEEP = 2, bool ROWS = false>
 __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int first, int stride, uint32_t epoch)
 {
-    constexpr int kDrainBatch = BATCH;
     bool gave_up = false;
-    const __amdgpu_buffer_rsrc_t rl =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.dst[a.g.rank], 0, a.slice_bytes, kRsrcFlags);
-    for (int base = first; base < m.nitems; base += kDrainBatch * stride) {
-        uint32_t boff[kDrainBatch];
-        u32x4 v[kDrainBatch][kPeers + 1];
+    for (int base = first; base < m.nitems; base += BATCH * stride) {
+        int item[BATCH];
 #pragma unroll
-        for (int b = 0; b < kDrainBatch; ++b) {
-            boff[b] = item_boff(m, a, base + b * stride);
-#pragma unroll
-            for (int s = 0; s < kPeers; ++s) {
-                const __amdgpu_buffer_rsrc_t rp =
-                    __builtin_amdgcn_make_buffer_rsrc((void*)a.peers[s], 0, a.slice_bytes, kRsrcFlags);
-                v[b][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, boff[b], 0, kAuxNt));
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < kDrainBatch; ++b) {
-            const int item = base + b * stride;
-            const bool ok = item < m.nitems && wait_tile<SLEEP, ROWS>(a, epoch, item >> m.ipt_log2, gave_up);
-            boff[b] = ok ? boff[b] : kOob;
-            v[b][kPeers] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, boff[b], 0, kAuxSc1));
-        }
-#pragma unroll
-        for (int b = 0; b < kDrainBatch; ++b) {
-            f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[b][s]);
-            store_sum(a, pack8(acc), boff[b]);
-        }
+        for (int b = 0; b < BATCH; ++b) item[b] = base + b * stride;
+        sum_batch<BATCH, SLEEP, ROWS>(a, m, item, epoch, gave_up);
     }
 }
 
@@ -1042,6 +1096,20 @@ __device__ __forceinline__ void stream_settle(Stream& s, const Args& a)
     s.real_cur = 0;
 }
 
+// (trace) Records stamps for a stream wave's items [first, last) on every own
+// tile they cover: a probe read (poll; acq if it latched) or, with n, the
+// items summed by `done`.
+__device__ __forceinline__ void stream_trace(const Args& a, const Stream& s, int first, int last, uint32_t poll,
+                                             uint32_t acq, uint32_t done, bool count)
+{
+    if (last <= first || (threadIdx.x & 63) != 0) return;
+    const int ipt = 1 << s.m.ipt_log2;
+    for (int t = first >> s.m.ipt_log2; t <= (last - 1) >> s.m.ipt_log2; ++t) {
+        const int lo = max(first, t * ipt), hi = min(last, (t + 1) * ipt);
+        trace_sum(a, t, poll, acq, done, count ? (uint32_t)(hi - lo) : 0u);
+    }
+}
+
 // ---------------------------------------------------------------- tile loop
 
 // State carried from one tile to the next: whether the previous tile's
@@ -1289,7 +1357,13 @@ struct SplitLoop {
         if (kt == kPub) publish_pending<false>(a, hk);
         if (!s.latched) {
             if (kt == kProbe - 1 && prober) stream_probe_issue(s, a);
-            if (kt == kProbe) stream_probe_read(s);
+            if (kt == kProbe) {
+                stream_probe_read(s);
+                if (a.trace_on && threadIdx.x >= C::LW * 64) {
+                    const uint32_t t = now32();
+                    stream_trace(a, s, s.first, s.end, t, s.latched ? t : 0xFFFFFFFFu, 0u, false);
+                }
+            }
         }
     }
 
@@ -1422,6 +1496,12 @@ __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileS
             // loop, after finishing an item begun in the previous tile
             const bool active = s.latched && s.item < s.end;
             if (!active && s.real_cur) stream_settle(s, a);
+            // (trace: a wave that has summed all its items records them at the
+            // next tile start; its range then starts at its end)
+            if (a.trace_on && !active && s.latched && s.first < s.item) {
+                stream_trace(a, s, s.first, s.item, 0xFFFFFFFFu, 0xFFFFFFFFu, now32(), true);
+                s.first = s.item;
+            }
             stage_barrier();
             load_frags<C>(lds, 0, xf[0], wf[0]);
             int kt = 0;
@@ -1450,6 +1530,73 @@ __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileS
     if (!STREAMER || hk.pend_flag >= 0) wait_vmcnt<0>();
     stage_barrier();
     publish_pending<false>(a, hk);
+}
+
+// ---------------------------------------------------------------- adaptive controller
+//
+// Reading of mKernel's adaptive role split ("mKernel: Fast Multi-GPU,
+// Multi-Node Fused Kernels", section 3.2: cost estimates from cycle counters,
+// a communication target, role changes at task boundaries) for one GPU whose
+// tiles fill whole rounds of the grid: a dedicated reducer workgroup takes its
+// CU out of the GEMM for the rest of the launch, which adds a round of tiles
+// whenever the tile count is a multiple of the grid (every workload here).
+// Instead every compute workgroup changes role at its tile boundaries and sums
+// a share of the slice there.  The slice's items are taken in release order
+// (own tiles in schedule order); wave w of the W * G owns items w, w + W G, ...
+// of that order, so every wave's share spreads over the whole release
+// timeline and no wave claims anything at run time.  At a boundary a wave sums
+// batches of four of its items: an even share of what it has left over the
+// boundaries it has left, limited to items of rounds already released (slots
+// below j * G after its j-th tile) and, once it has measured a batch with the
+// 100 MHz counter, to a quarter of its last tile's time.  The last boundary
+// sums everything left, as the tail does.
+constexpr int kUnitItems = 4;
+
+struct UnitCtl {
+    int n;             // this wave's next item (the n-th of its share)
+    uint32_t t_tile;   // this wave's last tile time (ticks)
+    uint32_t t_batch;  // this wave's last batch time (ticks; 0: none yet)
+    bool gave_up;      // a flag wait timed out (later ones are not waited for)
+};
+
+// The slice item of release-order item v (v = s * items_per_tile + i, s an
+// own tile's schedule slot).
+__device__ __forceinline__ int release_item(const Args& a, const ItemMap& m, int v)
+{
+    const TileCoord t = decode_slot(a.g, v >> m.ipt_log2);
+    return ((t.tml * a.g.tnc + t.tn) << m.ipt_log2) + (v & ((1 << m.ipt_log2) - 1));
+}
+
+// One wave at a boundary with nb boundaries left (this one included; nb == 1
+// is the last).  Its share: release-order items base, base + stride, ...;
+// `frontier`: release-order items below it are released.
+template <bool ROWS>
+__device__ __forceinline__ void sum_units(const Args& a, const ItemMap& m, UnitCtl& c, int nb, int frontier,
+                                          int base, int stride, uint32_t epoch)
+{
+    const int total = m.nitems;
+    const int mine = base < total ? (total - base + stride - 1) / stride : 0;
+    const int rem = mine - c.n;
+    if (rem <= 0) return;
+    int batches = (rem + kUnitItems * nb - 1) / (kUnitItems * nb);
+    if (nb > 1 && c.t_batch > 0u) batches = min(batches, max((int)((c.t_tile / 4u) / c.t_batch), 1));
+    for (int bt = 0; bt < batches; ++bt) {
+        int item[kUnitItems];
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < kUnitItems; ++q) {
+            const int nn = c.n + q;
+            const int v = base + nn * stride;
+            const bool take = nn < mine && (nb == 1 || v < frontier);
+            item[q] = take ? release_item(a, m, v) : -1;
+            cnt += take ? 1 : 0;
+        }
+        if (cnt == 0) return;
+        const uint32_t t0 = now32();
+        sum_batch<kUnitItems, 1, ROWS>(a, m, item, epoch, c.gave_up);
+        c.t_batch = now32() - t0;
+        c.n += cnt;
+    }
 }
 
 // Every group holds G/8 workgroups; group x has R_x = R/8 + (x < R%8) reducers
@@ -1496,6 +1643,15 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
     TileJob<C> job;
     Stream sm;
     if constexpr (SPLIT) stream_init(sm, a, lds + C::LDS_BYTES, pos, loader ? 0 : wave - C::LW, Ctot, epoch);
+    // the adaptive controller: units at the boundaries from j0 on (once the
+    // rounds holding own tiles are released)
+    constexpr bool DYN = FUSED && (VAR & kVarDyn) != 0;
+    const ItemMap um = item_map(a);
+    UnitCtl uc = {0, 0u, 0u, false};
+    const int ubase = pos * C::WAVES + wave, ustride = Ctot * C::WAVES;
+    const int ntile = pos < a.g.tiles ? (a.g.tiles - pos + Ctot - 1) / Ctot : 0;
+    const int j0 = a.g.ts > 0 ? (a.g.ts - 1) / Ctot + 1 : ntile;
+    int j = 0;
     int q = pos;
     TileCoord t;
     if (q < a.g.tiles) {
@@ -1507,6 +1663,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
                                     tile_cols(a.g, t));
     }
     while (q < a.g.tiles) {
+        const uint32_t t_start = DYN ? now32() : 0u;
         if constexpr (SPLIT) {
             if (loader)
                 tile_kloop_split<C, false>(a, lds, st, job, hk, sm);
@@ -1540,6 +1697,14 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
             hk.pend_q = q;
             hk.pend_flag = t.flag;
         }
+        if constexpr (DYN) {
+            uc.t_tile = now32() - t_start;
+            if (j >= j0 && j + 1 < ntile)
+                sum_units<(VAR & kVarRows) != 0>(a, um, uc, ntile - j, (int)min((int64_t)j * Ctot << um.ipt_log2,
+                                                                                 (int64_t)um.nitems),
+                                                 ubase, ustride, epoch);
+        }
+        ++j;
         q = qn;
         t = tn;
     }
@@ -1555,6 +1720,7 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         __shared__ int s_progress[C::EW];
         if (!loader) {
             stream_settle(sm, a);
+            if (a.trace_on) stream_trace(a, sm, sm.first, sm.item, 0xFFFFFFFFu, 0xFFFFFFFFu, now32(), true);
             if ((threadIdx.x & 63) == 0) s_progress[wave - C::LW] = sm.item;
         }
         __syncthreads();
@@ -1566,6 +1732,9 @@ __device__ __forceinline__ void compute_waves(const Args& a, char* lds, int pos,
         ItemMap m = sm.m;
         m.nitems = half ? end : mid;
         drain_items<2>(a, m, half ? mid : cur, 1, epoch);
+    } else if (DYN) {
+        // the last boundary: units until none is left
+        sum_units<(VAR & kVarRows) != 0>(a, um, uc, 1, um.nitems, ubase, ustride, epoch);
     } else if (sum_tail) {
         // every wave sums a share of the slice after its last tile (sixteen
         // items in flight per CU for the eight-wave and one-per-CU tiles; one
@@ -1604,10 +1773,12 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
     __shared__ int s_skip;
     uint32_t* unit = &a.state->unit[epoch & 1u];
     bool gave_up = false;  // (thread 0's)
+    uint32_t tp = 0u, ta = 0u;  // (thread 0's trace stamps of the unit)
     for (;;) {
         if (threadIdx.x == 0) {
             const int u = (int)atomicAdd(unit, 1u);
             int skip = 0;
+            if (a.trace_on) tp = now32();
             if (u < a.g.ts) {
                 const TileCoord t = decode_slot(a.g, u);
                 const uint32_t* f = ready_word<ROWS>(a, t.flag);
@@ -1630,6 +1801,7 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
                     }
                 }
             }
+            if (a.trace_on) ta = skip ? 0xFFFFFFFFu : now32();
             s_unit = u;
             s_skip = skip;
         }
@@ -1664,6 +1836,11 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
 #pragma unroll
                 for (int i = 0; i < kPeers; ++i) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.gather[i] + off));
             }
+        }
+        if (a.trace_on) {
+            __syncthreads();
+            if (threadIdx.x == 0)
+                trace_sum(a, t.tml * a.g.tnc + t.tn, tp, ta, now32(), (uint32_t)((a.g.bm * a.g.bn) >> 9));
         }
     }
 }
@@ -1706,6 +1883,7 @@ __device__ __forceinline__ void fused_body(const Args& a)
             __hip_atomic_store(&a.state->unit[nx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    if (FUSED && a.trace_on && threadIdx.x == 0) atomicMin(a.sum_trace + (int64_t)a.g.ts * 4, now32());
     __syncthreads();
     // (read through readfirstlane so that the compiler sees them uniform: the
     // tile loop then stays in scalar registers)
@@ -1730,8 +1908,10 @@ __device__ __forceinline__ void fused_body(const Args& a)
 
     if constexpr (FUSED) {
         __syncthreads();
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
+            if (a.trace_on) atomicMax(a.sum_trace + (int64_t)a.g.ts * 4 + 2, now32());
             __hip_atomic_store(a.finished + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

@@ -45,7 +45,8 @@ REDUCE_AUTO = 0
 REDUCE_TAIL = 1
 REDUCE_CORESIDENT = 2
 REDUCE_STREAM = 3
-REDUCE_MODES = {"auto": 0, "tail": 1, "coresident": 2, "stream": 3}
+REDUCE_ADAPTIVE = 4
+REDUCE_MODES = {"auto": 0, "tail": 1, "coresident": 2, "stream": 3, "adaptive": 4}
 
 STORES_DEVICE = 0
 STORES_NONTEMPORAL = 1
@@ -238,15 +239,20 @@ def gemm_rs_query(h) -> gemm_rs_info:
     return info
 
 
-def gemm_rs_debug_read(h, tiles: int):
-    """Returns (slot_log [tiles][4] uint32, flags [tiles] uint32) as numpy arrays."""
+def gemm_rs_debug_read(h, tiles: int, own_tiles=None):
+    """Returns (slot_log [tiles][4] uint32, flags [tiles] uint32) as numpy arrays;
+    with own_tiles (tiles per slice) also the slice-sum stamps [own_tiles][4]
+    (poll, acquire, done, items) and the launch's [first, -, last, -] words."""
     import numpy as np
 
-    log = np.zeros((max(tiles, 1), 4), np.uint32)
+    extra = 0 if own_tiles is None else own_tiles + 1
+    log = np.zeros((max(tiles + extra, 1), 4), np.uint32)
     flags = np.zeros(max(tiles, 1), np.uint32)
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
     _check(lib().gemm_rs_debug_read(h, p(log), log.size, p(flags), flags.size), "gemm_rs_debug_read")
-    return log[:tiles], flags[:tiles]
+    if own_tiles is None:
+        return log[:tiles], flags[:tiles]
+    return log[:tiles], flags[:tiles], log[tiles:tiles + own_tiles], log[tiles + own_tiles]
 
 
 def gemm_rs_destroy(h) -> None:
@@ -356,8 +362,8 @@ class GemmRS:
     def status(self) -> int:
         return gemm_rs_status(self.h)
 
-    def debug_read(self):
-        return gemm_rs_debug_read(self.h, self.info.tiles)
+    def debug_read(self, sums=False):
+        return gemm_rs_debug_read(self.h, self.info.tiles, self.info.tiles_per_slice if sums else None)
 
     def close(self):
         if self.h is not None:

@@ -80,12 +80,17 @@ def cfg(**kw):
     (dict(tile_stores=-1), gr.ERR_INVALID_ARG),
     (dict(flag_protocol="row_counter"), gr.OK),
     (dict(flag_protocol="row_counter", num_reducers=8), gr.OK),
-    (dict(flag_protocol="row_counter", num_reducers=-2), gr.OK),
+    (dict(flag_protocol="row_counter", num_reducers=-2), gr.ERR_INVALID_ARG),  # adaptive: tile flags
+    (dict(reduce_mode="adaptive"), gr.OK),
+    (dict(reduce_mode="adaptive", num_reducers=-2), gr.OK),
+    (dict(reduce_mode="adaptive", tile_stores="nt"), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode="adaptive", num_reducers=8), gr.ERR_INVALID_ARG),
+    (dict(num_reducers=-2, tile_stores="nt"), gr.ERR_INVALID_ARG),
     (dict(flag_protocol=2), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt", flag_protocol="row_counter"), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt", reduce_mode="coresident"), gr.OK),
     (dict(watchdog_us=-1), gr.ERR_INVALID_ARG),
-    (dict(reduce_mode=4), gr.ERR_INVALID_ARG),
+    (dict(reduce_mode=5), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="coresident"), gr.OK),
     (dict(reduce_mode="coresident", num_reducers=8), gr.ERR_INVALID_ARG),
     (dict(reduce_mode="stream"), gr.OK),                                   # 256x256 tile
@@ -162,7 +167,9 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
     (dict(M=32768, N=8192, K_local=3584), gr.REDUCE_STREAM),
     (dict(M=8192, N=5888, K_local=2048), gr.REDUCE_TAIL),            # 736 tiles
     (dict(M=8192, N=6144, K_local=320), gr.REDUCE_TAIL),             # five K steps
-    (dict(M=8192, N=6144, K_local=2048, num_reducers=-2), gr.REDUCE_TAIL),  # adaptive split
+    (dict(M=8192, N=6144, K_local=2048, num_reducers=-2), gr.REDUCE_ADAPTIVE),  # the controller
+    (dict(reduce_mode="adaptive"), gr.REDUCE_ADAPTIVE),
+    (dict(M=512, K_local=1024, num_reducers=-2), gr.REDUCE_ADAPTIVE),
     (dict(M=8192, N=6144, K_local=2048, num_reducers=8), gr.REDUCE_TAIL),
     (dict(M=8192, N=6144, K_local=2048, tile="128x128"), gr.REDUCE_TAIL),
     (dict(M=8192, N=6144, K_local=2048, reduce_mode="tail"), gr.REDUCE_TAIL),

@@ -26,6 +26,8 @@ REDUCE["nt"] = dict(tile_stores="nt")
 REDUCE["stream"] = dict(reduce_mode="stream")
 # the automatic placement with a released-tile counter per tile row
 REDUCE["rowc"] = dict(flag_protocol="row_counter")
+# the adaptive controller: units of the sum between the tiles
+REDUCE["adaptive"] = dict(reduce_mode="adaptive")
 
 
 def _op(cfg, M=None, **kw):

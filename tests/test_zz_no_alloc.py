@@ -35,7 +35,8 @@ def _outputs(b):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(num_reducers=8), dict(flag_stride=32, tile_stores="nt"),
-                                dict(flag_protocol="row_counter")], ids=["tail", "reducers8", "padded_nt", "rowc"])
+                                dict(flag_protocol="row_counter"), dict(reduce_mode="adaptive")],
+                         ids=["tail", "reducers8", "padded_nt", "rowc", "adaptive"])
 def test_static_runs_equal_handle_runs_big_then_small(kw):
     status = torch.full((2,), -99, dtype=torch.int32, device="cuda")
     for cfg, rank, mode in ((BIG, 3, "normal"), (SMALL, 6, "integer")):
@@ -129,8 +130,6 @@ def test_static_argument_checks():
     assert gr.gemm_rs_run_static(c, gr.MODE_FUSED, xp, wp, send, pp, out, None, None, s) == gr.ERR_INVALID_ARG
     assert gr.gemm_rs_run_static(c, 9, xp, wp, send, pp, out, local, None, s) == gr.ERR_INVALID_ARG
     assert gr.gemm_rs_run_static(c, gr.MODE_FUSED, xp + 2, wp, send, pp, out, local, None, s) == gr.ERR_MISALIGNED
-    adaptive = gr.make_config(cfg.M, cfg.N, cfg.K_local, num_reducers=-2)
-    assert gr.gemm_rs_run_static(adaptive, gr.MODE_FUSED, xp, wp, send, pp, out, local, None, s) == gr.ERR_INVALID_ARG
     traced = gr.make_config(cfg.M, cfg.N, cfg.K_local, debug_flags=gr.DEBUG_TRACE)
     assert gr.gemm_rs_run_static(traced, gr.MODE_FUSED, xp, wp, send, pp, out, local, None, s) == gr.ERR_INVALID_ARG
     # ready flags beyond the static array: 16384 tiles of 128x128, each padded to 128 bytes
