@@ -56,8 +56,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--tile", default="auto")
     p.add_argument("--reducers", type=int, default=-1,
-                   help="dedicated reducer workgroups: -1 the plan's default, -2 adaptive")
-    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "coresident", "stream"],
+                   help="dedicated reducer workgroups: -1 the plan's default, -2 the adaptive controller")
+    p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "coresident", "stream", "adaptive"],
                    help="where the fused launch sums the slice without dedicated reducers")
     p.add_argument("--tile-stores", default="device", choices=["device", "nt"],
                    help="cache policy of the routed tile stores (nt: non-temporal hint)")
@@ -78,6 +78,9 @@ def parse():
                         "OUT_JSON and exit")
     p.add_argument("--allgather-sweep", metavar="OUT_JSON",
                    help="time all-gather + GEMM (the column-parallel layer) per layer shape, write OUT_JSON")
+    p.add_argument("--timeline", metavar="OUT_MD",
+                   help="trace one fused launch per reduce placement (tail, stream, adaptive) and write a "
+                        "timeline summary of the GEMM's releases and the slice sum's stamps")
     p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -116,19 +119,12 @@ class Case:
         self.op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
                             num_reducers=args.reducers, reduce_mode=args.reduce_mode,
                             tile_stores=args.tile_stores)
-        # the adaptive split (reducers -2) times its candidates on uncaptured
-        # runs: give it those before anything is captured into a graph
-        if args.reducers == -2:
-            for _ in range(16):
-                self.run(gr.MODE_FUSED)
-                torch.cuda.synchronize()
-            log(f"[{name}] adaptive split settled: {gr.gemm_rs_query(self.op.h).reducer_wgs} reducer workgroups")
         # where the fused launch sums the slice elsewhere than after the last
         # tile, the same launch with the sum after the last tile is timed beside it
         self.op_tail = None
         if self.op.info.reduce_mode != gr.REDUCE_TAIL:
             self.op_tail = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=rank, tile=args.tile,
-                                     num_reducers=args.reducers, reduce_mode="tail",
+                                     num_reducers=max(args.reducers, -1), reduce_mode="tail",
                                      tile_stores=args.tile_stores)
         self.gr = gr
 
@@ -312,7 +308,7 @@ def measure_case(c: Case, warmup, iters):
         "reduce_pct_hbm": 100.0 * cfg.reduce_bytes / tr * 1e-3 / PEAK_HBM_GBS,
         "overlap": 1.0 - (tf - tg) / tr,
         "speedup_vs_sequential": seq["median_us"] / tf,
-        "reduce_mode": {0: "auto", 1: "tail", 2: "coresident", 3: "stream"}[c.op.info.reduce_mode],
+        "reduce_mode": {0: "auto", 1: "tail", 2: "coresident", 3: "stream", 4: "adaptive"}[c.op.info.reduce_mode],
         **extra,
     }
 
@@ -458,10 +454,11 @@ def traffic_from(args):
 
 
 SPLIT_KNOBS = (
-    [dict(num_reducers=r) for r in (0, 2, 4, 8, 16, 32, 64)]
-    + [dict(num_reducers=r, flag_stride=32) for r in (0, 8, 64)]
-    + [dict(num_reducers=r, tile_stores=1) for r in (0, 8, 64)]
-    + [dict(num_reducers=r, flag_protocol=1) for r in (0, 8, 64)]
+    [dict(reduce_mode="tail")] + [dict(num_reducers=r) for r in (2, 4, 8, 16, 32, 64)]
+    + [dict(reduce_mode="stream"), dict(reduce_mode="adaptive")]
+    + [dict(reduce_mode="tail", flag_stride=32), dict(num_reducers=8, flag_stride=32)]
+    + [dict(reduce_mode="tail", tile_stores=1), dict(num_reducers=8, tile_stores=1)]
+    + [dict(reduce_mode="tail", flag_protocol=1), dict(num_reducers=8, flag_protocol=1)]
 )
 
 
@@ -478,7 +475,11 @@ def split_sweep(args):
     cfg = base.cfg
     ops = []
     for kw in SPLIT_KNOBS:
-        op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=base.rank, tile=args.tile, **kw)
+        try:
+            op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=base.rank, tile=args.tile, **kw)
+        except gr.GemmRSError as e:  # (the stream needs the 256x256 tile)
+            log(f"[{args.workload}] {kw}: {e}")
+            continue
         ops.append((kw, op))
     run = lambda op, mode: op.run(mode, base.x, base.w, base.send, base.peers, base.out, base.local)
     base.run(gr.MODE_FUSED)
@@ -514,6 +515,101 @@ def split_sweep(args):
         json.dump(res, f, indent=1)
     if not all(same) or any(r["status"] != gr.gemm_rs_strerror(gr.OK) for r in rows):
         raise RuntimeError("a setting changed the result or reported an error")
+
+
+def timeline_summary(op, cfg, kernel_us):
+    """Per-launch figures from a traced fused run's slot log and slice-sum
+    stamps (100 MHz counter; times in us from the launch's first workgroup)."""
+    import numpy as np
+
+    log_, _, stamps, launch = op.debug_read(sums=True)
+    info = op.info
+    t0 = int(launch[0])
+    rel = lambda v: ((np.asarray(v, np.int64) - t0) % (1 << 32)) / 100.0
+    release = rel(log_[:, 2])              # per schedule slot
+    flag_of_slot = log_[:, 0].astype(np.int64)
+    gemm_end = float(release.max())
+    ts, ipt = info.tiles_per_slice, info.bm * info.bn // 512
+    own_first = op.cfg.rank * ts
+    slot_of_flag = {int(f): q for q, f in enumerate(flag_of_slot)}
+    own_release = np.array([release[slot_of_flag[own_first + t]] for t in range(ts)])
+    acq, done, items = rel(stamps[:, 1]), rel(stamps[:, 2]), stamps[:, 3].astype(np.int64)
+    launch_end = float(rel(launch[2]))
+    G = info.compute_wgs
+    rounds = []
+    for r in range((info.tiles + G - 1) // G):
+        sl = slice(r * G, min((r + 1) * G, info.tiles))
+        lo, hi = float(release[sl].min()), float(release[sl].max())
+        prev = rounds[-1]["release_last_us"] if rounds else 0.0
+        in_win = (done > prev) & (done <= hi)
+        rounds.append({"round": r, "release_first_us": lo, "release_last_us": hi,
+                       "own_tiles_released": int(np.sum((own_release > prev) & (own_release <= hi))),
+                       "sum_items_done_pct": 100.0 * float(items[in_win].sum()) / max(1, ts * ipt)})
+    before = 100.0 * float(items[done <= gemm_end].sum()) / max(1, ts * ipt)
+    return {"kernel_us": kernel_us, "launch_span_us": launch_end, "gemm_last_release_us": gemm_end,
+            "sum_before_gemm_end_pct": before, "sum_end_after_gemm_us": float(done.max()) - gemm_end,
+            "median_release_to_acquire_us": float(np.median(acq - own_release)),
+            "median_acquire_to_done_us": float(np.median(done - acq)),
+            "items_ok": bool(np.all(items == ipt)), "rounds": rounds}
+
+
+def timeline(args):
+    """One traced fused launch per reduce placement of a workload, after an
+    untraced timing of the same placement; writes a markdown summary."""
+    import torch
+
+    from tensor_gemm_reduce_amd import gemm_rs as gr
+
+    base = Case(args.workload, args)
+    cfg = base.cfg
+    rows = {}
+    for mode in ("tail", "stream", "adaptive"):
+        try:
+            op = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=base.rank, tile=args.tile, reduce_mode=mode,
+                           debug_flags=gr.DEBUG_TRACE)
+            plain = gr.GemmRS(cfg.M, cfg.N, cfg.K_local, rank=base.rank, tile=args.tile, reduce_mode=mode)
+        except gr.GemmRSError as e:
+            log(f"[{args.workload}] {mode}: {e}")
+            continue
+        run = lambda o: o.run(gr.MODE_FUSED, base.x, base.w, base.send, base.peers, base.out, base.local)
+        t = time_interleaved({"k": lambda: run(plain)}, rounds=8)
+        for _ in range(3):
+            run(op)
+        torch.cuda.synchronize()
+        if op.status() != gr.OK:
+            raise RuntimeError(f"{mode}: device status {gr.gemm_rs_strerror(op.status())}")
+        rows[mode] = timeline_summary(op, cfg, statistics.median(t["k"]))
+        log(f"[{args.workload}] {mode}: " + json.dumps({k: v for k, v in rows[mode].items() if k != "rounds"}))
+    cmd = " ".join(["python3", "bench.py"] + sys.argv[1:])
+    L = [f"# Slice-sum timeline, {args.workload}", "",
+         f"Command (on the GPU host, from the repository root): `{cmd}`", "",
+         "One traced fused launch per reduce placement (after three warm-up launches), read back with "
+         "`gemm_rs_debug_read`: the slot log's release times and the slice-sum stamps of the own tiles "
+         "(100 MHz counter; times in us from the launch's first workgroup start). `kernel us` is the same "
+         "placement's untraced launch time (interleaved graph replays). `sum before GEMM end` is the share "
+         "of the slice's items in own tiles whose last sum store precedes the GEMM's last tile release.",
+         f"Library source digest: {source_digest()}.", "",
+         "| placement | kernel us | GEMM last release us | launch span us | sum before GEMM end | "
+         "sum end after GEMM us | median release to acquire us | median acquire to done us |",
+         "|---|---|---|---|---|---|---|---|"]
+    for mode, r in rows.items():
+        L.append(f"| {mode} | {r['kernel_us']:.1f} | {r['gemm_last_release_us']:.1f} | {r['launch_span_us']:.1f} | "
+                 f"{r['sum_before_gemm_end_pct']:.1f}% | {r['sum_end_after_gemm_us']:.1f} | "
+                 f"{r['median_release_to_acquire_us']:.1f} | {r['median_acquire_to_done_us']:.1f} |")
+    for mode, r in rows.items():
+        L += ["", f"Per GEMM round, {mode} (rounds of {base.op.info.compute_wgs} slots; the sum's items counted "
+                  "in the round whose release window holds their last store):", "",
+              "| round | first release us | last release us | own tiles released | sum items done |",
+              "|---|---|---|---|---|"]
+        for x in r["rounds"]:
+            L.append(f"| {x['round']} | {x['release_first_us']:.1f} | {x['release_last_us']:.1f} | "
+                     f"{x['own_tiles_released']} | {x['sum_items_done_pct']:.1f}% |")
+        tail_pct = 100.0 - sum(x["sum_items_done_pct"] for x in r["rounds"])
+        L.append(f"| after | | | | {tail_pct:.1f}% |")
+    with open(args.timeline, "w") as f:
+        f.write("\n".join(L) + "\n")
+    if not all(r["items_ok"] for r in rows.values()):
+        raise RuntimeError("an own tile's item count is off")
 
 
 def allreduce_sweep(args):
@@ -661,6 +757,9 @@ def main():
         return
     if args.split_sweep:
         split_sweep(args)
+        return
+    if args.timeline:
+        timeline(args)
         return
     if args.allreduce_sweep:
         allreduce_sweep(args)
