@@ -81,6 +81,11 @@ def parse():
     p.add_argument("--timeline", metavar="OUT_MD",
                    help="trace one fused launch per reduce placement (tail, stream, adaptive) and write a "
                         "timeline summary of the GEMM's releases and the slice sum's stamps")
+    p.add_argument("--counter-probe", action="store_true",
+                   help="for rocprofv3 --pmc: two GEMM-only launches, two fused launches and two hipBLASLt "
+                        "GEMMs of the workload, each synchronized")
+    p.add_argument("--counters-from", nargs="+", metavar="COUNTER_CSV",
+                   help="markdown table of the per-kernel mean of every counter in rocprofv3 counter CSVs")
     p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -423,6 +428,50 @@ def traffic_probe(args):
     log(f"traffic probe done: copy {COPY_BYTES} B, {TRAFFIC_LAUNCHES} fused launches of {args.workload}")
 
 
+def counter_probe(args):
+    """Two launches each of the GEMM-only kernel, the fused kernel and
+    hipBLASLt's GEMM of the same product, each synchronized."""
+    import torch
+
+    from tensor_gemm_reduce_amd import gemm_rs as gr
+
+    c = Case(args.workload, args)
+    for fn in (lambda: c.run(gr.MODE_GEMM_ONLY), lambda: c.run(gr.MODE_FUSED), c.matmul):
+        for _ in range(2):
+            fn()
+            torch.cuda.synchronize()
+    log(f"counter probe done: {args.workload}")
+
+
+def counters_from(paths):
+    """Per-kernel means of rocprofv3 counter-collection CSVs (one table row
+    per kernel and counter pass), for kernels that ran at least 100 us."""
+    import collections
+    import csv
+
+    acc = collections.OrderedDict()
+    for path in paths:
+        per = collections.OrderedDict()
+        for r in csv.DictReader(open(path)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            e = per.setdefault(key, {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+        for (_, name), e in per.items():
+            if e["dur"] < 100:
+                continue
+            short = name if len(name) <= 90 else name[:40] + "..." + name[-47:]
+            a = acc.setdefault(short, {})
+            for k, v in e.items():
+                a.setdefault(k, []).append(v)
+    for name, a in acc.items():
+        print(f"**{name}**\n")
+        print("| counter | mean per launch |")
+        print("|---|---|")
+        for k, v in a.items():
+            print(f"| {'duration us (under counters)' if k == 'dur' else k} | {sum(v) / len(v):.4g} |")
+        print()
+
+
 def traffic_from(args):
     """HBM bytes per fused launch from the FETCH_SIZE and WRITE_SIZE passes,
     each scaled by what the same counter reads for the copy of known size."""
@@ -731,6 +780,9 @@ def stats_summary(path):
 
 def main():
     args = parse()
+    if args.counters_from:
+        counters_from(args.counters_from)
+        return
     if args.stats_summary:
         stats_summary(args.stats_summary)
         return
@@ -754,6 +806,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(args)
+        return
+    if args.counter_probe:
+        counter_probe(args)
         return
     if args.split_sweep:
         split_sweep(args)
