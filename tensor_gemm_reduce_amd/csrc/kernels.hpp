@@ -862,9 +862,11 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
 // The stream waves' K loop is unrolled by four, so the sources, the reset,
 // the store and the wait counts are constants of the step's code, which has
 // no branch and is interleaved with the step's MFMAs.  A tile runs the
-// groups only if the workgroup has latched (below) when the tile begins and
-// the wave still has items; other tiles run the plain loop, and a wave whose
-// last item was begun in the previous tile finishes it first.  A group past
+// groups if the workgroup has latched (below) when the tile begins and the
+// wave still has items, or, when the workgroup's later tiles hold fewer
+// groups than the wave has items left, from the step after the tile's probe
+// latches; other tiles run the plain loop, and a wave whose last item was
+// begun in the previous tile finishes it first.  A group past
 // the wave's last item issues the same instructions through an empty buffer
 // resource (they read zeros) and its store goes past its resource.  Loads land in two 2 KiB LDS slot pairs, pair PH & 1: a step
 // reads the pair of the step two back at its start and refills it once the
@@ -903,6 +905,7 @@ struct Stream {
     int real_prev;        // the previous group's
     uint32_t ioff, coff;  // this lane's byte offset of this / the previous group's item (kOob: none)
     bool latched;         // every own tile of the workgroup's items is released
+    int tiles_left;       // the workgroup's tiles after the current one
     int t_lo, t_hi;       // own tiles of the workgroup's items (t_hi < t_lo: none)
     uint32_t epoch;
     uint32_t slice_bytes;
@@ -949,6 +952,7 @@ __device__ __forceinline__ void stream_init(Stream& s, const Args& a, char* stre
     s.ioff = kOob;
     s.coff = kOob;
     s.latched = s.t_hi < s.t_lo;  // nothing to wait for
+    s.tiles_left = uni(pos < a.g.tiles ? (a.g.tiles - pos + C - 1) / C : 0);
     s.epoch = (uint32_t)uni((int)epoch);
     s.slice_bytes = a.slice_bytes;
     s.acc = f32x8{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -1494,7 +1498,8 @@ __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileS
             // a tile runs the stream's groups only while this wave has items
             // to sum and the slice's tiles are ready; otherwise the plain
             // loop, after finishing an item begun in the previous tile
-            const bool active = s.latched && s.item < s.end;
+            s.tiles_left -= 1;
+            bool active = s.latched && s.item < s.end;
             if (!active && s.real_cur) stream_settle(s, a);
             // (trace: a wave that has summed all its items records them at the
             // next tile start; its range then starts at its end)
@@ -1505,8 +1510,16 @@ __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileS
             stage_barrier();
             load_frags<C>(lds, 0, xf[0], wf[0]);
             int kt = 0;
+            if (!s.latched && (int64_t)s.tiles_left * ((nk - 1) / 4) < (int64_t)(s.end - s.item)) {
+                // the later tiles' groups cannot hold this wave's items: begin
+                // the groups in this tile, after the step whose probe latches
+                for (; kt + 1 < nk && kt <= kProbe; ++kt) L::plain_step(a, lds, st, hk, s, kt, xf, wf);
+                active = s.latched && s.item < s.end;
+            }
             if (active)
             for (; kt + 4 < nk; kt += 4) {
+                // (the previous tile's epilogue stores are younger than the
+                // previous group's loads only in a tile's first group)
                 const bool first = kt == 0;
                 L::template stream_step_k<0>(a, lds, st, hk, s, kt, first, xf, wf);
                 L::template stream_step_k<1>(a, lds, st, hk, s, kt + 1, first, xf, wf);
