@@ -880,10 +880,13 @@ __device__ __forceinline__ void drain_items(const Args& a, const ItemMap& m, int
 // The local partial of an item may be read only once its tile is released.
 // A workgroup's four stream waves own consecutive items, spanning own tiles
 // t_lo .. t_hi; until all of them are released (latched once seen), tiles
-// run the plain loop.  Loader wave 0 probes the tiles' flags with device-scope loads
-// into LDS right after the barrier of step kProbe - 1, while the workgroup
-// has not latched; the wait of step kProbe covers them, and after its
-// barrier every wave reads the probe and latches together.  The previous
+// run the plain loop.  Loader wave 0 probes the tiles' flags with device-scope
+// loads into LDS right after the barrier of step kProbe - 1 (and of every
+// fourth step after it), while the workgroup has not latched; the wait of the
+// next step covers them, and after its barrier every wave reads the probe and
+// latches together.  A tile's groups begin at its start, or, when the later
+// tiles cannot hold a wave's remaining items, right after the latching step.
+// The previous
 // tile's flag is published after the barrier of step kPub: the stream waves'
 // epilogue stores are older than the loads its wait covers.  Items a stream
 // wave has not finished after the workgroup's last tile are summed there by
@@ -1360,8 +1363,10 @@ struct SplitLoop {
     {
         if (kt == kPub) publish_pending<false>(a, hk);
         if (!s.latched) {
-            if (kt == kProbe - 1 && prober) stream_probe_issue(s, a);
-            if (kt == kProbe) {
+            // a probe after the barrier of step kProbe - 1 + 4j, read after
+            // the next one, until the workgroup latches
+            if (kt >= kProbe - 1 && ((kt - (kProbe - 1)) & 3) == 0 && prober) stream_probe_issue(s, a);
+            if (kt >= kProbe && ((kt - kProbe) & 3) == 0) {
                 stream_probe_read(s);
                 if (a.trace_on && threadIdx.x >= C::LW * 64) {
                     const uint32_t t = now32();
@@ -1513,7 +1518,8 @@ __device__ __forceinline__ void tile_kloop_split(const Args& a, char* lds, TileS
             if (!s.latched && (int64_t)s.tiles_left * ((nk - 1) / 4) < (int64_t)(s.end - s.item)) {
                 // the later tiles' groups cannot hold this wave's items: begin
                 // the groups in this tile, after the step whose probe latches
-                for (; kt + 1 < nk && kt <= kProbe; ++kt) L::plain_step(a, lds, st, hk, s, kt, xf, wf);
+                for (; kt + 1 < nk && kt < kProbe; ++kt) L::plain_step(a, lds, st, hk, s, kt, xf, wf);
+                for (; kt + 1 < nk && !s.latched; ++kt) L::plain_step(a, lds, st, hk, s, kt, xf, wf);
                 active = s.latched && s.item < s.end;
             }
             if (active)
