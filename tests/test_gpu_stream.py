@@ -2,9 +2,10 @@
 and four stream waves per compute workgroup, the slice sum streamed through
 the K loop once the workgroup's own tiles are released, the rest summed after
 the last tile.  Shapes cover one round (nothing can stream: all in the
-drain), several rounds (the stream latches in a later round), and ragged
-tiles; every result is compared with the oracle bit for bit (integer inputs)
-or with the sum after the last tile (normal inputs, same sum order)."""
+drain), several rounds (the stream latches in a later round), ragged tiles,
+and tiles long enough for the stream's groups to run; every result is
+compared with the oracle bit for bit (integer inputs) or with the sum after
+the last tile (normal inputs, same sum order)."""
 import numpy as np
 import pytest
 import torch
@@ -26,6 +27,17 @@ SHAPES = {
     "four_rounds": synthetic.Config("st_four", 43, 8 * 2048, 4096, 512),
     # S = 384 (a ragged tile row), N = 4160 (a ragged tile column), 7 K steps
     "ragged": synthetic.Config("st_ragged", 44, 8 * 384, 4160, 448),
+}
+
+# Shapes whose tiles are long enough for the stream's groups (four K steps
+# each after the probe): with many later tiles the groups begin at a tile's
+# start; with few (three rounds) they begin inside the tile whose probe
+# latches, after a later probe if the first one came too early.
+GROUP_SHAPES = {
+    # S = 2048, 128 own tiles of 1024 (four rounds), 48 K steps
+    "from_tile_start": synthetic.Config("st_groups_a", 47, 8 * 2048, 4096, 3072),
+    # S = 1024, 96 own tiles of 768 (three rounds), 32 K steps
+    "in_latching_tile": synthetic.Config("st_groups_b", 48, 8 * 1024, 6144, 2048),
 }
 
 
@@ -71,12 +83,13 @@ def test_stream_equals_tail_on_normal_inputs(name):
     assert np.array_equal(got["stream"][8], oracle.slice_sum(got["stream"][7], peers, tp=8))
 
 
-def test_stream_alternating_inputs_and_graph_replays():
+@pytest.mark.parametrize("name", ["four_rounds", "in_latching_tile"])
+def test_stream_alternating_inputs_and_graph_replays(name):
     """Back-to-back runs alternate two input sets on shared outputs with the
     local slice poisoned before each run (a stream wave that read a tile
     before its release, or a stale copy, would give a wrong slice); then a
     captured run is replayed with eager runs in between."""
-    base = SHAPES["four_rounds"]
+    base = {**SHAPES, **GROUP_SHAPES}[name]
     cfgs = [synthetic.Config("st_alt_a", 45, base.M, base.N, base.K_local),
             synthetic.Config("st_alt_b", 46, base.M, base.N, base.K_local)]
     rank = 6
@@ -165,3 +178,29 @@ def test_stream_modes_agree_and_all_reduce_sums_after_the_last_tile():
     b.refill()
     run(op, b, gr.MODE_FUSED)
     assert np.array_equal(host(b.out), fused[-1])
+
+
+@pytest.mark.parametrize("name", list(GROUP_SHAPES))
+def test_stream_groups_sum_the_slice_during_the_gemm(name):
+    """Bit-exact on integer inputs, and the slice-sum stamps of a traced run
+    show most own tiles summed before the GEMM's last tile is released (the
+    sum after the last tile alone would finish none of them before it)."""
+    cfg = GROUP_SHAPES[name]
+    rank = 4
+    x, w, peers = synthetic.make_inputs(cfg, "integer")
+    _, local_o, out_o = oracle.gemm_rs(x, w, peers, tp=8, rank=rank)
+    op = _op(cfg, rank, debug_flags=gr.DEBUG_TRACE, **STREAM)
+    b = Buffers(x, w, peers, cfg.S, cfg.N)
+    run(op, b)
+    run(op, b)  # (stamps of the second run)
+    assert np.array_equal(host(b.local), local_o)
+    assert np.array_equal(host(b.out), out_o)
+    log, flags, stamps, launch = op.debug_read(sums=True)
+    info = op.info
+    assert np.all(stamps[:, 3] == info.bm * info.bn // 512)
+    d = lambda p, q: (p.astype(np.int64) - q.astype(np.int64) + (1 << 31)) % (1 << 32) - (1 << 31)
+    release = log[:, 2].astype(np.int64) | (log[:, 3].astype(np.int64) << 32)
+    last = np.uint32(int(release.max()) & 0xFFFFFFFF)
+    done = stamps[:, 2]
+    early = int(np.sum(d(done, np.full_like(done, last)) < 0))
+    assert early >= len(done) // 2, (early, len(done))
