@@ -118,7 +118,7 @@ extern "C" {
                                    waves of each compute workgroup issue no stage
                                    loads and stream the slice sum between their
                                    MFMAs (two loads and a store per K step, each
-                                   load in flight for three steps) once the
+                                   load in flight for two steps) once the
                                    workgroup's own tiles are released; the rest
                                    is summed after the last tile.  Tile flags and
                                    device-scope stores only.  The all-reduce's

@@ -1368,7 +1368,9 @@ struct SplitLoop {
             if (kt >= kProbe - 1 && ((kt - (kProbe - 1)) & 3) == 0 && prober) stream_probe_issue(s, a);
             if (kt >= kProbe && ((kt - kProbe) & 3) == 0) {
                 stream_probe_read(s);
-                if (a.trace_on && threadIdx.x >= C::LW * 64) {
+                // (stamps: a tile's first probe and the latching one; stamping
+                // every probe would crowd the stamp words with atomics)
+                if (a.trace_on && threadIdx.x >= C::LW * 64 && (kt == kProbe || s.latched)) {
                     const uint32_t t = now32();
                     stream_trace(a, s, s.first, s.end, t, s.latched ? t : 0xFFFFFFFFu, 0u, false);
                 }
