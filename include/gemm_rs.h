@@ -101,10 +101,10 @@ extern "C" {
 #define GEMM_RS_TILE_COUNT 7
 
 /* ---- where the slice sum runs without dedicated reducers ------------------ */
-#define GEMM_RS_REDUCE_AUTO 0   /* STREAM for the 256x256 tile with K_local >= 384
-                                   and at least 768 tiles (three rounds of a
-                                   256-CU device) unless num_reducers is -2;
-                                   TAIL otherwise                                 */
+#define GEMM_RS_REDUCE_AUTO 0   /* STREAM for the 256x256 tile with
+                                   384 <= K_local < 3072 and at least 768 tiles
+                                   (three rounds of a 256-CU device) unless
+                                   num_reducers is -2; TAIL otherwise            */
 #define GEMM_RS_REDUCE_TAIL 1   /* each compute workgroup sums its share of the
                                    slice after its last tile                      */
 #define GEMM_RS_REDUCE_CORESIDENT 2 /* one reducer workgroup per CU beside the

@@ -40,8 +40,10 @@ typedef TileCfg<64, 128, 64, 2, 2, 2, 32> Tile64x128;
 typedef TileCfg<128, 128, 32, 3, 2, 2, 32> Tile128x128;
 typedef TileCfg<128, 256, 32, 4, 2, 2, 32> Tile128x256;
 typedef TileCfg<256, 128, 32, 4, 2, 2, 32> Tile256x128;
-typedef TileCfg<256, 256, 64, 2, 2, 4, 32> Tile256x256;
-// the stream kernel of the 256x256 tile: four loader waves, four stream waves
+// four waves, one per SIMD, on the long-tail K loop (tile_kloop_long)
+typedef TileCfg<256, 256, 64, 2, 2, 2, 32> Tile256x256;
+// the stream kernel of the 256x256 tile: eight waves, four of them loading
+// the stages and four streaming the slice sum
 typedef TileCfg<256, 256, 64, 2, 2, 4, 32, 4> Tile256x256S;
 
 struct TileDesc {
@@ -59,7 +61,9 @@ struct TileDesc {
     const void* stream_kernel;   // fused, reduce_mode STREAM (or null)
     const void* kernel_dyn;      // fused, reduce_mode ADAPTIVE (the sum between the tiles)
     int stream_lds_bytes;        // its stages, stream slots and probe area
+    int stream_threads;          // its workgroup size
     int fused_lds_bytes;         // LDS of `kernel` (set by variant_desc)
+    int fused_threads;           // workgroup size of `kernel` (set by variant_desc)
 };
 
 // Eight-wave tiles run one workgroup per CU with two waves per SIMD; four-wave
@@ -94,20 +98,20 @@ TileDesc desc()
     // occupancy is set by the stages
     constexpr bool two = C::LDS_BYTES <= 80 * 1024 - 64;
     const void* sk = nullptr;
-    int slds = 0;
+    int slds = 0, sthreads = 0;
     if constexpr (!std::is_void<CS>::value) {
-        static_assert(CS::LDS_BYTES == C::LDS_BYTES && CS::THREADS == C::THREADS &&
-                          CS::LDS_BYTES + kStreamLds <= 160 * 1024 - 256,
-                      "the stream kernel's LDS");
+        static_assert(CS::BM == C::BM && CS::BN == C::BN && CS::LDS_BYTES + kStreamLds <= 160 * 1024 - 256,
+                      "the stream kernel's tile and LDS");
         sk = reinterpret_cast<const void*>(&fused_kernel_8w<CS, true>);
         slds = CS::LDS_BYTES + kStreamLds;
+        sthreads = CS::THREADS;
     }
     return TileDesc{C::BM, C::BN, C::BK, C::THREADS, C::WAVES == 4 && two ? 2 : 1, C::LDS_BYTES,
                     kernel_for<C, true, two>(), kernel_for<C, false, two>(),
                     kernel_for<C, true, two, kVarNt>(), kernel_for<C, false, two, kVarNt>(),
                     kernel_for<C, true, two, kVarRows>(),
                     ag_kernel_for<C, true, two>(), ag_kernel_for<C, false, two>(), sk,
-                    kernel_for<C, true, two, kVarDyn>(), slds, C::LDS_BYTES};
+                    kernel_for<C, true, two, kVarDyn>(), slds, sthreads, C::LDS_BYTES, C::THREADS};
 }
 
 TileDesc tile_desc(int id)
@@ -146,12 +150,17 @@ int auto_tile(const gemm_rs_config& c)
 int resolve_tile(const gemm_rs_config& c) { return c.tile == GEMM_RS_TILE_AUTO ? auto_tile(c) : c.tile; }
 
 // Where the slice sum of a fused run without dedicated reducers runs.
-// AUTO: the stream where it can run beside the GEMM: the 256x256 tile, at
-// least kProbe + 2 K steps, and three or more rounds of tiles on a 256-CU
-// device (768 tiles; the own slice, an eighth of them, is released during the
-// first rounds and the stream runs in the later ones).  Otherwise the sum after
-// the last tile.
+// AUTO: the stream where it can run beside the GEMM and pays for its slower
+// GEMM: the 256x256 tile, at least kProbe + 2 K steps, three or more rounds of
+// tiles on a 256-CU device (768 tiles; the own slice, an eighth of them, is
+// released during the first rounds and the stream runs in the later ones),
+// and K_local below kAutoStreamMaxK.  The stream kernel is the eight-wave
+// tile (four waves stream); the sum after the last tile runs on the faster
+// four-wave tile, whose lead grows with K while the sum's share of the work
+// shrinks as 1/K_local (measured: the stream ahead at K_local = 2048, behind
+// at 3584).  Otherwise the sum after the last tile.
 constexpr int kAutoStreamTiles = 3 * 256;
+constexpr int kAutoStreamMaxK = 3072;
 
 int resolve_reduce_mode(const gemm_rs_config& c)
 {
@@ -162,7 +171,8 @@ int resolve_reduce_mode(const gemm_rs_config& c)
             return GEMM_RS_REDUCE_TAIL;
         const int64_t S = c.M / c.tp;
         const int64_t tiles = (int64_t)c.tp * ((S + 255) / 256) * (((int64_t)c.N + 255) / 256);
-        return tiles >= kAutoStreamTiles ? GEMM_RS_REDUCE_STREAM : GEMM_RS_REDUCE_TAIL;
+        return tiles >= kAutoStreamTiles && c.K_local < kAutoStreamMaxK ? GEMM_RS_REDUCE_STREAM
+                                                                          : GEMM_RS_REDUCE_TAIL;
     }
     return c.reduce_mode;
 }
@@ -408,6 +418,7 @@ static TileDesc variant_desc(const gemm_rs_config& c, int* variant)
     if (mode == GEMM_RS_REDUCE_STREAM) {
         td.kernel = td.stream_kernel;
         td.fused_lds_bytes = td.stream_lds_bytes;
+        td.fused_threads = td.stream_threads;
         *variant = 3;
     } else if (mode == GEMM_RS_REDUCE_ADAPTIVE) {
         td.kernel = td.kernel_dyn;
@@ -429,7 +440,7 @@ static int kernel_setup(const TileDesc& td, int* occ)
 {
     HIP_TRY(hipFuncSetAttribute(td.kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.fused_lds_bytes));
     HIP_TRY(hipFuncSetAttribute(td.gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, td.lds_bytes));
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, td.kernel, td.threads, td.fused_lds_bytes));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, td.kernel, td.fused_threads, td.fused_lds_bytes));
     return GEMM_RS_OK;
 }
 
@@ -610,7 +621,8 @@ static int launch_gemm(gemm_rs_handle* h, Args& a, bool fused, hipStream_t s, bo
     // (a GEMM-only launch runs on the compute workgroups' grid: the
     // co-resident reducers' extra workgroup per CU is not part of the GEMM)
     if (!fused) a.num_compute = h->gemm_grid;
-    HIP_TRY(hipLaunchKernel(k, dim3(fused ? h->grid : h->gemm_grid), dim3(h->td.threads), params,
+    HIP_TRY(hipLaunchKernel(k, dim3(fused ? h->grid : h->gemm_grid),
+                            dim3(fused && !tail ? h->td.fused_threads : h->td.threads), params,
                             fused ? (tail ? h->tail_lds : h->fused_lds) : h->td.lds_bytes, s));
     return GEMM_RS_OK;
 }

@@ -182,6 +182,10 @@ struct TileCfg {
     // One workgroup per CU (four waves whose stages fit only once, or eight
     // waves) with every wave loading: the K loop is pipelined across steps.
     static constexpr bool XP = LDS_BYTES > 80 * 1024 - 64 && KSUB % 2 == 0;
+    // Four waves (one per SIMD) with four substeps per stage of two: the
+    // barrier follows a step's first substep and the refill spreads over the
+    // other three (tile_kloop_long).
+    static constexpr bool LT = XP && WAVES == 4 && KSUB == 4 && NS == 2;
 };
 
 template <int MF> struct AccT;
@@ -1248,10 +1252,136 @@ __device__ __forceinline__ void publish_pending(const Args& a, StepHooks& hk)
 // stage waited for (stages of the prologue).  The first barrier that covers
 // those stores (the one waiting for stage NS-1, the first refill) publishes
 // the previous tile's flag.
+// The K loop of the four-wave two-stage tiles (C::LT).  With one wave per
+// SIMD nothing else fills the MFMA pipe while a wave stalls on issuing a
+// direct load, and a refill issued in a burst fills the TA's command queue
+// (measured on the two-stage eight-wave loop: the queue full a quarter of the
+// cycles).  So the barrier follows a step's first substep, which reads the
+// fragments of substeps 2 and 3; the other three substeps form the tail,
+// where MFMA m is followed by refill load m/3 (every third slot) and, from
+// slot 1 on, every third slot by a fragment read of the next step's
+// substeps 0 and 1, in that order.  Four fragment sets, one per substep; a
+// set is rewritten only after its substep's MFMAs have been issued.
+template <class C, bool ROWS = false>
+__device__ __forceinline__ void tile_kloop_long(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
+                                                StepHooks& hk)
+{
+    static_assert(C::LT && C::EW == 0, "four waves, four substeps, two stages");
+    constexpr int kMf = C::FM * C::FN;  // MFMAs per substep
+    constexpr int kDs = C::FM + C::FN;  // fragment reads per substep
+    constexpr int kLs = 3;              // tail slots per refill load
+    static_assert(C::LPS * kLs <= 3 * kMf && 1 + 3 * (2 * kDs - 1) < 3 * kMf, "the tail holds the refill and the reads");
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < AccT<C::MF>::N; ++e) st.acc[i][j][e] = 0.0f;
+
+    const int K = a.g.K;
+    const int nk = job.nk;
+    if (nk > 0) {
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(job.xp), 0, (uint32_t)uni((int)job.xbytes), kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, 0, a.w_bytes, kRsrcFlags);
+        bf16x8 x0[C::FM], w0[C::FN], x1[C::FM], w1[C::FN], x2[C::FM], w2[C::FN], x3[C::FM], w3[C::FN];
+        const int wave = uni((int)(threadIdx.x >> 6));
+        const int lane = threadIdx.x & 63;
+        const int wm = wave / C::WAVES_N, wc = wave % C::WAVES_N;
+        const int lr = lane % C::MF;
+        const uint32_t step = (uint32_t)uni((C::LTHREADS / C::CPR) * K * 2);
+        // stage 0 came from the prologue, before the previous tile's stores
+        if (hk.stores)
+            wait_vmcnt<C::STORES>();
+        else
+            wait_vmcnt<0>();
+        stage_barrier();
+        issue_stage<C>(job.lp, rx, rw, lds + C::STAGE_BYTES, C::BK, K);
+        load_frags<C>(lds, 0, x0, w0);
+        load_frags<C>(lds, 1, x1, w1);
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            char* cur = lds + (kt & 1) * C::STAGE_BYTES;
+            const char* nxt = lds + ((kt + 1) & 1) * C::STAGE_BYTES;
+            load_frags<C>(cur, 2, x2, w2);
+            load_frags<C>(cur, 3, x3, w3);
+            mfma_substep<C>(st, x0, w0);
+#pragma unroll
+            for (int m = 0; m < kMf; ++m) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                if (m < 2 * kDs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kDs > kMf ? 2 : 1, 0);
+            }
+            wait_vmcnt<0>();
+            wait_lgkm0();
+            stage_barrier();
+            if (kt == 0) publish_pending<ROWS>(a, hk);
+            // the refill of this step's buffer with stage kt + 2, as in issue_stage
+            const int k0 = (kt + 2) * C::BK;
+            const bool in_k = job.lp.kc < K - k0;
+            const uint32_t a0 = in_k ? job.lp.a_off + (uint32_t)k0 * 2u : kOob;
+            const uint32_t b0 = in_k ? job.lp.b_off + (uint32_t)k0 * 2u : kOob;
+#pragma unroll
+            for (int m = 0; m < 3 * kMf; ++m) {
+                const int ss = m / kMf, i = (m % kMf) / C::FN, j = m % C::FN;
+                if (ss == 0)
+                    st.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[j], x1[i], st.acc[i][j], 0, 0, 0);
+                else if (ss == 1)
+                    st.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[j], x2[i], st.acc[i][j], 0, 0, 0);
+                else
+                    st.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w3[j], x3[i], st.acc[i][j], 0, 0, 0);
+                if (m % kLs == 0 && m / kLs < C::LPS) {
+                    const int li = m / kLs;
+                    if (li < C::A_LD)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (lds_void_t*)(cur + (li * C::LTHREADS + wave * 64) * 16), 16, a0 + (uint32_t)li * step, 0,
+                            0, 0);
+                    else
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rw, (lds_void_t*)(cur + C::A_BYTES + ((li - C::A_LD) * C::LTHREADS + wave * 64) * 16), 16,
+                            b0 + (uint32_t)(li - C::A_LD) * step, 0, 0, 0);
+                }
+                if (m >= 1 && (m - 1) % 3 == 0 && (m - 1) / 3 < 2 * kDs) {
+                    // the next step's substep sb fragment di, as in load_frags
+                    const int dd = (m - 1) / 3, sb = dd / kDs, di = dd % kDs;
+                    const int c = sb * (C::KF / 8) + lane / C::MF;
+                    if (di < C::FM) {
+                        const int r = wm * C::WTM + di * C::MF + lr;
+                        const bf16x8 v =
+                            *reinterpret_cast<const bf16x8*>(nxt + r * C::ROW_BYTES + ((c ^ swz<C::CPR>(r)) << 4));
+                        if (sb == 0) x0[di] = v; else x1[di] = v;
+                    } else {
+                        const int r = wc * C::WTN + (di - C::FM) * C::MF + lr;
+                        const bf16x8 v = *reinterpret_cast<const bf16x8*>(nxt + C::A_BYTES + r * C::ROW_BYTES +
+                                                                          ((c ^ swz<C::CPR>(r)) << 4));
+                        if (sb == 0) w0[di - C::FM] = v; else w1[di - C::FM] = v;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // the last step (its substep 0 and 1 fragments are in sets 0 and 1)
+        const char* cur = lds + ((nk - 1) & 1) * C::STAGE_BYTES;
+        load_frags<C>(cur, 2, x2, w2);
+        load_frags<C>(cur, 3, x3, w3);
+        mfma_substep<C>(st, x0, w0);
+        mfma_substep<C>(st, x1, w1);
+        mfma_substep<C>(st, x2, w2);
+        mfma_substep<C>(st, x3, w3);
+    }
+    // the zero-filling loads past the end drain; every wave finishes reading
+    // LDS before the next tile's loads overwrite it; a flag still pending
+    // (nk < 2) is published here
+    wait_vmcnt<0>();
+    stage_barrier();
+    publish_pending<ROWS>(a, hk);
+}
+
 template <class C, bool ROWS = false>
 __device__ __forceinline__ void tile_kloop_xp(const Args& a, char* lds, TileState<C>& st, const TileJob<C>& job,
                                               StepHooks& hk)
 {
+    if constexpr (C::LT) {
+        tile_kloop_long<C, ROWS>(a, lds, st, job, hk);
+        return;
+    }
     static_assert(C::KSUB % 2 == 0, "substep s of every step uses fragment buffer s % 2");
     static_assert(C::EW == 0, "every wave loads stages");
 #pragma unroll

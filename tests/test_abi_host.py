@@ -163,8 +163,12 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
     (dict(num_reducers=8), gr.REDUCE_TAIL),           # dedicated reducers run the sum
     (dict(M=512, K_local=1024), gr.REDUCE_TAIL),     # o_proj: 64x128 tile
     # automatic: the stream from 768 tiles of 256x256 (three rounds of 256 CUs)
+    # with K_local below 3072; the sum after the last tile from there on
     (dict(M=8192, N=6144, K_local=2048), gr.REDUCE_STREAM),          # 768 tiles
-    (dict(M=32768, N=8192, K_local=3584), gr.REDUCE_STREAM),
+    (dict(M=32768, N=8192, K_local=2048), gr.REDUCE_STREAM),
+    (dict(M=32768, N=8192, K_local=3008), gr.REDUCE_STREAM),
+    (dict(M=32768, N=8192, K_local=3072), gr.REDUCE_TAIL),
+    (dict(M=32768, N=8192, K_local=3584), gr.REDUCE_TAIL),           # large prefill
     (dict(M=8192, N=5888, K_local=2048), gr.REDUCE_TAIL),            # 736 tiles
     (dict(M=8192, N=6144, K_local=320), gr.REDUCE_TAIL),             # five K steps
     (dict(M=8192, N=6144, K_local=2048, num_reducers=-2), gr.REDUCE_ADAPTIVE),  # the controller
