@@ -503,7 +503,7 @@ def traffic_from(args):
 
 
 SPLIT_KNOBS = (
-    [dict(reduce_mode="tail")] + [dict(num_reducers=r) for r in (2, 4, 8, 16, 32, 64)]
+    [dict(reduce_mode="tail")] + [dict(num_reducers=r) for r in (2, 4, 8, 12, 16, 24, 32, 64)]
     + [dict(reduce_mode="stream"), dict(reduce_mode="adaptive")]
     + [dict(reduce_mode="tail", flag_stride=32), dict(num_reducers=8, flag_stride=32)]
     + [dict(reduce_mode="tail", tile_stores=1), dict(num_reducers=8, tile_stores=1)]

@@ -1965,27 +1965,46 @@ __device__ void reducer_role(const Args& a, uint32_t epoch)
         const TileCoord t = decode_slot(a.g, u);
         const int rows = tile_rows(a.g, t), cols = tile_cols(a.g, t);
         const int cpr = cols >> 3;
+        const int n = rows * cpr;
         const uint16_t* local = a.dst[a.g.rank];
-        for (int c = threadIdx.x; c < rows * cpr; c += (int)blockDim.x) {
-            const int r = c / cpr;
-            const int64_t off = (int64_t)(t.tml * a.g.bm + r) * a.g.N + t.tn * a.g.bn + (c - r * cpr) * 8;
-            u32x4 v[kPeers + 1];
+        // four chunks per thread and pass: all their loads are issued before
+        // any sum is stored (the stores could alias the loads of a later
+        // pass, so the compiler keeps passes apart).  A reducer workgroup has
+        // a CU to itself; the loads in flight set its share of HBM bandwidth.
+        constexpr int kCh = 4;
+        for (int c0 = threadIdx.x; c0 < n; c0 += kCh * (int)blockDim.x) {
+            int64_t off[kCh];
+            bool on[kCh];
+            u32x4 v[kCh][kPeers + 1];
 #pragma unroll
-            for (int s = 0; s < kPeers; ++s)
-                v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.peers[s] + off));
-            // the local slice at device scope (two 8-byte relaxed agent-scope loads)
-            const uint64_t* lp = reinterpret_cast<const uint64_t*>(local + off);
-            const uint64_t l0 = __hip_atomic_load(lp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t l1 = __hip_atomic_load(lp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v[kPeers] = u32x4{(uint32_t)l0, (uint32_t)(l0 >> 32), (uint32_t)l1, (uint32_t)(l1 >> 32)};
-            f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+            for (int h = 0; h < kCh; ++h) {
+                const int c = c0 + h * (int)blockDim.x;
+                on[h] = c < n;
+                const int cc = on[h] ? c : c0;
+                const int r = cc / cpr;
+                off[h] = (int64_t)(t.tml * a.g.bm + r) * a.g.N + t.tn * a.g.bn + (cc - r * cpr) * 8;
 #pragma unroll
-            for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[s]);
-            const u32x4 o = pack8(acc);
-            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + off));
-            if (a.gather_on) {
+                for (int s = 0; s < kPeers; ++s)
+                    v[h][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.peers[s] + off[h]));
+                // the local slice at device scope (two 8-byte relaxed agent-scope loads)
+                const uint64_t* lp = reinterpret_cast<const uint64_t*>(local + off[h]);
+                const uint64_t l0 = __hip_atomic_load(lp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t l1 = __hip_atomic_load(lp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v[h][kPeers] = u32x4{(uint32_t)l0, (uint32_t)(l0 >> 32), (uint32_t)l1, (uint32_t)(l1 >> 32)};
+            }
 #pragma unroll
-                for (int i = 0; i < kPeers; ++i) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.gather[i] + off));
+            for (int h = 0; h < kCh; ++h) {
+                if (!on[h]) continue;
+                f32x8 acc = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s <= kPeers; ++s) acc = add8(acc, v[h][s]);
+                const u32x4 o = pack8(acc);
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + off[h]));
+                if (a.gather_on) {
+#pragma unroll
+                    for (int i = 0; i < kPeers; ++i)
+                        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.gather[i] + off[h]));
+                }
             }
         }
         if (a.trace_on) {
