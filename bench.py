@@ -59,8 +59,8 @@ def parse():
                    help="dedicated reducer workgroups: -1 the plan's default, -2 the adaptive controller")
     p.add_argument("--reduce-mode", default="auto", choices=["auto", "tail", "coresident", "stream", "adaptive"],
                    help="where the fused launch sums the slice without dedicated reducers")
-    p.add_argument("--tile-stores", default="device", choices=["device", "nt"],
-                   help="cache policy of the routed tile stores (nt: non-temporal hint)")
+    p.add_argument("--tile-stores", default="auto", choices=["auto", "device", "nt"],
+                   help="cache policy of the routed tile stores (nt: non-temporal hint; auto: the library's choice)")
     p.add_argument("--cold", action="store_true",
                    help="also time the fused, GEMM-only and reduce launches with cold caches (a 512 MiB "
                         "buffer written before each launch)")
@@ -904,7 +904,7 @@ def main():
         "T_reduce_us": m["T_reduce_us"]["median_us"],
         "reduce_gbs": m["reduce_gbs"],
         "reduce_mode": m["reduce_mode"],
-        "tile_stores": args.tile_stores,
+        "tile_stores": {gr.STORES_DEVICE: "device", gr.STORES_NONTEMPORAL: "nt"}[c.op.info.tile_stores],
         "cold": m.get("cold"),
         "T_fused_tail_us": (m.get("T_fused_tail_us") or {}).get("median_us"),
         "overlap_tail": m.get("overlap_tail"),

@@ -145,6 +145,14 @@ extern "C" {
                                         the tiles are not kept in L2 for reuse.
                                         A separate kernel variant (also of
                                         GEMM_ONLY); not with row counters      */
+#define GEMM_RS_STORES_AUTO 2        /* NONTEMPORAL for the 256x256 tile with at
+                                        least 1024 tiles when the sum runs
+                                        after the tiles (TAIL, also with
+                                        dedicated reducers) with tile flags;
+                                        DEVICE otherwise.  Measured: 0.3-2.5%
+                                        faster from 8 rounds of 256x256 tiles,
+                                        no gain below, 1% slower on o_proj's
+                                        64x128 tile                           */
 
 /* ---- how a released tile is signalled ------------------------------------ */
 #define GEMM_RS_FLAGS_TILE 0        /* one ready flag per tile, set to the run's
@@ -209,6 +217,7 @@ typedef struct gemm_rs_info {
                                  no dedicated reducers                        */
     int32_t split_state;      /* 0: fixed reducer count; 1: the adaptive
                                  controller decides on the device           */
+    int32_t tile_stores;      /* resolved GEMM_RS_STORES_* (never AUTO)      */
 } gemm_rs_info;
 
 typedef struct gemm_rs_handle gemm_rs_handle;

@@ -50,7 +50,8 @@ REDUCE_MODES = {"auto": 0, "tail": 1, "coresident": 2, "stream": 3, "adaptive": 
 
 STORES_DEVICE = 0
 STORES_NONTEMPORAL = 1
-TILE_STORES = {"device": 0, "nt": 1}
+STORES_AUTO = 2
+TILE_STORES = {"device": 0, "nt": 1, "auto": 2}
 
 FLAGS_TILE = 0
 FLAGS_ROW_COUNTER = 1
@@ -79,7 +80,8 @@ class gemm_rs_info(ctypes.Structure):
         "tile_cols", "grid", "compute_wgs", "reducer_wgs", "num_cus", "wgs_per_cu",
         "lds_bytes", "reduce_grid", "xcd_split")] + [("epoch", ctypes.c_uint32),
                                                      ("reduce_mode", ctypes.c_int32),
-                                                     ("split_state", ctypes.c_int32)]
+                                                     ("split_state", ctypes.c_int32),
+                                                     ("tile_stores", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -146,7 +148,7 @@ def _check(code: int, what: str) -> int:
 
 def make_config(M, N, K_local, tp=8, rank=0, tile=TILE_AUTO, group_m=0, num_reducers=-1,
                 debug_flags=0, drop_flag=-1, flag_stride=1,
-                watchdog_us=0, reduce_mode=REDUCE_AUTO, tile_stores=STORES_DEVICE,
+                watchdog_us=0, reduce_mode=REDUCE_AUTO, tile_stores=STORES_AUTO,
                 flag_protocol=FLAGS_TILE) -> gemm_rs_config:
     if isinstance(tile, str):
         tile = TILES[tile]

@@ -76,7 +76,13 @@ def cfg(**kw):
     (dict(num_reducers=-2, reduce_mode="coresident"), gr.ERR_INVALID_ARG),
     (dict(tile_stores="nt"), gr.OK),
     (dict(tile_stores="nt", num_reducers=8), gr.OK),
-    (dict(tile_stores=2), gr.ERR_INVALID_ARG),
+    (dict(tile_stores=3), gr.ERR_INVALID_ARG),
+    (dict(tile_stores="auto"), gr.OK),
+    (dict(tile_stores="auto", flag_protocol="row_counter"), gr.OK),
+    (dict(tile_stores="auto", reduce_mode="stream"), gr.OK),
+    (dict(tile_stores="auto", reduce_mode="adaptive"), gr.OK),
+    (dict(tile_stores="auto", num_reducers=-2), gr.OK),
+    (dict(tile_stores="device", reduce_mode="stream"), gr.OK),
     (dict(tile_stores=-1), gr.ERR_INVALID_ARG),
     (dict(flag_protocol="row_counter"), gr.OK),
     (dict(flag_protocol="row_counter", num_reducers=8), gr.OK),
@@ -180,6 +186,30 @@ def test_kernel_tiles_inside_buffers(M, N, K, tile, gm):
 ])
 def test_plan_resolves_reduce_mode(kw, mode):
     assert gr.gemm_rs_plan(cfg(**kw)).reduce_mode == mode
+
+
+@pytest.mark.parametrize("kw,stores", [
+    (dict(M=32768, N=8192, K_local=3584), gr.STORES_NONTEMPORAL),    # large prefill: 4096 tiles, tail
+    (dict(M=8192, N=8192, K_local=3584), gr.STORES_NONTEMPORAL),     # 1024 tiles
+    (dict(M=8192, N=7936, K_local=3584), gr.STORES_DEVICE),          # 992 tiles
+    (dict(M=2048, N=8192, K_local=3584), gr.STORES_DEVICE),          # down_proj: one round
+    (dict(M=512, N=8192, K_local=1024), gr.STORES_DEVICE),           # o_proj: 64x128 tile
+    (dict(M=8192, N=6144, K_local=2048), gr.STORES_DEVICE),          # the stream
+    (dict(M=32768, N=8192, K_local=2048), gr.STORES_DEVICE),         # the stream
+    (dict(M=32768, N=8192, K_local=2048, reduce_mode="tail"), gr.STORES_NONTEMPORAL),
+    (dict(M=32768, N=8192, K_local=3584, num_reducers=8), gr.STORES_NONTEMPORAL),
+    (dict(M=32768, N=8192, K_local=3584, flag_protocol="row_counter"), gr.STORES_DEVICE),
+    (dict(M=32768, N=8192, K_local=3584, reduce_mode="adaptive"), gr.STORES_DEVICE),
+    (dict(M=32768, N=8192, K_local=3584, tile="128x128"), gr.STORES_DEVICE),
+    (dict(M=32768, N=8192, K_local=3584, tile_stores="device"), gr.STORES_DEVICE),
+    (dict(M=512, N=8192, K_local=1024, tile_stores="nt"), gr.STORES_NONTEMPORAL),
+])
+def test_plan_resolves_tile_stores(kw, stores):
+    # the automatic store policy (the binding's default): the non-temporal hint
+    # for the 256x256 tile from 1024 tiles when the sum runs after the tiles,
+    # tile flags
+    assert gr.make_config(1, 1, 8).tile_stores == gr.STORES_AUTO
+    assert gr.gemm_rs_plan(cfg(**kw)).tile_stores == stores
 
 
 def test_plan_resolves_auto_tile():

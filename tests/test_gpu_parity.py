@@ -20,8 +20,11 @@ pytestmark = pytest.mark.gpu
 # (default) or by 8 dedicated reducer workgroups
 REDUCE = {"tail": dict(num_reducers=0), "reducers8": dict(num_reducers=8)}
 REDUCERS = list(REDUCE)
-# the automatic placement with the routed tiles stored non-temporally
+# the automatic placement with the routed tiles stored non-temporally, and
+# with device-scope stores only (the automatic store policy picks the
+# non-temporal hint for the 256x256 tile when the sum runs after the tiles)
 REDUCE["nt"] = dict(tile_stores="nt")
+REDUCE["device"] = dict(tile_stores="device")
 # the sum streamed through the K loop by four of the eight waves (256x256 tile)
 REDUCE["stream"] = dict(reduce_mode="stream")
 # the automatic placement with a released-tile counter per tile row
@@ -57,7 +60,7 @@ def test_tiny_integer_bit_exact_all_ranks(rank, red):
     assert np.array_equal(host(b.out), out_o)
 
 
-@pytest.mark.parametrize("red", REDUCERS)
+@pytest.mark.parametrize("red", REDUCERS + ["device"])
 @pytest.mark.parametrize("tile", ["16x64", "64x128", "128x128", "128x256", "256x128", "256x256"])
 def test_every_tile_config_integer_bit_exact(tile, red):
     # ragged: S = 264 is not a multiple of any BM > 8 and N = 392 of no BN;
@@ -168,7 +171,7 @@ def test_error_within_1p1x_of_unfused_path(name, mode):
 
 # ------------------------------------------------------------------ full shapes, sampled rows
 
-@pytest.mark.parametrize("red", ["bench", "reducers8", "nt", "rowc", "stream"])
+@pytest.mark.parametrize("red", ["bench", "reducers8", "nt", "device", "rowc", "stream"])
 @pytest.mark.parametrize("name", ["o_proj", "down_proj", "mixtral_down", "large_prefill"])
 @pytest.mark.parametrize("mode", ["normal", "integer"])
 def test_benchmark_shapes_sampled_rows(name, mode, red):
