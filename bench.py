@@ -506,6 +506,7 @@ SPLIT_KNOBS = (
     [dict(reduce_mode="tail")] + [dict(num_reducers=r) for r in (2, 4, 8, 12, 16, 24, 32, 64)]
     + [dict(reduce_mode="stream"), dict(reduce_mode="adaptive")]
     + [dict(reduce_mode="tail", flag_stride=32), dict(num_reducers=8, flag_stride=32)]
+    + [dict(reduce_mode="tail", tile_stores=0), dict(num_reducers=8, tile_stores=0)]
     + [dict(reduce_mode="tail", tile_stores=1), dict(num_reducers=8, tile_stores=1)]
     + [dict(reduce_mode="tail", flag_protocol=1), dict(num_reducers=8, flag_protocol=1)]
 )
@@ -550,7 +551,7 @@ def split_sweep(args):
         st = op.status()
         tf = statistics.median(t[f"k{i}"])
         rows.append({**kw, "flag_stride": kw.get("flag_stride", 1),
-                     "tile_stores": kw.get("tile_stores", 0),
+                     "tile_stores": op.info.tile_stores,
                      "flag_protocol": kw.get("flag_protocol", 0),
                      "compute_wgs": op.info.compute_wgs, "reducer_wgs": op.info.reducer_wgs,
                      "T_fused_us": tf, "fused_tflops": cfg.flops / tf * 1e-6,
