@@ -792,7 +792,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of a TP=8 layer on a single GPU; --gpus {args.gpus} "
-              "is not supported (no multi-GPU path in this build).", file=sys.stderr)
+              "is not supported (the library runs one GPU; sharding across GPUs is a design only).", file=sys.stderr)
         sys.exit(2)
     import torch
 
