@@ -890,7 +890,7 @@ def main():
                 log(f"[{name}] error: {e!r}")
     if args.sweep_out:
         with open(args.sweep_out, "w") as f:
-            json.dump({args.workload: m, **sweep}, f, indent=1)
+            json.dump({args.workload: m, **sweep, "source_digest": source_digest()}, f, indent=1)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
